@@ -1,0 +1,244 @@
+// C ABI of libmsa: argument validation, workspace layout and kernel launch
+// order.  Declarations and the contract of every entry point are in
+// include/msa.h.  No entry point allocates device memory or synchronises.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "msa.h"
+#include "msa_internal.hpp"
+
+using namespace msa;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+msa_status fail(msa_status st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+msa_status hip_fail(hipError_t e, const char *where) {
+    return fail(MSA_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+// Decode top-k holds up to 128 candidates per lane: 8192 blocks.
+constexpr int kDecodeMaxBlocks = 64 * 128;
+
+struct SelectWs {
+    size_t docs, off, scores, total;
+};
+
+SelectWs select_layout(int T, int ndocs, int max_seqlen) {
+    SelectWs w;
+    const int nb_max = ceil_div(max_seqlen, kBlock);
+    w.docs = 0;
+    w.off = align256(w.docs + sizeof(DocSpan) * size_t(ndocs));
+    w.scores = align256(w.off + sizeof(int32_t) * (size_t(ndocs) + 1));
+    w.total = align256(w.scores + sizeof(float) * size_t(kIdxHeads) * nb_max * size_t(T));
+    return w;
+}
+
+struct PrefillWs {
+    size_t docs, off, total;
+};
+
+PrefillWs prefill_layout(int ndocs) {
+    PrefillWs w;
+    w.docs = 0;
+    w.off = align256(sizeof(DocSpan) * size_t(ndocs));
+    w.total = align256(w.off + sizeof(int32_t) * (size_t(ndocs) + 1));
+    return w;
+}
+
+struct DecodeWs {
+    size_t scores, q2k, part, total;
+};
+
+DecodeWs decode_layout(int B, int max_ctx, int topk) {
+    DecodeWs w;
+    const int nb_max = ceil_div(max_ctx, kBlock);
+    w.scores = 0;
+    w.q2k = align256(sizeof(float) * size_t(B) * kIdxHeads * nb_max);
+    w.part = align256(w.q2k + sizeof(int32_t) * size_t(kIdxHeads) * B * topk);
+    const size_t part_floats = size_t(B) * kKvHeads * topk * kGroup * (kDim + 2);
+    w.total = align256(w.part + sizeof(float) * part_floats);
+    return w;
+}
+
+msa_status check_geometry(const int32_t *cu, int ndocs, int T, int max_seqlen) {
+    if (!cu) return fail(MSA_ERR_INVALID_ARG, "cu_seqlens is NULL");
+    if (T < 1) return fail(MSA_ERR_INVALID_ARG, "total_tokens must be >= 1 (got %d)", T);
+    if (ndocs < 1 || ndocs > T)
+        return fail(MSA_ERR_INVALID_ARG, "num_docs must be in [1, total_tokens] (got %d)", ndocs);
+    if (max_seqlen < 1 || max_seqlen > T)
+        return fail(MSA_ERR_INVALID_ARG, "max_seqlen must be in [1, total_tokens] (got %d)", max_seqlen);
+    return MSA_OK;
+}
+
+msa_status check_selection(int topk, int init, int local) {
+    if (topk < 1 || topk > kMaxTopk)
+        return fail(MSA_ERR_UNSUPPORTED, "topk must be in [1, %d] (got %d)", kMaxTopk, topk);
+    if (init < 0 || local < 0)
+        return fail(MSA_ERR_INVALID_ARG, "init_blocks and local_blocks must be >= 0");
+    if (init + local > topk)
+        return fail(MSA_ERR_INVALID_ARG, "init_blocks + local_blocks (%d) exceeds topk (%d)",
+                    init + local, topk);
+    return MSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *msa_last_error(void) { return g_err; }
+
+int msa_version(void) { return 100; }
+
+const char *msa_unsupported_reason(int num_heads, int num_kv_heads, int head_dim,
+                                   int num_index_heads, int index_dim, int topk,
+                                   int block_size) {
+    if (num_heads != MSA_NUM_HEADS) return "num_heads must be 64";
+    if (num_kv_heads != MSA_NUM_KV_HEADS) return "num_kv_heads must be 4";
+    if (head_dim != MSA_HEAD_DIM) return "head_dim must be 128";
+    if (num_index_heads != MSA_NUM_INDEX_HEADS) return "num_index_heads must be 4";
+    if (index_dim != MSA_INDEX_DIM) return "index_dim must be 128";
+    if (block_size != MSA_BLOCK_SIZE) return "block_size must be 128";
+    if (topk < 1 || topk > MSA_MAX_TOPK) return "topk must be in [1, 16]";
+    return NULL;
+}
+
+size_t msa_select_blocks_workspace_bytes(int total_tokens, int num_docs, int max_seqlen) {
+    if (total_tokens < 1 || num_docs < 1 || num_docs > total_tokens || max_seqlen < 1 ||
+        max_seqlen > total_tokens)
+        return 0;
+    return select_layout(total_tokens, num_docs, max_seqlen).total;
+}
+
+size_t msa_prefill_workspace_bytes(int total_tokens, int num_docs, int max_seqlen) {
+    if (total_tokens < 1 || num_docs < 1 || num_docs > total_tokens || max_seqlen < 1 ||
+        max_seqlen > total_tokens)
+        return 0;
+    return prefill_layout(num_docs).total;
+}
+
+size_t msa_decode_workspace_bytes(int batch, int max_context_len, int topk) {
+    if (batch < 1 || max_context_len < 1 || topk < 1 || topk > kMaxTopk ||
+        ceil_div(max_context_len, kBlock) > kDecodeMaxBlocks)
+        return 0;
+    return decode_layout(batch, max_context_len, topk).total;
+}
+
+msa_status msa_select_blocks(const void *index_q, const void *index_k, int index_dtype,
+                             const int32_t *cu_seqlens, int num_docs, int total_tokens,
+                             int max_seqlen, int topk, int init_blocks, int local_blocks,
+                             int32_t *q2k, float *scores_out, void *workspace,
+                             size_t workspace_bytes, void *stream) {
+    if (!index_q || !index_k || !q2k) return fail(MSA_ERR_INVALID_ARG, "index_q, index_k and q2k must be non-NULL");
+    if (index_dtype != MSA_INDEX_BF16 && index_dtype != MSA_INDEX_FP8_E4M3)
+        return fail(MSA_ERR_UNSUPPORTED, "index_dtype must be MSA_INDEX_BF16 or MSA_INDEX_FP8_E4M3");
+    msa_status st = check_geometry(cu_seqlens, num_docs, total_tokens, max_seqlen);
+    if (st != MSA_OK) return st;
+    if ((st = check_selection(topk, init_blocks, local_blocks)) != MSA_OK) return st;
+    const SelectWs ws = select_layout(total_tokens, num_docs, max_seqlen);
+    if (!workspace || workspace_bytes < ws.total)
+        return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", ws.total,
+                    workspace ? workspace_bytes : size_t(0));
+    hipStream_t s = (hipStream_t)stream;
+    uint8_t *base = (uint8_t *)workspace;
+    DocSpan *docs = (DocSpan *)(base + ws.docs);
+    int32_t *off = (int32_t *)(base + ws.off);
+    float *S = scores_out ? scores_out : (float *)(base + ws.scores);
+    const int nb_max = ceil_div(max_seqlen, kBlock);
+    hipError_t e = launch_doc_setup(cu_seqlens, num_docs, total_tokens, max_seqlen, kScoreTile, 0,
+                                    docs, off, nullptr, s);
+    if (e != hipSuccess) return hip_fail(e, "doc_setup");
+    e = launch_block_scores(index_q, index_k, index_dtype == MSA_INDEX_FP8_E4M3, docs, off, num_docs,
+                            total_tokens, max_seqlen, S, s);
+    if (e != hipSuccess) return hip_fail(e, "block_scores");
+    e = launch_topk_prefill(S, docs, num_docs, total_tokens, nb_max, topk, init_blocks, local_blocks,
+                            q2k, s);
+    if (e != hipSuccess) return hip_fail(e, "topk");
+    return MSA_OK;
+}
+
+msa_status msa_sparse_attend_prefill(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                     const int32_t *q2k, int topk, const int32_t *cu_seqlens,
+                                     int num_docs, int total_tokens, int max_seqlen,
+                                     float softmax_scale, uint16_t *out, void *workspace,
+                                     size_t workspace_bytes, void *stream) {
+    if (!q || !k || !v || !q2k || !out) return fail(MSA_ERR_INVALID_ARG, "q, k, v, q2k and out must be non-NULL");
+    if (topk < 1 || topk > kMaxTopk)
+        return fail(MSA_ERR_UNSUPPORTED, "topk must be in [1, %d] (got %d)", kMaxTopk, topk);
+    msa_status st = check_geometry(cu_seqlens, num_docs, total_tokens, max_seqlen);
+    if (st != MSA_OK) return st;
+    if (!(softmax_scale > 0.f) || softmax_scale > 1e30f)
+        return fail(MSA_ERR_INVALID_ARG, "softmax_scale must be a positive finite number");
+    const PrefillWs ws = prefill_layout(num_docs);
+    if (!workspace || workspace_bytes < ws.total)
+        return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", ws.total,
+                    workspace ? workspace_bytes : size_t(0));
+    hipStream_t s = (hipStream_t)stream;
+    uint8_t *base = (uint8_t *)workspace;
+    DocSpan *docs = (DocSpan *)(base + ws.docs);
+    int32_t *off = (int32_t *)(base + ws.off);
+    hipError_t e = launch_doc_setup(cu_seqlens, num_docs, total_tokens, max_seqlen, kAttnTile, 0,
+                                    docs, off, nullptr, s);
+    if (e != hipSuccess) return hip_fail(e, "doc_setup");
+    e = launch_attend_prefill(q, k, v, q2k, topk, docs, off, num_docs, total_tokens, max_seqlen,
+                              softmax_scale, out, s);
+    if (e != hipSuccess) return hip_fail(e, "attend_prefill");
+    return MSA_OK;
+}
+
+msa_status msa_sparse_attend_decode_paged(
+    const uint16_t *q, const void *index_q, const uint16_t *k_cache, const uint16_t *v_cache,
+    const void *index_k_cache, int index_dtype, const int32_t *page_table, int max_pages_per_seq,
+    const int32_t *context_lens, int batch, int max_context_len, int topk, int init_blocks,
+    int local_blocks, float softmax_scale, uint16_t *out, int32_t *q2k_out, void *workspace,
+    size_t workspace_bytes, void *stream) {
+    if (!q || !index_q || !k_cache || !v_cache || !index_k_cache || !page_table || !context_lens || !out)
+        return fail(MSA_ERR_INVALID_ARG, "tensor arguments must be non-NULL (q2k_out may be NULL)");
+    if (index_dtype != MSA_INDEX_BF16 && index_dtype != MSA_INDEX_FP8_E4M3)
+        return fail(MSA_ERR_UNSUPPORTED, "index_dtype must be MSA_INDEX_BF16 or MSA_INDEX_FP8_E4M3");
+    if (batch < 1) return fail(MSA_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", batch);
+    if (max_context_len < 1) return fail(MSA_ERR_INVALID_ARG, "max_context_len must be >= 1");
+    const int nb_max = ceil_div(max_context_len, kBlock);
+    if (nb_max > kDecodeMaxBlocks)
+        return fail(MSA_ERR_UNSUPPORTED, "max_context_len above %d is not supported",
+                    kDecodeMaxBlocks * kBlock);
+    if (max_pages_per_seq < nb_max)
+        return fail(MSA_ERR_INVALID_ARG, "max_pages_per_seq (%d) < ceil(max_context_len/128) (%d)",
+                    max_pages_per_seq, nb_max);
+    msa_status st = check_selection(topk, init_blocks, local_blocks);
+    if (st != MSA_OK) return st;
+    if (!(softmax_scale > 0.f) || softmax_scale > 1e30f)
+        return fail(MSA_ERR_INVALID_ARG, "softmax_scale must be a positive finite number");
+    const DecodeWs ws = decode_layout(batch, max_context_len, topk);
+    if (!workspace || workspace_bytes < ws.total)
+        return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", ws.total,
+                    workspace ? workspace_bytes : size_t(0));
+    hipStream_t s = (hipStream_t)stream;
+    uint8_t *base = (uint8_t *)workspace;
+    float *S = (float *)(base + ws.scores);
+    int32_t *q2k = q2k_out ? q2k_out : (int32_t *)(base + ws.q2k);
+    float *part = (float *)(base + ws.part);
+    hipError_t e = launch_decode_scores(index_q, index_k_cache, index_dtype == MSA_INDEX_FP8_E4M3,
+                                        page_table, max_pages_per_seq, context_lens, batch,
+                                        max_context_len, nb_max, S, s);
+    if (e != hipSuccess) return hip_fail(e, "decode_scores");
+    e = launch_decode_topk(S, context_lens, batch, max_context_len, nb_max, topk, init_blocks,
+                           local_blocks, q2k, s);
+    if (e != hipSuccess) return hip_fail(e, "decode_topk");
+    e = launch_decode_attend(q, k_cache, v_cache, page_table, max_pages_per_seq, context_lens,
+                             max_context_len, batch, q2k, topk, softmax_scale, part, out, s);
+    if (e != hipSuccess) return hip_fail(e, "decode_attend");
+    return MSA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,50 @@
+// Internal launch interface between the C ABI (msa_api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "msa_common.hpp"
+
+namespace msa {
+
+constexpr int kScoreTile = 64;   // query tokens per block-scorer workgroup
+constexpr int kAttnTile = 8;     // query tokens per prefill-attention workgroup
+
+inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Geometry: sanitised document spans plus, for two tile sizes, the prefix
+// count of document-aligned tiles (off[d] = tiles in documents < d).
+hipError_t launch_doc_setup(const int32_t *cu, int ndocs, int T, int max_seqlen, int tile_a,
+                            int tile_b, DocSpan *docs, int32_t *off_a, int32_t *off_b,
+                            hipStream_t stream);
+
+// Block scores S[h][b][t] (fp32, [4][nb_max][T]) for b <= c(t).
+hipError_t launch_block_scores(const void *iq, const void *ik, bool fp8, const DocSpan *docs,
+                               const int32_t *tile_off, int ndocs, int T, int max_seqlen,
+                               float *S, hipStream_t stream);
+
+// Forced blocks + top-k from S into q2k [4][T][topk].
+hipError_t launch_topk_prefill(const float *S, const DocSpan *docs, int ndocs, int T, int nb_max,
+                               int topk, int init, int local, int32_t *q2k, hipStream_t stream);
+
+// Sparse GQA prefill attention.
+hipError_t launch_attend_prefill(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                 const int32_t *q2k, int topk, const DocSpan *docs,
+                                 const int32_t *tile_off, int ndocs, int T, int max_seqlen,
+                                 float scale, uint16_t *out, hipStream_t stream);
+
+// Paged decode.
+hipError_t launch_decode_scores(const void *iq, const void *ikc, bool fp8, const int32_t *pt,
+                                int max_pages, const int32_t *ctx, int B, int max_ctx, int nb_max,
+                                float *S, hipStream_t stream);
+hipError_t launch_decode_topk(const float *S, const int32_t *ctx, int B, int max_ctx, int nb_max, int topk,
+                              int init, int local, int32_t *q2k, hipStream_t stream);
+hipError_t launch_decode_attend(const uint16_t *q, const uint16_t *kc, const uint16_t *vc,
+                                const int32_t *pt, int max_pages, const int32_t *ctx, int max_ctx, int B,
+                                const int32_t *q2k, int topk, float scale, float *partial,
+                                uint16_t *out, hipStream_t stream);
+
+}  // namespace msa

@@ -1,0 +1,324 @@
+// Index-branch block selection for packed-document prefill.
+//
+// Method (TensorRT-LLM "MiniMaxM3SparseAttentionConfig", class description
+// and the sparse_* fields; NeMo AutoModel minimax_m3_vl.msa,
+// MSAMicrobatch.select_blocks): every 128-key block of the query's own
+// document is scored by the largest raw dot product between the query's
+// index vector (per index head) and the single shared index key, over the
+// block's keys at or before the query; blocks 0..init-1 and the last
+// `local` blocks up to the query's own block are forced; the remaining
+// top-k slots take the best-scoring other blocks; ids are document-local,
+// ascending, padded with -1.
+//
+// Kernels:
+//   doc_setup_kernel    - sanitised document spans + tile prefix counts.
+//   block_scores_kernel - S^T = K . IQ^T on MFMA (bf16 32x32x16 or E4M3
+//                         32x32x64 with unit scales), fused causal mask and
+//                         per-block row max; one workgroup = 64 query tokens
+//                         x 4 index heads of one document, looping over key
+//                         blocks 0..c staged through double-buffered LDS.
+//   topk_prefill_kernel - one lane per (head, token) row: top-R insertion
+//                         over 64-bit (score, ~id) keys, then an ascending
+//                         emit pass against the R-th key.
+#include "msa_internal.hpp"
+
+namespace msa {
+
+// ---------------------------------------------------------------------------
+// G0: document spans and tile offsets
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void doc_setup_kernel(const int32_t *__restrict__ cu, int ndocs,
+                                                         int T, int max_seqlen, int tile_a,
+                                                         int tile_b, DocSpan *__restrict__ docs,
+                                                         int32_t *__restrict__ off_a,
+                                                         int32_t *__restrict__ off_b) {
+    __shared__ int wsum_a[16], wsum_b[16];
+    __shared__ int carry_a, carry_b;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (tid == 0) {
+        carry_a = 0;
+        carry_b = 0;
+        off_a[0] = 0;
+        if (off_b) off_b[0] = 0;
+    }
+    __syncthreads();
+    for (int base = 0; base < ndocs; base += 1024) {
+        const int d = base + tid;
+        int na = 0, nb = 0;
+        if (d < ndocs) {
+            int s = min(max(cu[d], 0), T);
+            int e = min(max(cu[d + 1], s), T);
+            int len = min(e - s, max_seqlen);
+            docs[d] = DocSpan{s, len};
+            na = (len + tile_a - 1) / tile_a;
+            nb = tile_b > 0 ? (len + tile_b - 1) / tile_b : 0;
+        }
+        // inclusive wave scans
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            int ya = __shfl_up(na, o), yb = __shfl_up(nb, o);
+            if (lane >= o) { na += ya; nb += yb; }
+        }
+        if (lane == 63) { wsum_a[wave] = na; wsum_b[wave] = nb; }
+        __syncthreads();
+        int pa = carry_a, pb = carry_b;
+        for (int w = 0; w < wave; ++w) { pa += wsum_a[w]; pb += wsum_b[w]; }
+        if (d < ndocs) {
+            off_a[d + 1] = pa + na;
+            if (off_b) off_b[d + 1] = pb + nb;
+        }
+        __syncthreads();
+        if (tid == 1023) { carry_a = pa + na; carry_b = pb + nb; }
+        __syncthreads();
+    }
+}
+
+hipError_t launch_doc_setup(const int32_t *cu, int ndocs, int T, int max_seqlen, int tile_a,
+                            int tile_b, DocSpan *docs, int32_t *off_a, int32_t *off_b,
+                            hipStream_t stream) {
+    hipLaunchKernelGGL(doc_setup_kernel, dim3(1), dim3(1024), 0, stream, cu, ndocs, T, max_seqlen,
+                       tile_a, tile_b, docs, off_a, off_b);
+    return hipGetLastError();
+}
+
+// Tile t of a prefix-count array off[0..ndocs]: the document d with
+// off[d] <= t < off[d+1] (uniform across the workgroup).
+__device__ __forceinline__ int tile_doc(const int32_t *off, int ndocs, int t) {
+    int lo = 0, hi = ndocs - 1;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (off[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// ---------------------------------------------------------------------------
+// G1: block scores
+// ---------------------------------------------------------------------------
+template <bool kFp8>
+struct ScoreLayout {
+    static constexpr int kRowBytes = kFp8 ? 128 : 256;         // one index row
+    static constexpr int kPitch = kRowBytes + 16;              // LDS row pitch (bank spread)
+    static constexpr int kChunksPerRow = kRowBytes / 16;
+    static constexpr int kChunksPerThread = kBlock * kChunksPerRow / 256;
+    static constexpr int kBufBytes = kBlock * kPitch;
+};
+
+template <bool kFp8>
+__global__ __launch_bounds__(256) void block_scores_kernel(
+    const uint8_t *__restrict__ iq, const uint8_t *__restrict__ ik, const DocSpan *__restrict__ docs,
+    const int32_t *__restrict__ tile_off, int ndocs, int T, int nb_max, float *__restrict__ S) {
+    using L = ScoreLayout<kFp8>;
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+
+    const int tile = blockIdx.x;
+    if (tile >= tile_off[ndocs]) return;
+    const int d = tile_doc(tile_off, ndocs, tile);
+    const int nt_doc = tile_off[d + 1] - tile_off[d];
+    const int local_tile = nt_doc - 1 - (tile - tile_off[d]);  // longest rows first
+    const DocSpan doc = docs[d];
+    const int p0 = local_tile * kScoreTile;                     // doc-local first query
+    const int c = p0 / kBlock;                                  // query block (shared by tile)
+    const int key_end = min(doc.len, p0 + kScoreTile);          // keys past this never count
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = lane & 31, hb = lane >> 5;
+
+    // Index-query operand (B), kept in registers for the whole key loop.
+    // Column n of N-tile nt is row (token p0+16*wave+8*nt+n/4, head n%4).
+    constexpr int kSteps = kFp8 ? 2 : 8;
+    typedef typename std::conditional<kFp8, i32x8, bf16x8>::type Frag;
+    Frag qb[2][kSteps];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+        const int p = p0 + 16 * wave + 8 * nt + n / 4;
+        const bool ok = p < doc.len;
+        const size_t row = size_t(doc.start + (ok ? p : 0)) * kIdxHeads + (n & 3);
+        const uint8_t *src = iq + row * L::kRowBytes;
+#pragma unroll
+        for (int ks = 0; ks < kSteps; ++ks) {
+            if constexpr (kFp8) {
+                u32x4 lo = ok ? *(const u32x4 *)(src + 64 * ks + 32 * hb) : u32x4{0, 0, 0, 0};
+                u32x4 hi = ok ? *(const u32x4 *)(src + 64 * ks + 32 * hb + 16) : u32x4{0, 0, 0, 0};
+                qb[nt][ks] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                   (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+            } else {
+                u32x4 v = ok ? *(const u32x4 *)(src + 2 * (16 * ks + 8 * hb)) : u32x4{0, 0, 0, 0};
+                qb[nt][ks] = __builtin_bit_cast(bf16x8, v);
+            }
+        }
+    }
+
+    // Stage key block b (rows doc.start + 128b + r, r < 128) into registers.
+    u32x4 stage[L::kChunksPerThread];
+    auto load_block = [&](int b) {
+#pragma unroll
+        for (int i = 0; i < L::kChunksPerThread; ++i) {
+            const int chunk = tid + 256 * i;
+            const int r = chunk / L::kChunksPerRow, col = chunk % L::kChunksPerRow;
+            const int kp = b * kBlock + r;
+            stage[i] = kp < key_end
+                           ? *(const u32x4 *)(ik + size_t(doc.start + kp) * L::kRowBytes + 16 * col)
+                           : u32x4{0, 0, 0, 0};
+        }
+    };
+    auto store_block = [&](int buf) {
+        uint8_t *dst = smem + buf * L::kBufBytes;
+#pragma unroll
+        for (int i = 0; i < L::kChunksPerThread; ++i) {
+            const int chunk = tid + 256 * i;
+            const int r = chunk / L::kChunksPerRow, col = chunk % L::kChunksPerRow;
+            *(u32x4 *)(dst + r * L::kPitch + 16 * col) = stage[i];
+        }
+    };
+
+    load_block(0);
+    store_block(0);
+    __syncthreads();
+
+    for (int b = 0; b <= c; ++b) {
+        const int buf = b & 1;
+        if (b < c) load_block(b + 1);
+
+        f32x16 acc[4][2];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f32x16{};
+
+        const uint8_t *kb = smem + buf * L::kBufBytes;
+#pragma unroll
+        for (int ks = 0; ks < kSteps; ++ks) {
+            Frag a[4];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                const uint8_t *src = kb + (32 * mt + n) * L::kPitch;
+                if constexpr (kFp8) {
+                    u32x4 lo = *(const u32x4 *)(src + 64 * ks + 32 * hb);
+                    u32x4 hi = *(const u32x4 *)(src + 64 * ks + 32 * hb + 16);
+                    a[mt] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                  (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+                } else {
+                    a[mt] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(src + 2 * (16 * ks + 8 * hb)));
+                }
+            }
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    if constexpr (kFp8)
+                        acc[mt][nt] = mfma_32x32x64_e4m3(a[mt], qb[nt][ks], acc[mt][nt]);
+                    else
+                        acc[mt][nt] = mfma_32x32x16(a[mt], qb[nt][ks], acc[mt][nt]);
+                }
+        }
+
+        // Per query column: max over the block's 128 keys (rows), causal in
+        // the query's own block.
+        const bool diag = (b == c);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            const int p = p0 + 16 * wave + 8 * nt + n / 4;
+            float mx = -INFINITY;
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int kp = b * kBlock + 32 * mt + 8 * (r >> 2) + 4 * hb + (r & 3);
+                    const float v = (diag && kp > p) ? -INFINITY : acc[mt][nt][r];
+                    mx = fmaxf(mx, v);
+                }
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            if (hb == 0 && p < doc.len)
+                S[(size_t(n & 3) * nb_max + b) * T + doc.start + p] = mx;
+        }
+
+        if (b < c) store_block(buf ^ 1);
+        __syncthreads();
+    }
+}
+
+hipError_t launch_block_scores(const void *iq, const void *ik, bool fp8, const DocSpan *docs,
+                               const int32_t *tile_off, int ndocs, int T, int max_seqlen,
+                               float *S, hipStream_t stream) {
+    const int nb_max = ceil_div(max_seqlen, kBlock);
+    const int grid = ceil_div(T, kScoreTile) + ndocs;  // upper bound on document-aligned tiles
+    if (fp8) {
+        const size_t lds = 2 * ScoreLayout<true>::kBufBytes;
+        hipLaunchKernelGGL(block_scores_kernel<true>, dim3(grid), dim3(256), lds, stream,
+                           (const uint8_t *)iq, (const uint8_t *)ik, docs, tile_off, ndocs, T,
+                           nb_max, S);
+    } else {
+        const size_t lds = 2 * ScoreLayout<false>::kBufBytes;
+        hipLaunchKernelGGL(block_scores_kernel<false>, dim3(grid), dim3(256), lds, stream,
+                           (const uint8_t *)iq, (const uint8_t *)ik, docs, tile_off, ndocs, T,
+                           nb_max, S);
+    }
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// G2: forced blocks + top-k
+// ---------------------------------------------------------------------------
+// Insert `key` into the descending list top[0..15] (smallest falls off).
+__device__ __forceinline__ void topk_insert(uint64_t (&top)[kMaxTopk], uint64_t key) {
+#pragma unroll
+    for (int i = kMaxTopk - 1; i >= 0; --i) {
+        const uint64_t prev = i > 0 ? top[i - 1] : ~0ull;
+        if (key > top[i]) top[i] = key > prev ? prev : key;
+    }
+}
+
+__device__ __forceinline__ uint64_t topk_at(const uint64_t (&top)[kMaxTopk], int i) {
+    uint64_t v = 0;
+#pragma unroll
+    for (int j = 0; j < kMaxTopk; ++j) v = (j == i) ? top[j] : v;
+    return v;
+}
+
+__global__ __launch_bounds__(256) void topk_prefill_kernel(const float *__restrict__ S,
+                                                           const DocSpan *__restrict__ docs,
+                                                           int ndocs, int T, int nb_max, int topk,
+                                                           int init, int local,
+                                                           int32_t *__restrict__ q2k) {
+    const int t = blockIdx.x * 256 + threadIdx.x;
+    const int h = blockIdx.y;
+    if (t >= T) return;
+    int32_t *out = q2k + (size_t(h) * T + t) * topk;
+    const int d = find_doc(docs, ndocs, t);
+    if (d < 0) {
+        for (int i = 0; i < topk; ++i) out[i] = -1;
+        return;
+    }
+    const int c = (t - docs[d].start) / kBlock;
+    const int R = topk - forced_count(c, init, local);
+    const float *row = S + size_t(h) * nb_max * T + t;  // row[b*T]
+
+    uint64_t top[kMaxTopk];
+#pragma unroll
+    for (int i = 0; i < kMaxTopk; ++i) top[i] = 0;
+    if (R > 0) {
+        for (int b = 0; b <= c; ++b) {
+            if (is_forced(b, c, init, local)) continue;
+            const uint64_t key = select_key(row[size_t(b) * T], b);
+            topk_insert(top, key);
+        }
+    }
+    const uint64_t thresh = R > 0 ? topk_at(top, R - 1) : ~0ull;
+    int k = 0;
+    for (int b = 0; b <= c && k < topk; ++b) {
+        bool take = is_forced(b, c, init, local);
+        if (!take && R > 0) take = select_key(row[size_t(b) * T], b) >= thresh;
+        if (take) out[k++] = b;
+    }
+    for (; k < topk; ++k) out[k] = -1;
+}
+
+hipError_t launch_topk_prefill(const float *S, const DocSpan *docs, int ndocs, int T, int nb_max,
+                               int topk, int init, int local, int32_t *q2k, hipStream_t stream) {
+    hipLaunchKernelGGL(topk_prefill_kernel, dim3(ceil_div(T, 256), kIdxHeads), dim3(256), 0, stream,
+                       S, docs, ndocs, T, nb_max, topk, init, local, q2k);
+    return hipGetLastError();
+}
+
+}  // namespace msa

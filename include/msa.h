@@ -1,0 +1,170 @@
+/*
+ * msa.h - C ABI of libmsa, MiniMax-M3 two-step block-sparse GQA attention
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * Step one (index branch): index queries [T,4,128] score a single shared
+ * index key [T,1,128]; every 128-key block of the query's own document gets
+ * the maximum raw dot product over its causal keys; a hard top-k per
+ * (KV head, query token) with init blocks forced at the head and local
+ * blocks forced at the tail yields int32 q2k [4,T,topk] padded with -1.
+ * Step two: GQA softmax attention (64 query heads, 4 KV heads, head dim 128,
+ * bf16) over only the selected blocks, for prefill over packed documents and
+ * for decode over a paged K/V cache plus a side index-K cache.
+ *
+ * Sources: TensorRT-LLM "MiniMaxM3SparseAttentionConfig" (class description;
+ * fields sparse_num_index_heads, sparse_index_dim, sparse_block_size,
+ * sparse_topk_blocks, sparse_init_blocks, sparse_local_blocks,
+ * sparse_score_type, indexer_kv_dtype); NeMo AutoModel
+ * "nemo_automodel.components.models.minimax_m3_vl.msa" (MSAMicrobatch.
+ * select_blocks, sparse_attention, the document-map classmethod,
+ * require_msa_support); vLLM "vllm.models.minimax_m3.amd.
+ * sparse_attention_nvfp4" (rocm_nvfp4_unsupported_reason).
+ *
+ * Conventions for every entry point:
+ *  - Tensor arguments are caller-owned DEVICE pointers, contiguous,
+ *    row-major, in the layouts stated.  bf16 is passed as its uint16_t bit
+ *    pattern; E4M3 as uint8_t bytes (OCP E4M3FN).
+ *  - Host scalars (token counts, max_seqlen, max_context_len) bound the
+ *    launch grids, so no call reads device memory back to the host.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *    enqueue work on it and return; they never synchronise and never
+ *    allocate: scratch memory is the caller's `workspace` (size from the
+ *    matching *_workspace_bytes query; any 256-byte-aligned device buffer).
+ *  - Host-side argument errors return a non-zero msa_status before any
+ *    GPU work is enqueued; msa_last_error() then returns a message
+ *    (thread-local).  Contract violations in device data (e.g. a
+ *    cu_seqlens that is not increasing, a page id out of range) are not
+ *    detected: kernels clamp document bounds to [0, total_tokens] so they
+ *    never read outside the buffers the host scalars describe, but the
+ *    output is then unspecified.  Page ids must lie in the cache.
+ *  - The same inputs give bitwise identical outputs on every call (no
+ *    atomics in any reduction).
+ */
+#ifndef MSA_H
+#define MSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MSA_OK = 0,
+    MSA_ERR_INVALID_ARG = 1, /* malformed argument (null pointer, bad size)      */
+    MSA_ERR_UNSUPPORTED = 2, /* well-formed but outside what the kernels handle  */
+    MSA_ERR_WORKSPACE = 3,   /* workspace_bytes below the *_workspace_bytes size */
+    MSA_ERR_HIP = 4          /* a HIP launch failed; message has the HIP error   */
+} msa_status;
+
+/* Storage and score dtype of index q/k (TensorRT-LLM config, indexer_kv_dtype:
+ * 'fp8' means unscaled E4M3 values with FP32 score accumulation). */
+typedef enum { MSA_INDEX_BF16 = 0, MSA_INDEX_FP8_E4M3 = 1 } msa_index_dtype;
+
+/* Fixed topology (NeMo msa page, require_msa_support: 64 query heads, 4 KV
+ * heads, 128 channels, max block score; TensorRT-LLM config: 4 index heads
+ * of dim 128, blocks of 128). */
+#define MSA_NUM_HEADS 64
+#define MSA_NUM_KV_HEADS 4
+#define MSA_HEAD_DIM 128
+#define MSA_NUM_INDEX_HEADS 4
+#define MSA_INDEX_DIM 128
+#define MSA_BLOCK_SIZE 128
+#define MSA_MAX_TOPK 16
+
+/* NULL when the kernels serve this layer shape, else a static string saying
+ * why not (same role as rocm_nvfp4_unsupported_reason on the vLLM page and
+ * the ValueError of require_msa_support on the NeMo page).  Served: the
+ * fixed topology above with 1 <= topk <= 16. */
+const char *msa_unsupported_reason(int num_heads, int num_kv_heads, int head_dim,
+                                   int num_index_heads, int index_dim, int topk,
+                                   int block_size);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char *msa_last_error(void);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int msa_version(void);
+
+/* Workspace sizes in bytes (0 if the arguments are invalid). */
+size_t msa_select_blocks_workspace_bytes(int total_tokens, int num_docs, int max_seqlen);
+size_t msa_prefill_workspace_bytes(int total_tokens, int num_docs, int max_seqlen);
+size_t msa_decode_workspace_bytes(int batch, int max_context_len, int topk);
+
+/*
+ * Index-branch block selection over packed documents (NeMo msa page,
+ * MSAMicrobatch.select_blocks; TensorRT-LLM config class description).
+ *
+ *  index_q     [T,4,128]  bf16 bits or E4M3 bytes, post norm and RoPE.
+ *  index_k     [T,1,128]  same dtype; one key shared by the 4 index heads.
+ *  index_dtype msa_index_dtype.
+ *  cu_seqlens  int32 [num_docs+1]: 0 = cu[0] < cu[1] < ... < cu[num_docs] = T;
+ *              document d is tokens cu[d]..cu[d+1]-1 (compact packed layout).
+ *  num_docs >= 1, total_tokens = T >= 1, max_seqlen >= every document length.
+ *  topk in [1,16]; init_blocks, local_blocks >= 0, init+local <= topk.
+ *  q2k         out int32 [4,T,topk]: row (g,t) lists the document-local block
+ *              ids chosen for KV head g and token t, ascending, then -1.
+ *              Block b of a document holds its positions 128b..128b+127.  For
+ *              a token at position p (c = p div 128) the candidates are blocks
+ *              0..c; blocks 0..init-1 and c-local+1..c are forced; the other
+ *              slots take the highest-scoring candidates (lower id on ties).
+ *  scores_out  optional out fp32 [4, ceil(max_seqlen/128), T] (head, block,
+ *              token): the block score max_{j in block b, j<=t} iq.ik
+ *              (raw dot, FP32 accumulation) for b <= c; entries b > c are
+ *              left unwritten.  NULL to skip.
+ */
+msa_status msa_select_blocks(const void *index_q, const void *index_k, int index_dtype,
+                             const int32_t *cu_seqlens, int num_docs, int total_tokens,
+                             int max_seqlen, int topk, int init_blocks, int local_blocks,
+                             int32_t *q2k, float *scores_out, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
+/*
+ * Sparse GQA attention over the selected blocks, prefill (NeMo msa page,
+ * sparse_attention; TensorRT-LLM config class description, step two).
+ *
+ *  q [T,64,128], k [T,4,128], v [T,4,128]  bf16 bits.
+ *  q2k int32 [4,T,topk] as produced by msa_select_blocks (any order; ids
+ *      outside 0..c and -1 contribute no keys; repeats count once).
+ *  cu_seqlens / num_docs / total_tokens / max_seqlen as above.
+ *  softmax_scale: logits are softmax_scale * q.k.
+ *  out [T,64,128] bf16 bits: for query head h (KV head g = h/16) and token t,
+ *      softmax attention over keys j of t's document with j <= t whose block
+ *      is in q2k row (g,t); fp32 accumulation, rounded to nearest even.
+ */
+msa_status msa_sparse_attend_prefill(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                     const int32_t *q2k, int topk, const int32_t *cu_seqlens,
+                                     int num_docs, int total_tokens, int max_seqlen,
+                                     float softmax_scale, uint16_t *out, void *workspace,
+                                     size_t workspace_bytes, void *stream);
+
+/*
+ * One decode step over a paged cache (TensorRT-LLM config class description:
+ * paged side index-K cache [num_slots,1,index_dim] parallel to the main K/V
+ * cache, same slot).  Request r has context length L = context_lens[r]
+ * (including the current token, whose K, V and index-K are already in the
+ * caches); its query is position L-1.  Logical key j lives in slot
+ * page_table[r, j div 128]*128 + j mod 128.  Selection and attention are
+ * those of msa_select_blocks / msa_sparse_attend_prefill for that token.
+ *
+ *  q [B,64,128] bf16; index_q [B,4,128] bf16 or E4M3.
+ *  k_cache, v_cache [num_pages*128,4,128] bf16; index_k_cache
+ *      [num_pages*128,1,128] in index_dtype.  Slots past L are never used
+ *      (they may hold anything, NaN included).
+ *  page_table int32 [B,max_pages_per_seq]; entries past ceil(L/128) unread.
+ *  context_lens int32 [B], each in [1, max_context_len].
+ *  out [B,64,128] bf16.  q2k_out optional int32 [4,B,topk] (NULL to skip).
+ */
+msa_status msa_sparse_attend_decode_paged(
+    const uint16_t *q, const void *index_q, const uint16_t *k_cache, const uint16_t *v_cache,
+    const void *index_k_cache, int index_dtype, const int32_t *page_table,
+    int max_pages_per_seq, const int32_t *context_lens, int batch, int max_context_len,
+    int topk, int init_blocks, int local_blocks, float softmax_scale, uint16_t *out,
+    int32_t *q2k_out, void *workspace, size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSA_H */

@@ -1,0 +1,90 @@
+"""GPU parity at the five workloads' full sizes, in the launch configuration
+the benchmark times.  The oracle computes every row where it can in seconds
+(the 2048-token prefill, both decode batches) and sampled rows elsewhere
+(first/last tokens, block edges and a seeded spread of every document)."""
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_gqa_score_amd as msa
+import oracle
+import workloads as W
+from parity import check_attention, check_scores, check_selection, dev, sample_tokens
+
+pytestmark = pytest.mark.gpu
+
+
+def _prefill_case(i, tokens=None):
+    t0 = time.time()
+    w = W.config(i)
+    print(f"[config {i}: {w.name}] T={w.T} docs={w.num_docs} generated in {time.time() - t0:.1f}s",
+          flush=True)
+    iq, ik, cu = dev(w.iq), dev(w.ik), dev(w.cu_seqlens)
+    q, k, v = dev(w.q), dev(w.k), dev(w.v)
+    q2k, S = msa.select_blocks(iq, ik, cu, w.max_seqlen, w.topk, w.init_blocks, w.local_blocks,
+                               scores=True)
+    torch.cuda.synchronize()
+    if tokens is None:
+        tokens = sample_tokens(w.cu_seqlens)
+    ref = oracle.prefill(w, tokens=tokens)
+    print(f"  oracle rows: {len(tokens)}", flush=True)
+    gpu_rows = q2k.cpu().numpy()[:, tokens].transpose(1, 0, 2)
+    check_scores(S.cpu().numpy(), ref, tokens)
+    same = check_selection(gpu_rows, ref, w.topk, w.init_blocks, w.local_blocks)
+    # step two alone: the sampled rows take the oracle's selection
+    q2k_fed = q2k.clone()
+    q2k_fed[:, torch.from_numpy(tokens).long().cuda()] = dev(ref["q2k"].transpose(1, 0, 2).copy())
+    out = msa.sparse_attend_prefill(q, k, v, q2k_fed, cu, w.max_seqlen, w.scale)
+    check_attention(out.float().cpu().numpy()[tokens], ref["out"], what=w.name)
+    # end to end on rows whose selection matched
+    out_e2e = msa.sparse_attend_prefill(q, k, v, q2k, cu, w.max_seqlen, w.scale)
+    rows = same.all(axis=1)
+    check_attention(out_e2e.float().cpu().numpy()[tokens][rows], ref["out"][rows],
+                    what=w.name + " end-to-end")
+    return w, same
+
+
+def test_config0_prefill_2k_all_tokens():
+    w, same = _prefill_case(0, tokens=np.arange(2048, dtype=np.int32))
+    assert same.mean() > 0.99
+
+
+def test_config2_prefill_32k_planted_sampled():
+    w, same = _prefill_case(2)
+    assert same.mean() > 0.95
+
+
+def test_config3_packed_documents_sampled():
+    w, same = _prefill_case(3)
+    assert w.num_docs >= 2
+    assert same.mean() > 0.95
+
+
+def _decode_case(i):
+    t0 = time.time()
+    d = W.config(i)
+    print(f"[config {i}: {d.name}] B={d.B} max_ctx={d.max_context_len} generated in "
+          f"{time.time() - t0:.1f}s", flush=True)
+    out, q2k = msa.sparse_attend_decode_paged(
+        dev(d.q), dev(d.iq), dev(d.k_cache), dev(d.v_cache), dev(d.ik_cache), dev(d.page_table),
+        dev(d.context_lens), d.max_context_len, d.topk, d.init_blocks, d.local_blocks, d.scale,
+        return_q2k=True)
+    torch.cuda.synchronize()
+    ref = oracle.decode(d)
+    same = check_selection(q2k.cpu().numpy().transpose(1, 0, 2), ref, d.topk, d.init_blocks,
+                           d.local_blocks)
+    rows = same.all(axis=1)
+    tol = 5e-2 if d.index_dtype == "fp8" else 2e-2
+    check_attention(out.float().cpu().numpy()[rows], ref["out"][rows], max_tol=tol, what=d.name)
+    assert rows.mean() > 0.9
+    return d
+
+
+def test_config1_decode_b32_all_requests():
+    _decode_case(1)
+
+
+def test_config4_decode_fp8_indexer_all_requests():
+    _decode_case(4)
