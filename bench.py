@@ -1,0 +1,338 @@
+#!/usr/bin/env python3
+"""Benchmark of the MiniMax-M3 block-sparse attention hot path on one MI355X.
+
+Default workload: paged decode, batch 32, context lengths ~ U[8192, 32768],
+topk 16 (one step = index scoring + selection + sparse attention + combine,
+i.e. one msa_sparse_attend_decode_paged call).  A second line of numbers for
+the 32768-token planted prefill (select + attend) is attached under
+"prefill_32k".  Inputs are seeded synthetic tensors, resident in HBM before
+timing; L2 and the 256 MB MALL are flushed by a 1 GiB fill before every step
+(outside the timed span).  Each step is timed with HIP events on the stream
+the kernels run on; per-kernel times come from events the library records
+around each of its launches (msa_set_timing_events).
+
+Prints ONE JSON line.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E, GB/s
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--prefill-steps", type=int, default=20)
+    ap.add_argument("--no-prefill", action="store_true", help="skip the 32k prefill numbers")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-flush", action="store_true", help="do not flush L2/MALL between steps")
+    return ap.parse_args()
+
+
+class Hip:
+    """hipEvent_t helpers on the HIP runtime torch already loaded."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so.7")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def events(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            assert self.lib.hipEventCreate(ctypes.byref(e)) == 0
+            out.append(e)
+        return out
+
+    def record(self, ev, stream):
+        assert self.lib.hipEventRecord(ev, ctypes.c_void_p(stream)) == 0
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        assert self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return ms.value
+
+
+def dev(a):
+    """numpy -> torch on cuda:0 (uint16 bit patterns become bf16)."""
+    import numpy as np
+    import torch
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def keys_of(L, topk):
+    """Keys attended by the query at position L-1 of a length-L sequence when
+    all min(topk, nb) chosen blocks are full except the query's own."""
+    nb = (L + 127) // 128
+    return 128 * (min(topk, nb) - 1) + (L - 128 * (nb - 1))
+
+
+def timed_steps(run, steps, warmup, hip, stream, flush, n_events):
+    """Run warmup + steps; returns (per-step ms list, per-kernel ms lists)."""
+    import torch
+    import block_sparse_gqa_score_amd as msa
+    L = msa.lib()
+    ev_arrays = [(ctypes.c_void_p * n_events)(*hip.events(n_events)) for _ in range(steps)]
+    starts, ends = hip.events(steps), hip.events(steps)
+    for _ in range(warmup):
+        if flush is not None:
+            flush.zero_()
+        run(None)
+    torch.cuda.synchronize()
+    names = None
+    for i in range(steps):
+        if flush is not None:
+            flush.zero_()
+        hip.record(starts[i], stream)
+        run(ev_arrays[i])
+        hip.record(ends[i], stream)
+        if names is None:
+            names = [L.msa_timing_kernel_name(j).decode() for j in range(L.msa_timing_kernel_count())]
+    torch.cuda.synchronize()
+    step_ms = [hip.elapsed_ms(starts[i], ends[i]) for i in range(steps)]
+    return step_ms, ev_arrays, names
+
+
+def kernel_times(ev_arrays, names_per_call, hip):
+    """ev_arrays[i] holds, call after call, (k+1) events per call."""
+    out = {}
+    for arr in ev_arrays:
+        off = 0
+        for names in names_per_call:
+            for j, nm in enumerate(names):
+                out.setdefault(nm, []).append(hip.elapsed_ms(arr[off + j], arr[off + j + 1]))
+            off += len(names) + 1
+    return out
+
+
+def stats(xs):
+    import numpy as np
+    a = np.asarray(xs)
+    return dict(mean=float(a.mean()), median=float(np.median(a)), p10=float(np.percentile(a, 10)),
+                p90=float(np.percentile(a, 90)))
+
+
+def bench_decode(args, hip, flush):
+    import numpy as np
+    import torch
+    import block_sparse_gqa_score_amd as msa
+    import workloads as W
+    t0 = time.time()
+    d = W.config(1)
+    gen_s = time.time() - t0
+    dq, diq = dev(d.q), dev(d.iq)
+    dk, dv, dik = dev(d.k_cache), dev(d.v_cache), dev(d.ik_cache)
+    dpt, dctx = dev(d.page_table), dev(d.context_lens)
+    ws = torch.empty(msa.decode_workspace_bytes(d.B, d.max_context_len, d.topk), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.empty((d.B, 64, 128), dtype=torch.bfloat16, device="cuda")
+    L = msa.lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+
+    def run(events):
+        if events is not None:
+            L.msa_set_timing_events(ctypes.c_void_p(ctypes.addressof(events)), len(events))
+        st = L.msa_sparse_attend_decode_paged(
+            P(dq), P(diq), P(dk), P(dv), P(dik), 0, P(dpt), d.max_pages, P(dctx), d.B,
+            d.max_context_len, d.topk, d.init_blocks, d.local_blocks, d.scale, P(out), None, P(ws),
+            ws.numel(), ctypes.c_void_p(stream))
+        if st != 0:
+            raise RuntimeError(L.msa_last_error().decode())
+
+    step_ms, evs, names = timed_steps(run, args.steps, args.warmup, hip, stream, flush, 5)
+    kt = kernel_times(evs, [names], hip)
+
+    # algorithmic bytes (per request: index-K rows, selected K/V rows, q/iq/out, page table)
+    lens = d.context_lens.astype(np.int64)
+    nb = (lens + 127) // 128
+    idx_bytes = int((lens * 256).sum() + d.B * 4 * 128 * 2 + (nb * 4).sum())
+    kv_bytes = int(sum(4 * 512 * keys_of(int(x), d.topk) for x in lens))
+    qo_bytes = d.B * 64 * 128 * 2 * 2
+    total_bytes = idx_bytes + kv_bytes + qo_bytes
+    per_kernel = {k: stats(v)["mean"] for k, v in kt.items()}
+    alg = {"decode_scores": idx_bytes, "decode_attend": kv_bytes + d.B * 64 * 128 * 2}
+    dom = max(alg, key=lambda k: per_kernel.get(k, 0.0))
+    return dict(d=d, gen_s=gen_s, step=stats(step_ms), per_kernel_ms=per_kernel, alg_bytes=alg,
+                dominant=dom, total_bytes=total_bytes, out=out)
+
+
+def bench_prefill(args, hip, flush):
+    import numpy as np
+    import torch
+    import block_sparse_gqa_score_amd as msa
+    import workloads as W
+    t0 = time.time()
+    w = W.config(2)
+    gen_s = time.time() - t0
+    iq, ik, cu = dev(w.iq), dev(w.ik), dev(w.cu_seqlens)
+    q, k, v = dev(w.q), dev(w.k), dev(w.v)
+    ws_s = torch.empty(msa.select_blocks_workspace_bytes(w.T, w.num_docs, w.max_seqlen),
+                       dtype=torch.uint8, device="cuda")
+    ws_a = torch.empty(max(256, msa.prefill_workspace_bytes(w.T, w.num_docs, w.max_seqlen)),
+                       dtype=torch.uint8, device="cuda")
+    q2k = torch.empty((4, w.T, w.topk), dtype=torch.int32, device="cuda")
+    out = torch.empty((w.T, 64, 128), dtype=torch.bfloat16, device="cuda")
+    L = msa.lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+
+    def run(events):
+        if events is not None:
+            L.msa_set_timing_events(ctypes.c_void_p(ctypes.addressof(events)), 4)
+        st = L.msa_select_blocks(P(iq), P(ik), 0, P(cu), w.num_docs, w.T, w.max_seqlen, w.topk,
+                                 w.init_blocks, w.local_blocks, P(q2k), None, P(ws_s), ws_s.numel(),
+                                 ctypes.c_void_p(stream))
+        if st != 0:
+            raise RuntimeError(L.msa_last_error().decode())
+        if events is not None:
+            L.msa_set_timing_events(ctypes.c_void_p(ctypes.addressof(events) + 4 * 8), 3)
+        st = L.msa_sparse_attend_prefill(P(q), P(k), P(v), P(q2k), w.topk, P(cu), w.num_docs, w.T,
+                                         w.max_seqlen, w.scale, P(out), P(ws_a), ws_a.numel(),
+                                         ctypes.c_void_p(stream))
+        if st != 0:
+            raise RuntimeError(L.msa_last_error().decode())
+
+    names_per_call = [["doc_setup", "block_scores", "topk_prefill"], ["doc_setup", "attend_prefill"]]
+    step_ms, evs, _ = timed_steps(run, args.prefill_steps, args.warmup, hip, stream, flush, 7)
+    kt = {}
+    for arr in evs:
+        for nm, (a, b) in {"doc_setup(select)": (0, 1), "block_scores": (1, 2), "topk_prefill": (2, 3),
+                           "doc_setup(attend)": (4, 5), "attend_prefill": (5, 6)}.items():
+            kt.setdefault(nm, []).append(hip.elapsed_ms(arr[a], arr[b]))
+    # algorithmic flops (causal index dots + selected-key attention)
+    T = w.T
+    pos = np.arange(T)
+    keys = 128 * (np.minimum(w.topk, pos // 128 + 1) - 1) + pos % 128 + 1
+    score_flops = 4 * T * (T + 1) / 2 * 256
+    attn_flops = 64 * 512 * int(keys.sum())
+    per_kernel = {kk: stats(vv)["mean"] for kk, vv in kt.items()}
+    return dict(w=w, gen_s=gen_s, step=stats(step_ms), per_kernel_ms=per_kernel,
+                score_flops=score_flops, attn_flops=attn_flops, q2k=q2k, out=out)
+
+
+def cpu_baseline_decode(d, seconds):
+    import numpy as np
+    import oracle
+    t0 = time.time()
+    reps = 0
+    while True:
+        oracle.decode(d)
+        reps += 1
+        if time.time() - t0 >= seconds or reps >= 20:
+            break
+    el = time.time() - t0
+    return dict(value=el / reps * 1e6, unit="us/step", cores=oracle.num_threads(), kind="oracle",
+                sample=f"{reps} full decode step(s) of the same batch (all {d.B} requests)")
+
+
+def cpu_baseline_prefill(w, seconds):
+    import numpy as np
+    import oracle
+    rng = np.random.default_rng(0)
+    n = 16
+    t0 = time.time()
+    done = 0
+    while time.time() - t0 < seconds and done < 4096:
+        toks = np.sort(rng.integers(0, w.T, size=n)).astype(np.int32)
+        oracle.prefill(w, tokens=toks)
+        done += n
+    el = time.time() - t0
+    return dict(value=done / el, unit="tok/s", cores=oracle.num_threads(), kind="oracle",
+                sample=f"{done} tokens drawn uniformly from the 32768-token document")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+              f"multi-GPU path: run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs an MI355X"
+    torch.cuda.set_device(0)
+    hip = Hip()
+    flush = None if args.no_flush else torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+
+    dres = bench_decode(args, hip, flush)
+    d = dres["d"]
+    step_ms = dres["step"]["mean"]
+    dom = dres["dominant"]
+    dom_ms = dres["per_kernel_ms"][dom]
+    achieved = dres["alg_bytes"][dom] / (dom_ms * 1e-3) / 1e9
+    line = {
+        "metric": "sparse-attn prefill tok/s & decode µs/step at 1 GPU; % MFMA / HBM roofline",
+        "value": round(step_ms * 1e3, 3),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; pages shaped like the described decode workload)",
+        "config": {"workload": "decode_b32_ctx8k-32k", "batch": d.B, "topk": d.topk,
+                   "init_blocks": d.init_blocks, "local_blocks": d.local_blocks,
+                   "context_lens": "U[8192,32768] seed 1001",
+                   "mean_context": float(d.context_lens.mean()), "index_dtype": "bf16",
+                   "heads": "64q/4kv/4idx x 128", "l2_mall_flushed": flush is not None},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": None, "alg_bytes_per_launch": dres["alg_bytes"][dom],
+                     "avg_launch_us": round(dom_ms * 1e3, 3)},
+        "step_stats_ms": {k: round(v, 6) for k, v in dres["step"].items()},
+        "per_kernel_us": {k: round(v * 1e3, 3) for k, v in dres["per_kernel_ms"].items()},
+        "path_bytes_per_step": dres["total_bytes"],
+        "path_hbm_frac": round(dres["total_bytes"] / (step_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+    }
+    if not args.no_prefill:
+        pres = bench_prefill(args, hip, flush)
+        w = pres["w"]
+        p_ms = pres["step"]["mean"]
+        a_ms = pres["per_kernel_ms"]["attend_prefill"]
+        s_ms = pres["per_kernel_ms"]["block_scores"]
+        total_flops = pres["score_flops"] + pres["attn_flops"]
+        line["prefill_32k"] = {
+            "workload": "prefill_32k_planted", "value": round(w.T / (p_ms * 1e-3), 1), "unit": "tok/s",
+            "ms_per_step": round(p_ms, 6), "steps": args.prefill_steps,
+            "per_kernel_us": {k: round(v * 1e3, 3) for k, v in pres["per_kernel_ms"].items()},
+            "path_mfma_frac": round(total_flops / (p_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "roofline": {"bound": "mfma", "kernel": "attend_prefill",
+                         "achieved": round(pres["attn_flops"] / (a_ms * 1e-3) / 1e12, 2),
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(pres["attn_flops"] / (a_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                         "traffic": None, "alg_flops_per_launch": pres["attn_flops"],
+                         "avg_launch_us": round(a_ms * 1e3, 3)},
+            "block_scores": {"achieved_tflops": round(pres["score_flops"] / (s_ms * 1e-3) / 1e12, 2),
+                             "frac": round(pres["score_flops"] / (s_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+        }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_decode(d, args.cpu_seconds)
+        if not args.no_prefill:
+            line["prefill_32k"]["cpu_baseline"] = cpu_baseline_prefill(pres["w"], args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

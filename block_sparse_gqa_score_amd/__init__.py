@@ -72,6 +72,12 @@ def lib():
         L.msa_select_blocks.argtypes = [P, P, i, P, i, i, i, i, i, i, P, P, P, sz, P]
         L.msa_sparse_attend_prefill.restype = i
         L.msa_sparse_attend_prefill.argtypes = [P, P, P, P, i, P, i, i, i, f, P, P, sz, P]
+        L.msa_set_timing_events.restype = None
+        L.msa_set_timing_events.argtypes = [P, i]
+        L.msa_timing_kernel_count.restype = i
+        L.msa_timing_kernel_count.argtypes = []
+        L.msa_timing_kernel_name.restype = ctypes.c_char_p
+        L.msa_timing_kernel_name.argtypes = [i]
         L.msa_sparse_attend_decode_paged.restype = i
         L.msa_sparse_attend_decode_paged.argtypes = [P, P, P, P, P, i, P, i, P, i, i, i, i, i, f,
                                                      P, P, P, sz, P]

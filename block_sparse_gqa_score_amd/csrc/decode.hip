@@ -409,10 +409,16 @@ hipError_t launch_decode_attend(const uint16_t *q, const uint16_t *kc, const uin
                                 uint16_t *out, hipStream_t stream) {
     float *part_o = partial;
     float *part_ml = partial + size_t(B) * kKvHeads * topk * kGroup * kDim;
+    (void)out;
     hipLaunchKernelGGL(decode_attend_kernel, dim3(topk, kKvHeads, B), dim3(256), 0, stream, q, kc, vc,
                        pt, max_pages, ctx, max_ctx, B, q2k, topk, scale * kLog2e, part_o, part_ml);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_combine(const float *partial, int B, int topk, uint16_t *out,
+                                 hipStream_t stream) {
+    const float *part_o = partial;
+    const float *part_ml = partial + size_t(B) * kKvHeads * topk * kGroup * kDim;
     hipLaunchKernelGGL(decode_combine_kernel, dim3(kHeads, B), dim3(128), 0, stream, part_o, part_ml,
                        topk, out);
     return hipGetLastError();

@@ -27,6 +27,36 @@ msa_status hip_fail(hipError_t e, const char *where) {
     return fail(MSA_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
 }
 
+// Benchmark instrumentation armed by msa_set_timing_events (one call).
+struct Timing {
+    void *const *events = nullptr;
+    int capacity = 0;
+    int recorded = 0;
+    const char *names[16] = {};
+    int kernels = 0;
+};
+thread_local Timing g_timing;
+
+// Start of an entry point: take the arming for this call.
+struct TimingScope {
+    void *const *events;
+    int capacity;
+    int n = 0;
+    explicit TimingScope() : events(g_timing.events), capacity(g_timing.capacity) {
+        g_timing.events = nullptr;
+        g_timing.capacity = 0;
+        if (events) g_timing.kernels = 0;
+    }
+    // before launching kernel `name` (or after the last one with name == nullptr)
+    void mark(hipStream_t s, const char *name) {
+        if (!events || n >= capacity) return;
+        hipEventRecord((hipEvent_t)events[n], s);
+        if (name && n < 16) g_timing.names[n] = name;
+        g_timing.kernels = name ? n + 1 : n;
+        ++n;
+    }
+};
+
 // Decode top-k holds up to 128 candidates per lane: 8192 blocks.
 constexpr int kDecodeMaxBlocks = 64 * 128;
 
@@ -98,6 +128,17 @@ extern "C" {
 
 const char *msa_last_error(void) { return g_err; }
 
+void msa_set_timing_events(void *const *events, int count) {
+    g_timing.events = count > 0 ? events : nullptr;
+    g_timing.capacity = count > 0 ? count : 0;
+}
+
+int msa_timing_kernel_count(void) { return g_timing.kernels; }
+
+const char *msa_timing_kernel_name(int i) {
+    return (i >= 0 && i < g_timing.kernels && i < 16) ? g_timing.names[i] : "";
+}
+
 int msa_version(void) { return 100; }
 
 const char *msa_unsupported_reason(int num_heads, int num_kv_heads, int head_dim,
@@ -155,15 +196,20 @@ msa_status msa_select_blocks(const void *index_q, const void *index_k, int index
     int32_t *off = (int32_t *)(base + ws.off);
     float *S = scores_out ? scores_out : (float *)(base + ws.scores);
     const int nb_max = ceil_div(max_seqlen, kBlock);
+    TimingScope tm;
+    tm.mark(s, "doc_setup");
     hipError_t e = launch_doc_setup(cu_seqlens, num_docs, total_tokens, max_seqlen, kScoreTile, 0,
                                     docs, off, nullptr, s);
     if (e != hipSuccess) return hip_fail(e, "doc_setup");
+    tm.mark(s, "block_scores");
     e = launch_block_scores(index_q, index_k, index_dtype == MSA_INDEX_FP8_E4M3, docs, off, num_docs,
                             total_tokens, max_seqlen, S, s);
     if (e != hipSuccess) return hip_fail(e, "block_scores");
+    tm.mark(s, "topk_prefill");
     e = launch_topk_prefill(S, docs, num_docs, total_tokens, nb_max, topk, init_blocks, local_blocks,
                             q2k, s);
     if (e != hipSuccess) return hip_fail(e, "topk");
+    tm.mark(s, nullptr);
     return MSA_OK;
 }
 
@@ -187,12 +233,16 @@ msa_status msa_sparse_attend_prefill(const uint16_t *q, const uint16_t *k, const
     uint8_t *base = (uint8_t *)workspace;
     DocSpan *docs = (DocSpan *)(base + ws.docs);
     int32_t *off = (int32_t *)(base + ws.off);
+    TimingScope tm;
+    tm.mark(s, "doc_setup");
     hipError_t e = launch_doc_setup(cu_seqlens, num_docs, total_tokens, max_seqlen, kAttnTile, 0,
                                     docs, off, nullptr, s);
     if (e != hipSuccess) return hip_fail(e, "doc_setup");
+    tm.mark(s, "attend_prefill");
     e = launch_attend_prefill(q, k, v, q2k, topk, docs, off, num_docs, total_tokens, max_seqlen,
                               softmax_scale, out, s);
     if (e != hipSuccess) return hip_fail(e, "attend_prefill");
+    tm.mark(s, nullptr);
     return MSA_OK;
 }
 
@@ -228,16 +278,24 @@ msa_status msa_sparse_attend_decode_paged(
     float *S = (float *)(base + ws.scores);
     int32_t *q2k = q2k_out ? q2k_out : (int32_t *)(base + ws.q2k);
     float *part = (float *)(base + ws.part);
+    TimingScope tm;
+    tm.mark(s, "decode_scores");
     hipError_t e = launch_decode_scores(index_q, index_k_cache, index_dtype == MSA_INDEX_FP8_E4M3,
                                         page_table, max_pages_per_seq, context_lens, batch,
                                         max_context_len, nb_max, S, s);
     if (e != hipSuccess) return hip_fail(e, "decode_scores");
+    tm.mark(s, "decode_topk");
     e = launch_decode_topk(S, context_lens, batch, max_context_len, nb_max, topk, init_blocks,
                            local_blocks, q2k, s);
     if (e != hipSuccess) return hip_fail(e, "decode_topk");
+    tm.mark(s, "decode_attend");
     e = launch_decode_attend(q, k_cache, v_cache, page_table, max_pages_per_seq, context_lens,
                              max_context_len, batch, q2k, topk, softmax_scale, part, out, s);
     if (e != hipSuccess) return hip_fail(e, "decode_attend");
+    tm.mark(s, "decode_combine");
+    e = launch_decode_combine(part, batch, topk, out, s);
+    if (e != hipSuccess) return hip_fail(e, "decode_combine");
+    tm.mark(s, nullptr);
     return MSA_OK;
 }
 

@@ -46,5 +46,7 @@ hipError_t launch_decode_attend(const uint16_t *q, const uint16_t *kc, const uin
                                 const int32_t *pt, int max_pages, const int32_t *ctx, int max_ctx, int B,
                                 const int32_t *q2k, int topk, float scale, float *partial,
                                 uint16_t *out, hipStream_t stream);
+hipError_t launch_decode_combine(const float *partial, int B, int topk, uint16_t *out,
+                                 hipStream_t stream);
 
 }  // namespace msa

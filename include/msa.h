@@ -163,6 +163,20 @@ msa_status msa_sparse_attend_decode_paged(
     int topk, int init_blocks, int local_blocks, float softmax_scale, uint16_t *out,
     int32_t *q2k_out, void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Benchmark instrumentation (not part of the method).  Arms the NEXT
+ * entry-point call on this thread to record caller-created hipEvent_t
+ * handles on its stream: events[0] before its first kernel, events[i]
+ * before kernel i, events[k] after its last kernel (k = kernels launched).
+ * The call consumes the arming (one-shot); it records at most `count`
+ * events.  msa_timing_kernel_count() then returns k and
+ * msa_timing_kernel_name(i) the name of kernel i of that call.  Events stay
+ * owned by the caller; pass count = 0 to disarm.
+ */
+void msa_set_timing_events(void *const *events, int count);
+int msa_timing_kernel_count(void);
+const char *msa_timing_kernel_name(int i);
+
 #ifdef __cplusplus
 }
 #endif
