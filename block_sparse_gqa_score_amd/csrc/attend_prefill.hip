@@ -6,34 +6,50 @@
 // t's document at or before t whose document-local 128-key block appears in
 // q2k row (h/16, t).
 //
-// Workgroup = (KV head g, 8 consecutive tokens of one document, all inside
-// one 128-token block so they share the query block c).  Its 4 waves each own
+// Workgroup = (KV head g, 16 consecutive tokens of one document inside one
+// 128-token block, so all share the query block c); 8 waves, each owning
 // 2 tokens x 16 heads = 32 query columns.  The workgroup walks the UNION of
-// its 8 tokens' selected blocks in ascending order; each block's K (row
-// major) and V (transposed, d-major) are staged once into LDS through
-// coalesced 256-byte row loads and prefetched into registers one block
-// ahead.  A wave whose two tokens did not select the block skips it.
+// its tokens' selected blocks in ascending order.  Each block's K and V
+// (128 x 128 bf16 each, natural [key][d] layout, 16-byte chunks XOR-swizzled
+// per row) are copied HBM -> LDS by global_load_lds_dwordx4 into a 2-stage
+// ring: block u+1 streams in while block u is computed, with no register
+// staging.  A wave whose two tokens did not select the block skips it.
 //
 // Per wave and block (key rows m, query columns n):
-//   S^T[128 x 32] = K[128 x 128] . Q^T   4 M-tiles x 8 k-steps of MFMA 32x32x16
-//   mask (selected by the column's token, key <= query in the own block),
-//   online softmax in the exp2 domain, P^T packed to bf16 straight from the
+//   S^T[128 x 32] = K . Q^T   4 M-tiles x 8 k-steps of MFMA 32x32x16; the K
+//                              operand is a 16-byte LDS read per lane.
+//   mask (selected by the column's token; key <= query in the own block),
+//   online softmax in the exp2 domain with lazy rescaling (the reference max
+//   only moves when it grows by more than 2^8), P^T packed to bf16 from the
 //   S^T accumulators,
-//   O^T[128 x 32] += V^T . P^T            4 d-tiles x 8 k-steps of MFMA 32x32x16
-// The accumulator of S^T gives lane (n, hb) the keys 8*(r/4) + 4*hb + r%4 of
+//   O^T[128 x 32] += V^T . P^T   4 d-tiles x 8 k-steps of MFMA 32x32x16; the
+//                              V^T operand comes from two ds_read_b64_tr_b16.
+// The S^T accumulator gives lane (n, hb) the keys 8*(r/4) + 4*hb + r%4 of
 // each 32-key tile, so PV step s consumes registers 8*(s%2)..8*(s%2)+7 of
-// tile s/2, i.e. keys 16s + 8*(i/4) + 4*hb + i%4; the V^T operand reads the
-// same keys as two 4-key runs of the transposed LDS copy.
+// tile s/2: keys 16s + 4hb + e and 16s + 8 + 4hb + e (e < 4), exactly the
+// two 4-row groups each transposing read returns for lane (d, hb).
 #include "msa_internal.hpp"
 
 namespace msa {
 
 namespace {
-constexpr int kKPitch = kDim + 8;     // bf16 per K row in LDS   (272 B)
-constexpr int kVPitch = kBlock + 4;   // bf16 per V^T row in LDS (264 B)
-constexpr int kKBytes = kBlock * kKPitch * 2;
-constexpr int kVBytes = kDim * kVPitch * 2;
+constexpr int kTok = kAttnTile;        // 16 tokens per workgroup
+constexpr int kWaves = kTok / 2;       // 8 waves
+constexpr int kThreads = 64 * kWaves;  // 512
+constexpr int kRowBytes = kDim * 2;    // 256
+constexpr int kTileBytes = kBlock * kRowBytes;  // 32 KiB (K or V block)
+constexpr int kStageBytes = 2 * kTileBytes;     // K + V
+constexpr int kStages = 2;
+constexpr int kLoadsPerWave = kStageBytes / 1024 / kWaves;  // 1 KiB per wave instruction
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazyLog2 = 8.f;  // rescale only when the max grows by > 2^8
+
+// Chunk position of 16-byte chunk c in row r is c ^ swz(r): 16 consecutive
+// rows hit 16 distinct positions (K operand reads), and 8 consecutive rows x
+// 4 consecutive chunks hit every position exactly twice (V^T reads).
+__device__ __forceinline__ int swz(int r) {
+    return (((r >> 1) & 3) << 2) | ((r & 1) << 1) | ((r >> 3) & 1);
+}
 
 __device__ __forceinline__ int tile_doc(const int32_t *off, int ndocs, int t) {
     int lo = 0, hi = ndocs - 1;
@@ -44,61 +60,74 @@ __device__ __forceinline__ int tile_doc(const int32_t *off, int ndocs, int t) {
     return lo;
 }
 
-// 4 keys x 8 d (bf16) -> 8 d-rows x 4 keys: pick 16-bit halves.
-__device__ __forceinline__ u32x2 pick_column(const u32x4 (&r)[4], int dpair, bool high) {
-    // element (key kk, d = 2*dpair + high) of the 4 loaded rows
-    uint32_t e[4];
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) e[kk] = high ? (r[kk][dpair] >> 16) : (r[kk][dpair] & 0xFFFFu);
-    return u32x2{e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// Workgroup barrier that drains this wave's LDS operations but leaves its
+// global->LDS prefetch in flight (a plain __syncthreads would also wait for
+// every outstanding vector-memory operation).  Callers wait for the block
+// they are about to read with an explicit vmcnt first.
+__device__ __forceinline__ void barrier_keep_prefetch() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ i16x4 ds_read_tr16(const uint8_t *p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p));
 }
 }  // namespace
 
-__global__ __launch_bounds__(256) void attend_prefill_kernel(
+__global__ __launch_bounds__(kThreads) void attend_prefill_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const int32_t *__restrict__ q2k, int topk, const DocSpan *__restrict__ docs,
     const int32_t *__restrict__ tile_off, int ndocs, int T, float scale_log2,
     uint16_t *__restrict__ out) {
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    uint16_t *Ks = (uint16_t *)smem;
-    uint16_t *Vt = (uint16_t *)(smem + kKBytes);
-    __shared__ int s_id[128];
-    __shared__ int s_first[128];
-    __shared__ int s_mask[128];
-    __shared__ int s_ublk[128];
-    __shared__ int s_umask[128];
+    extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+    constexpr int kEntries = kTok * kMaxTopk;  // 256 (token, slot) pairs
+    __shared__ int s_id[kEntries];
+    __shared__ int s_first[kEntries];
+    __shared__ int s_mask[kEntries];
+    __shared__ int s_ublk[kEntries];
+    __shared__ int s_umask[kEntries];
     __shared__ int s_nu;
 
-    const int tile = blockIdx.x;
-    const int g = blockIdx.y;
+    // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs; XCD x
+    // serves KV head x/2 and alternate groups of 8 tiles (one 128-token query
+    // block) of that head, longest first, so the tiles sharing a query block
+    // share one L2.
+    const int bid = blockIdx.x;
+    const int xcd = bid & 7, xslot = bid >> 3;
+    const int g = xcd >> 1;
+    const int tile = 16 * (xslot >> 3) + 8 * (xcd & 1) + (xslot & 7);
     if (tile >= tile_off[ndocs]) return;
     const int d = tile_doc(tile_off, ndocs, tile);
     const int nt_doc = tile_off[d + 1] - tile_off[d];
     const int local_tile = nt_doc - 1 - (tile - tile_off[d]);
     const DocSpan doc = docs[d];
-    const int p0 = local_tile * kAttnTile;
+    const int p0 = local_tile * kTok;
     const int c = p0 / kBlock;
-    const int ntok = min(kAttnTile, doc.len - p0);
+    const int ntok = min(kTok, doc.len - p0);
     const int p_last = p0 + ntok - 1;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
     const int n = lane & 31, hb = lane >> 5;
 
     // ---- union of the tile's selected blocks (ascending, with token masks)
     if (tid == 0) s_nu = 0;
-    if (tid < 128) {
-        const int tok = tid >> 4, slot = tid & 15;
+    if (tid < kEntries) {
+        const int tok = tid >> 4, sl = tid & 15;
         int id = -1;
-        if (tok < ntok && slot < topk) id = q2k[(size_t(g) * T + doc.start + p0 + tok) * topk + slot];
+        if (tok < ntok && sl < topk) id = q2k[(size_t(g) * T + doc.start + p0 + tok) * topk + sl];
         s_id[tid] = (id >= 0 && id <= c) ? id : -1;
     }
     __syncthreads();
-    if (tid < 128) {
+    if (tid < kEntries) {
         const int my = s_id[tid];
         int first = my >= 0, mask = 0;
-        for (int j = 0; j < 128; ++j) {
-            const int o = s_id[j];
-            if (o == my) {
+        for (int j = 0; j < kEntries; ++j) {
+            if (s_id[j] == my) {
                 mask |= 1 << (j >> 4);
                 if (j < tid) first = 0;
             }
@@ -107,10 +136,10 @@ __global__ __launch_bounds__(256) void attend_prefill_kernel(
         s_mask[tid] = mask;
     }
     __syncthreads();
-    if (tid < 128 && s_first[tid]) {
+    if (tid < kEntries && s_first[tid]) {
         const int my = s_id[tid];
         int pos = 0;
-        for (int j = 0; j < 128; ++j) pos += (s_first[j] && s_id[j] < my);
+        for (int j = 0; j < kEntries; ++j) pos += (s_first[j] && s_id[j] < my);
         s_ublk[pos] = my;
         s_umask[pos] = s_mask[tid];
         atomicAdd(&s_nu, 1);
@@ -132,126 +161,149 @@ __global__ __launch_bounds__(256) void attend_prefill_kernel(
                             : bf16x8{};
     }
 
-    // ---- staging: K rows (8 chunks of 16 B) and V (2 items of 4 keys x 8 d)
-    u32x4 kst[8];
-    u32x4 vst[2][4];
-    auto load_block = [&](int b) {
-        const size_t row0 = size_t(doc.start) + size_t(b) * kBlock;
+    // ---- HBM -> LDS block copy: 64 one-KiB instructions per block (K then V),
+    // kLoadsPerWave per wave.  Instruction j' fills rows 4j'..4j'+3 of its tile;
+    // lane l writes position l%16 of row 4j' + l/16, i.e. chunk (l%16)^swz(row).
+    // Rows past the last query of the tile are never attended: they re-read
+    // row p_last so that no load leaves the document.
+    auto issue_block = [&](int b, int stage) {
+        uint8_t *base = smem + stage * kStageBytes;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int chunk = tid + 256 * i;
-            const int r = chunk >> 4, col = chunk & 15;
-            const int kp = b * kBlock + r;
-            kst[i] = kp <= p_last ? *(const u32x4 *)(k + ((row0 + r) * kKvHeads + g) * kDim + 8 * col)
-                                  : u32x4{0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int item = tid + 256 * j;
-            const int dg = item & 15, kg = item >> 4;  // d 8dg..8dg+7, keys 4kg..4kg+3
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const int r = 4 * kg + kk;
-                const int kp = b * kBlock + r;
-                vst[j][kk] = kp <= p_last
-                                 ? *(const u32x4 *)(v + ((row0 + r) * kKvHeads + g) * kDim + 8 * dg)
-                                 : u32x4{0, 0, 0, 0};
-            }
-        }
-    };
-    auto store_block = [&]() {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int chunk = tid + 256 * i;
-            const int r = chunk >> 4, col = chunk & 15;
-            *(u32x4 *)(Ks + r * kKPitch + 8 * col) = kst[i];
-        }
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int item = tid + 256 * j;
-            const int dg = item & 15, kg = item >> 4;
-#pragma unroll
-            for (int dd = 0; dd < 8; ++dd)
-                *(u32x2 *)(Vt + (8 * dg + dd) * kVPitch + 4 * kg) = pick_column(vst[j], dd >> 1, dd & 1);
+        for (int j = 0; j < kLoadsPerWave; ++j) {
+            const int id = kLoadsPerWave * wave + j;  // 0..63
+            const int part = id >> 5, row4 = id & 31;
+            const int r = 4 * row4 + (lane >> 4);
+            const int chunk = (lane & 15) ^ swz(r);
+            const int kp = min(b * kBlock + r, p_last);
+            const uint16_t *src = (part ? v : k) +
+                                  (size_t(doc.start + kp) * kKvHeads + g) * kDim + 8 * chunk;
+            __builtin_amdgcn_global_load_lds((const void *)src,
+                                             (lds_void *)(base + part * kTileBytes + row4 * 1024),
+                                             16, 0, 0);
         }
     };
 
     f32x16 acc_o[4];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) acc_o[dt] = f32x16{};
-    float m_run = -INFINITY, l_run = 0.f;
+    float m_ref = -INFINITY;  // raw-score reference of the exponentials
+    float l_run = 0.f;
 
-    if (nu > 0) load_block(s_ublk[0]);
+    // lane-constant LDS offsets
+    const int k_swz = swz(n);              // rows 32mt + n share n's low 4 bits
+    const int G = lane >> 4, gi = lane & 15;
+    const int v_col = 16 * (G & 1) + 4 * (gi & 3);  // + 32 dt
+    int v_off[2];                                    // row within the 16-key PV step
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) v_off[h2] = 8 * h2 + 4 * (G >> 1) + (gi >> 2);
+
+    if (nu > 0) issue_block(s_ublk[0], 0);
     for (int u = 0; u < nu; ++u) {
+        if (u + 1 < nu) {
+            issue_block(s_ublk[u + 1], (u + 1) & 1);
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoadsPerWave) : "memory");
+        } else {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+        barrier_keep_prefetch();  // block u is in LDS for every wave
+
         const int b = s_ublk[u];
         const int umask = s_umask[u];
-        store_block();
-        __syncthreads();
-        if (u + 1 < nu) load_block(s_ublk[u + 1]);
-
-        const bool wave_active = ((umask >> (2 * wave)) & 3) != 0;
-        if (wave_active) {
-            f32x16 acc_s[4];
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) acc_s[mt] = f32x16{};
-#pragma unroll
-            for (int ks = 0; ks < 8; ++ks) {
-                bf16x8 a[4];
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt)
-                    a[mt] = __builtin_bit_cast(
-                        bf16x8, *(const u32x4 *)(Ks + (32 * mt + n) * kKPitch + 16 * ks + 8 * hb));
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt) acc_s[mt] = mfma_32x32x16(a[mt], qb[ks], acc_s[mt]);
-            }
-
+        const uint8_t *Kt = smem + (u & 1) * kStageBytes;
+        const uint8_t *Vt = Kt + kTileBytes;
+        if ((umask >> (2 * wave)) & 3) {
             const bool sel = tok_ok && ((umask >> my_tok) & 1);
-            const bool diag = (b == c);
-            float mloc = -INFINITY;
+            // two 64-key halves, each a full S / softmax / PV round
+#pragma unroll 1
+            for (int hf = 0; hf < 2; ++hf) {
+                f32x16 acc_s[2];
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
+                for (int mt = 0; mt < 2; ++mt) acc_s[mt] = f32x16{};
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int kp = b * kBlock + 32 * mt + 8 * (r >> 2) + 4 * hb + (r & 3);
-                    const bool ok = sel && (!diag || kp <= my_p);
-                    const float s = ok ? acc_s[mt][r] * scale_log2 : -INFINITY;
-                    acc_s[mt][r] = s;
-                    mloc = fmaxf(mloc, s);
+                for (int ks = 0; ks < 8; ++ks) {
+                    bf16x8 a[2];
+                    const int pos = ((2 * ks + hb) ^ k_swz) << 4;
+#pragma unroll
+                    for (int mt = 0; mt < 2; ++mt)
+                        a[mt] = __builtin_bit_cast(
+                            bf16x8, *(const u32x4 *)(Kt + (64 * hf + 32 * mt + n) * kRowBytes + pos));
+#pragma unroll
+                    for (int mt = 0; mt < 2; ++mt) acc_s[mt] = mfma_32x32x16(a[mt], qb[ks], acc_s[mt]);
                 }
-            mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-            const float m_new = fmaxf(m_run, mloc);
-            const float base = m_new == -INFINITY ? 0.f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f(m_run - base);
-            m_run = m_new;
-            float psum = 0.f;
+
+                // mask to -inf: columns whose token did not select b; keys
+                // after the query inside its own block
+                float mloc = -INFINITY;
+                if (b == c) {
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
+                    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float p = __builtin_amdgcn_exp2f(acc_s[mt][r] - base);
-                    acc_s[mt][r] = p;
-                    psum += p;
+                        for (int r = 0; r < 16; ++r) {
+                            const int kp = b * kBlock + 64 * hf + 32 * mt + 8 * (r >> 2) + 4 * hb + (r & 3);
+                            const float sv = (sel && kp <= my_p) ? acc_s[mt][r] : -INFINITY;
+                            acc_s[mt][r] = sv;
+                            mloc = fmaxf(mloc, sv);
+                        }
+                } else {
+#pragma unroll
+                    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const float sv = sel ? acc_s[mt][r] : -INFINITY;
+                            acc_s[mt][r] = sv;
+                            mloc = fmaxf(mloc, sv);
+                        }
                 }
-            l_run = l_run * alpha + psum;
+                mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+                // lazy reference: move it (and rescale) only on a large increase
+                const bool grow = mloc > m_ref &&
+                                  (m_ref == -INFINITY || (mloc - m_ref) * scale_log2 > kLazyLog2);
+                if (__ballot(grow)) {
+                    const float m_new = grow ? mloc : m_ref;
+                    const float alpha = m_ref == -INFINITY
+                                            ? 0.f
+                                            : __builtin_amdgcn_exp2f((m_ref - m_new) * scale_log2);
+                    l_run *= alpha;
 #pragma unroll
-            for (int dt = 0; dt < 4; ++dt) acc_o[dt] *= alpha;
+                    for (int dt = 0; dt < 4; ++dt) acc_o[dt] *= alpha;
+                    m_ref = m_new;
+                }
+                const float mb = m_ref == -INFINITY ? 0.f : m_ref * scale_log2;
+                float psum = 0.f;
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const float pv = __builtin_amdgcn_exp2f(acc_s[mt][r] * scale_log2 - mb);
+                        acc_s[mt][r] = pv;
+                        psum += pv;
+                    }
+                l_run += psum;
 
 #pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                bf16x8 pb;
+                for (int s4 = 0; s4 < 4; ++s4) {
+                    const int s = 4 * hf + s4;  // 16-key PV step within the block
+                    bf16x8 pb;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) pb[i] = (__bf16)acc_s[s >> 1][8 * (s & 1) + i];
+                    for (int i = 0; i < 8; ++i) pb[i] = (__bf16)acc_s[s4 >> 1][8 * (s4 & 1) + i];
 #pragma unroll
-                for (int dt = 0; dt < 4; ++dt) {
-                    const uint16_t *row = Vt + (32 * dt + n) * kVPitch + 16 * s + 4 * hb;
-                    const u32x2 lo = *(const u32x2 *)(row);
-                    const u32x2 hi = *(const u32x2 *)(row + 8);
-                    const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-                    acc_o[dt] = mfma_32x32x16(a, pb, acc_o[dt]);
+                    for (int dt = 0; dt < 4; ++dt) {
+                        i16x4 t[2];
+#pragma unroll
+                        for (int h2 = 0; h2 < 2; ++h2) {
+                            const int row = 16 * s + v_off[h2];
+                            const int col = 32 * dt + v_col;
+                            const int chunk = (col >> 3) ^ swz(row);
+                            t[h2] = ds_read_tr16(Vt + row * kRowBytes + (chunk << 4) + ((col & 7) << 1));
+                        }
+                        const i16x8 ab = {t[0][0], t[0][1], t[0][2], t[0][3],
+                                          t[1][0], t[1][1], t[1][2], t[1][3]};
+                        acc_o[dt] = mfma_32x32x16(__builtin_bit_cast(bf16x8, ab), pb, acc_o[dt]);
+                    }
                 }
             }
         }
-        __syncthreads();
+        barrier_keep_prefetch();  // stage u&1 is refilled by the next iteration's prefetch
     }
 
     // ---- epilogue: normalise and store bf16
@@ -277,10 +329,11 @@ hipError_t launch_attend_prefill(const uint16_t *q, const uint16_t *k, const uin
                                  const int32_t *tile_off, int ndocs, int T, int max_seqlen,
                                  float scale, uint16_t *out, hipStream_t stream) {
     (void)max_seqlen;
-    const int grid = ceil_div(T, kAttnTile) + ndocs;
-    const size_t lds = size_t(kKBytes) + size_t(kVBytes);
-    hipLaunchKernelGGL(attend_prefill_kernel, dim3(grid, kKvHeads), dim3(256), lds, stream, q, k, v,
-                       q2k, topk, docs, tile_off, ndocs, T, scale * kLog2e, out);
+    const int max_tiles = ceil_div(T, kTok) + ndocs;  // document-aligned tiles (upper bound)
+    const int grid = 8 * 8 * ceil_div(max_tiles, 16);  // 8 XCDs x slots
+    const size_t lds = size_t(kStages) * kStageBytes;
+    hipLaunchKernelGGL(attend_prefill_kernel, dim3(grid), dim3(kThreads), lds, stream, q, k, v, q2k,
+                       topk, docs, tile_off, ndocs, T, scale * kLog2e, out);
     return hipGetLastError();
 }
 

@@ -10,7 +10,7 @@
 namespace msa {
 
 constexpr int kScoreTile = 64;   // query tokens per block-scorer workgroup
-constexpr int kAttnTile = 8;     // query tokens per prefill-attention workgroup
+constexpr int kAttnTile = 16;    // query tokens per prefill-attention workgroup
 
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
