@@ -189,13 +189,24 @@ __global__ __launch_bounds__(kThreads) void attend_prefill_kernel(
     float m_ref = -INFINITY;  // raw-score reference of the exponentials
     float l_run = 0.f;
 
-    // lane-constant LDS offsets
-    const int k_swz = swz(n);              // rows 32mt + n share n's low 4 bits
-    const int G = lane >> 4, gi = lane & 15;
-    const int v_col = 16 * (G & 1) + 4 * (gi & 3);  // + 32 dt
-    int v_off[2];                                    // row within the 16-key PV step
+    // Lane-constant LDS byte offsets; the row parts that vary with the
+    // unrolled loop indices (32mt, 64hf rows; 16s rows) are compile-time
+    // immediates because swz() only depends on a row's low 4 bits.
+    int k_off[8];                  // K operand: row n, chunk 2ks+hb
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) v_off[h2] = 8 * h2 + 4 * (G >> 1) + (gi >> 2);
+    for (int ks = 0; ks < 8; ++ks) k_off[ks] = n * kRowBytes + (((2 * ks + hb) ^ swz(n)) << 4);
+    int v_off[4][2];               // V^T operand: row 4*(G/2) + gi/4 (+8 h2), column 32dt + ...
+    {
+        const int G = lane >> 4, gi = lane & 15;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                const int row = 8 * h2 + 4 * (G >> 1) + (gi >> 2);
+                const int col = 32 * dt + 16 * (G & 1) + 4 * (gi & 3);
+                v_off[dt][h2] = row * kRowBytes + ((((col >> 3) ^ swz(row))) << 4) + ((col & 7) << 1);
+            }
+    }
 
     if (nu > 0) issue_block(s_ublk[0], 0);
     for (int u = 0; u < nu; ++u) {
@@ -216,23 +227,25 @@ __global__ __launch_bounds__(kThreads) void attend_prefill_kernel(
             // two 64-key halves, each a full S / softmax / PV round
 #pragma unroll 1
             for (int hf = 0; hf < 2; ++hf) {
+                const uint8_t *Kh = Kt + 64 * hf * kRowBytes;
+                const uint8_t *Vh = Vt + 64 * hf * kRowBytes;
                 f32x16 acc_s[2];
 #pragma unroll
                 for (int mt = 0; mt < 2; ++mt) acc_s[mt] = f32x16{};
 #pragma unroll
                 for (int ks = 0; ks < 8; ++ks) {
                     bf16x8 a[2];
-                    const int pos = ((2 * ks + hb) ^ k_swz) << 4;
 #pragma unroll
                     for (int mt = 0; mt < 2; ++mt)
                         a[mt] = __builtin_bit_cast(
-                            bf16x8, *(const u32x4 *)(Kt + (64 * hf + 32 * mt + n) * kRowBytes + pos));
+                            bf16x8, *(const u32x4 *)(Kh + 32 * mt * kRowBytes + k_off[ks]));
 #pragma unroll
                     for (int mt = 0; mt < 2; ++mt) acc_s[mt] = mfma_32x32x16(a[mt], qb[ks], acc_s[mt]);
                 }
 
-                // mask to -inf: columns whose token did not select b; keys
-                // after the query inside its own block
+                // Column mask (token did not select b) goes into the exp2
+                // offset; the per-key causal mask is only needed in the
+                // query's own block.
                 float mloc = -INFINITY;
                 if (b == c) {
 #pragma unroll
@@ -240,7 +253,7 @@ __global__ __launch_bounds__(kThreads) void attend_prefill_kernel(
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
                             const int kp = b * kBlock + 64 * hf + 32 * mt + 8 * (r >> 2) + 4 * hb + (r & 3);
-                            const float sv = (sel && kp <= my_p) ? acc_s[mt][r] : -INFINITY;
+                            const float sv = kp <= my_p ? acc_s[mt][r] : -INFINITY;
                             acc_s[mt][r] = sv;
                             mloc = fmaxf(mloc, sv);
                         }
@@ -248,12 +261,9 @@ __global__ __launch_bounds__(kThreads) void attend_prefill_kernel(
 #pragma unroll
                     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const float sv = sel ? acc_s[mt][r] : -INFINITY;
-                            acc_s[mt][r] = sv;
-                            mloc = fmaxf(mloc, sv);
-                        }
+                        for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, acc_s[mt][r]);
                 }
+                mloc = sel ? mloc : -INFINITY;
                 mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
                 // lazy reference: move it (and rescale) only on a large increase
                 const bool grow = mloc > m_ref &&
@@ -268,7 +278,8 @@ __global__ __launch_bounds__(kThreads) void attend_prefill_kernel(
                     for (int dt = 0; dt < 4; ++dt) acc_o[dt] *= alpha;
                     m_ref = m_new;
                 }
-                const float mb = m_ref == -INFINITY ? 0.f : m_ref * scale_log2;
+                // unselected columns: offset +inf makes every exponential 0
+                const float mb = !sel ? INFINITY : (m_ref == -INFINITY ? 0.f : m_ref * scale_log2);
                 float psum = 0.f;
 #pragma unroll
                 for (int mt = 0; mt < 2; ++mt)
@@ -281,8 +292,7 @@ __global__ __launch_bounds__(kThreads) void attend_prefill_kernel(
                 l_run += psum;
 
 #pragma unroll
-                for (int s4 = 0; s4 < 4; ++s4) {
-                    const int s = 4 * hf + s4;  // 16-key PV step within the block
+                for (int s4 = 0; s4 < 4; ++s4) {  // 16-key PV steps of this half
                     bf16x8 pb;
 #pragma unroll
                     for (int i = 0; i < 8; ++i) pb[i] = (__bf16)acc_s[s4 >> 1][8 * (s4 & 1) + i];
@@ -290,12 +300,8 @@ __global__ __launch_bounds__(kThreads) void attend_prefill_kernel(
                     for (int dt = 0; dt < 4; ++dt) {
                         i16x4 t[2];
 #pragma unroll
-                        for (int h2 = 0; h2 < 2; ++h2) {
-                            const int row = 16 * s + v_off[h2];
-                            const int col = 32 * dt + v_col;
-                            const int chunk = (col >> 3) ^ swz(row);
-                            t[h2] = ds_read_tr16(Vt + row * kRowBytes + (chunk << 4) + ((col & 7) << 1));
-                        }
+                        for (int h2 = 0; h2 < 2; ++h2)
+                            t[h2] = ds_read_tr16(Vh + 16 * s4 * kRowBytes + v_off[dt][h2]);
                         const i16x8 ab = {t[0][0], t[0][1], t[0][2], t[0][3],
                                           t[1][0], t[1][1], t[1][2], t[1][3]};
                         acc_o[dt] = mfma_32x32x16(__builtin_bit_cast(bf16x8, ab), pb, acc_o[dt]);
