@@ -17,8 +17,8 @@
 //       request); 4 waves x 32 keys: S^T = K Q^T and O^T = V^T P^T on MFMA
 //       16x16x32 (16 query heads = N), partial softmax merged across waves in
 //       LDS, one (O, m, l) partial per selected block written to workspace.
-//   decode_combine_kernel - per (request, query head): log-sum-exp merge of
-//       the partials in fixed block order, bf16 output.
+//   decode_combine_kernel - per (request, KV head): log-sum-exp merge of the
+//       topk partials in fixed block order, bf16 output.
 #include "msa_internal.hpp"
 
 namespace msa {
@@ -68,19 +68,20 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(
             acc[mt] = mfma_16x16x128_e4m3(a, qb, f32x4{});
         }
     } else {
-        // lane (m, qd), step ks holds d = 32qd + 8ks .. +7 (64 contiguous bytes per lane).
+        // lane (m, qd), step ks holds 16-byte chunk 4ks + qd of its row (the
+        // four lanes of a row read 64 contiguous bytes per instruction).
         bf16x8 qb[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
             qb[ks] = n < kIdxHeads
-                         ? __builtin_bit_cast(bf16x8, *(const u32x4 *)(qrow + 2 * (32 * qd + 8 * ks)))
+                         ? __builtin_bit_cast(bf16x8, *(const u32x4 *)(qrow + 16 * (4 * ks + qd)))
                          : bf16x8{};
         u32x4 ka[8][4];
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks)
-                ka[mt][ks] = *(const u32x4 *)(kbase + (16 * mt + n) * kRowBytes + 2 * (32 * qd + 8 * ks));
+                ka[mt][ks] = *(const u32x4 *)(kbase + (16 * mt + n) * kRowBytes + 16 * (4 * ks + qd));
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
             acc[mt] = f32x4{};
@@ -119,11 +120,8 @@ hipError_t launch_decode_scores(const void *iq, const void *ikc, bool fp8, const
 // ---------------------------------------------------------------------------
 // G5: top-k per (request, index head), one wave each
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-    return v;
-}
+// Number of lanes whose predicate holds, summed over the wave (scalar).
+__device__ __forceinline__ int wave_count(bool pred) { return __popcll(__ballot(pred)); }
 
 template <int kCpl>  // candidates per lane: blocks lane + 64*i
 __global__ __launch_bounds__(256) void decode_topk_kernel(const float *__restrict__ S,
@@ -153,16 +151,14 @@ __global__ __launch_bounds__(256) void decode_topk_kernel(const float *__restric
             const uint32_t trial = thr | (1u << bit);
             int cnt = 0;
 #pragma unroll
-            for (int i = 0; i < kCpl; ++i) cnt += u[i] >= trial;
-            if (wave_sum(cnt) >= R) thr = trial;
+            for (int i = 0; i < kCpl; ++i) cnt += wave_count(u[i] >= trial);
+            if (cnt >= R) thr = trial;
         }
     }
     int n_gt = 0;
     if (R > 0) {
-        int cnt = 0;
 #pragma unroll
-        for (int i = 0; i < kCpl; ++i) cnt += u[i] > thr;
-        n_gt = wave_sum(cnt);
+        for (int i = 0; i < kCpl; ++i) n_gt += wave_count(u[i] > thr);
     }
     const int ties_wanted = R > 0 ? R - n_gt : 0;  // equal-to-threshold picks, lowest ids first
     int ties_seen = 0, emitted = 0;
@@ -210,28 +206,35 @@ hipError_t launch_decode_topk(const float *S, const int32_t *ctx, int B, int max
 // G6: attention over one selected block per workgroup
 // ---------------------------------------------------------------------------
 namespace {
-constexpr int kDVPitch = 32 + 4;  // bf16 per V^T row (32 keys + pad) per wave
-constexpr int kDecVtBytes = kDim * kDVPitch * 2;
+constexpr int kRowB = kDim * 2;          // 256-byte K/V row of one head
+constexpr int kWaveVBytes = 32 * kRowB;  // 32 keys per wave
 
-__device__ __forceinline__ u32x2 pick_col4(const u32x4 (&r)[4], int dd) {
-    const int dp = dd >> 1;
-    const bool high = dd & 1;
-    uint32_t e[4];
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) e[kk] = high ? (r[kk][dp] >> 16) : (r[kk][dp] & 0xFFFFu);
-    return u32x2{e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
-}
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// 16-byte chunk c of V row r sits at chunk position c ^ vswz(r); any 16
+// consecutive rows map one chunk to 16 distinct positions.
+__device__ __forceinline__ int vswz(int r) { return r & 15; }
 }  // namespace
 
+// Workgroup (s, g, r): selected block s of KV head g for request r; 4 waves,
+// wave w owns keys 32w..32w+31 of the block.
+//   S^T[32 keys x 16 heads] = K . Q^T   (MFMA 16x16x32, K straight from HBM)
+//   per-wave softmax partial, V rows copied HBM -> LDS (global_load_lds),
+//   O^T[128 x 16] = V^T . P^T with V^T from ds_read_b64_tr_b16,
+//   the 4 waves merged in LDS into one (O, m, l) partial of the block.
 __global__ __launch_bounds__(256) void decode_attend_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc, const uint16_t *__restrict__ vc,
-    const int32_t *__restrict__ pt, int max_pages, const int32_t *__restrict__ ctx, int max_ctx, int B,
-    const int32_t *__restrict__ q2k, int topk, float scale_log2, float *__restrict__ part_o,
+    const int32_t *__restrict__ pt, int max_pages, const int32_t *__restrict__ ctx, int max_ctx,
+    int B, const int32_t *__restrict__ q2k, int topk, float scale_log2, float *__restrict__ part_o,
     float *__restrict__ part_ml) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[4 * kDecVtBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * kWaveVBytes];  // V, then O^T
     __shared__ float s_m[4][16], s_l[4][16];
     const int s = blockIdx.x, g = blockIdx.y, r = blockIdx.z;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 15, qd = lane >> 4;
     const size_t pidx = (size_t(r) * kKvHeads + g) * topk + s;
     float *po = part_o + pidx * (kGroup * kDim);
@@ -240,116 +243,106 @@ __global__ __launch_bounds__(256) void decode_attend_kernel(
     const int L = min(max(ctx[r], 1), max_ctx);
     const int c = (L - 1) / kBlock;
     const int b = q2k[(size_t(g) * B + r) * topk + s];
-    if (b < 0 || b > c) {
-        if (tid < kGroup) {
-            pml[2 * tid] = -INFINITY;
-            pml[2 * tid + 1] = 0.f;
+    if (b >= 0 && b <= c) {
+        const size_t slot0 = size_t(pt[size_t(r) * max_pages + b]) * kBlock;
+        const int key0 = 32 * wave;
+        const int kmax = L - 1 - b * kBlock;  // last valid key of the block
+        uint8_t *vt = smem + wave * kWaveVBytes;
+
+        // V rows key0..key0+31 -> LDS (8 one-KiB copies); rows past L re-read
+        // the last valid row (their probabilities are 0).
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int rr = 4 * j + (lane >> 4);  // row within the wave's 32
+            const int chunk = (lane & 15) ^ vswz(rr);
+            const int key = min(key0 + rr, kmax);
+            const uint16_t *src = vc + ((slot0 + key) * kKvHeads + g) * kDim + 8 * chunk;
+            __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(vt + j * 1024), 16, 0, 0);
         }
-        return;
-    }
-    const size_t slot0 = size_t(pt[size_t(r) * max_pages + b]) * kBlock;
-    const int key0 = 32 * wave;  // this wave's keys within the block
-
-    // Q^T operand: lane (n = head, qd), step ks: d = 32qd + 8ks .. +7
-    const uint16_t *qrow = q + (size_t(r) * kHeads + g * kGroup + n) * kDim;
-    bf16x8 qb[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-        qb[ks] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qrow + 32 * qd + 8 * ks));
-
-    // K operand: M-tile mt = keys key0 + 16mt + m, same d order as Q
-    u32x4 ka[2][4];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-        const uint16_t *src = kc + ((slot0 + key0 + 16 * mt + n) * kKvHeads + g) * kDim + 32 * qd;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) ka[mt][ks] = *(const u32x4 *)(src + 8 * ks);
-    }
-    // V: 2 items of 4 keys x 8 d per lane (keys 4kg.., d 8dg..)
-    u32x4 vr[2][4];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int item = lane + 64 * j;
-        const int dg = item & 15, kg = item >> 4;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const int key = key0 + 4 * kg + kk;
-            const bool ok = b * kBlock + key < L;  // slots past L may hold NaN
-            vr[j][kk] = ok ? *(const u32x4 *)(vc + ((slot0 + key) * kKvHeads + g) * kDim + 8 * dg)
-                           : u32x4{0, 0, 0, 0};
-        }
-    }
-
-    f32x4 sacc[2];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-        sacc[mt] = f32x4{};
+        // Q^T operand: lane (n = head, qd), step ks: 16-byte chunk 4ks + qd
+        const uint16_t *qrow = q + (size_t(r) * kHeads + g * kGroup + n) * kDim;
+        bf16x8 qb[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
-            sacc[mt] = mfma_16x16x32(__builtin_bit_cast(bf16x8, ka[mt][ks]), qb[ks], sacc[mt]);
-    }
-
-    // stage V^T for this wave
-    uint16_t *vt = (uint16_t *)(smem + wave * kDecVtBytes);
+            qb[ks] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qrow + 8 * (4 * ks + qd)));
+        // K operand: M-tile mt = keys key0 + 16mt + m, same chunk order
+        u32x4 ka[2][4];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int item = lane + 64 * j;
-        const int dg = item & 15, kg = item >> 4;
+        for (int mt = 0; mt < 2; ++mt) {
+            const int key = min(key0 + 16 * mt + n, kmax);
+            const uint16_t *src = kc + ((slot0 + key) * kKvHeads + g) * kDim;
 #pragma unroll
-        for (int dd = 0; dd < 8; ++dd) *(u32x2 *)(vt + (8 * dg + dd) * kDVPitch + 4 * kg) = pick_col4(vr[j], dd);
-    }
-
-    // softmax over this wave's 32 keys, per head column n
-    float mloc = -INFINITY;
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int j = b * kBlock + key0 + 16 * mt + 4 * qd + i;
-            const float z = j < L ? sacc[mt][i] * scale_log2 : -INFINITY;
-            sacc[mt][i] = z;
-            mloc = fmaxf(mloc, z);
+            for (int ks = 0; ks < 4; ++ks) ka[mt][ks] = *(const u32x4 *)(src + 8 * (4 * ks + qd));
         }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    const float base = mloc == -INFINITY ? 0.f : mloc;
-    float psum = 0.f;
-    bf16x8 pb;
+        f32x4 sacc[2];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+        for (int mt = 0; mt < 2; ++mt) {
+            sacc[mt] = f32x4{};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float p = __builtin_amdgcn_exp2f(sacc[mt][i] - base);
-            psum += p;
-            pb[4 * mt + i] = (__bf16)p;
+            for (int ks = 0; ks < 4; ++ks)
+                sacc[mt] = mfma_16x16x32(__builtin_bit_cast(bf16x8, ka[mt][ks]), qb[ks], sacc[mt]);
         }
-    psum += __shfl_xor(psum, 16);
-    psum += __shfl_xor(psum, 32);
-    __syncthreads();
+        // softmax over this wave's 32 keys for head column n (lane holds keys
+        // 16mt + 4qd + i of its column)
+        float mloc = -INFINITY;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool ok = key0 + 16 * mt + 4 * qd + i <= kmax;
+                const float z = ok ? sacc[mt][i] * scale_log2 : -INFINITY;
+                sacc[mt][i] = z;
+                mloc = fmaxf(mloc, z);
+            }
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+        const float base = mloc == -INFINITY ? 0.f : mloc;
+        float psum = 0.f;
+        bf16x8 pb;  // P^T operand: keys 4qd + e (tile 0) then 16 + 4qd + e (tile 1)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float p = __builtin_amdgcn_exp2f(sacc[mt][i] - base);
+                psum += p;
+                pb[4 * mt + i] = (__bf16)p;
+            }
+        psum += __shfl_xor(psum, 16);
+        psum += __shfl_xor(psum, 32);
 
-    // O^T[d x heads] = V^T . P^T; lane (m = d, qd) reads keys 4qd.. and 16+4qd..
-    f32x4 oacc[8];
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's V rows are in LDS
+        // O^T[d x heads] = V^T . P^T.  Transposing read: in lane group qd, lane
+        // i supplies row (16h + 4qd + i/4), columns 16dt + 4(i%4)..+3, and
+        // lane j receives V[row0 + e][16dt + j] for e = 0..3.
+        f32x4 oacc[8];
+        const int gi = lane & 15;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-        const uint16_t *row = vt + (16 * dt + n) * kDVPitch + 4 * qd;
-        const u32x2 lo = *(const u32x2 *)row;
-        const u32x2 hi = *(const u32x2 *)(row + 16);
-        oacc[dt] = mfma_16x16x32(__builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]}), pb, f32x4{});
-    }
-    __syncthreads();  // V^T no longer needed: reuse LDS for the cross-wave merge
-
-    float *so = (float *)smem;  // [4 waves][16 heads][128 d]
+        for (int dt = 0; dt < 8; ++dt) {
+            i16x4 t[2];
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
+            for (int h = 0; h < 2; ++h) {
+                const int rr = 16 * h + 4 * qd + (gi >> 2);
+                const int col = 16 * dt + 4 * (gi & 3);
+                const int pos = ((col >> 3) ^ vswz(rr)) << 4;
+                t[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_i16x4 *)(vt + rr * kRowB + pos + ((col & 7) << 1)));
+            }
+            const i16x8 ab = {t[0][0], t[0][1], t[0][2], t[0][3], t[1][0], t[1][1], t[1][2], t[1][3]};
+            oacc[dt] = mfma_16x16x32(__builtin_bit_cast(bf16x8, ab), pb, f32x4{});
+        }
+        // wave partial O^T -> LDS (over this wave's own V rows, already consumed)
+        float *so = (float *)vt;  // [16 heads][128 d]
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-        for (int i = 0; i < 4; ++i) so[(wave * kGroup + n) * kDim + 16 * dt + 4 * qd + i] = oacc[dt][i];
-    if (qd == 0) {
-        s_m[wave][n] = mloc;
-        s_l[wave][n] = psum;
-    }
-    __syncthreads();
-    // merge: thread -> (head hh, 8 d)
-    {
+        for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) so[n * kDim + 16 * dt + 4 * qd + i] = oacc[dt][i];
+        if (qd == 0) {
+            s_m[wave][n] = mloc;
+            s_l[wave][n] = psum;
+        }
+        __syncthreads();
+        // merge the 4 waves: thread -> (head hh, 8 d)
         const int hh = tid >> 4, d0 = (tid & 15) * 8;
         float mw[4], M = -INFINITY;
 #pragma unroll
@@ -366,7 +359,8 @@ __global__ __launch_bounds__(256) void decode_attend_kernel(
         for (int e = 0; e < 8; ++e) {
             float acc = 0.f;
 #pragma unroll
-            for (int w = 0; w < 4; ++w) acc += sc[w] * so[(w * kGroup + hh) * kDim + d0 + e];
+            for (int w = 0; w < 4; ++w)
+                acc += sc[w] * ((const float *)(smem + w * kWaveVBytes))[hh * kDim + d0 + e];
             o[e] = acc;
         }
         *(f32x4 *)(po + hh * kDim + d0) = f32x4{o[0], o[1], o[2], o[3]};
@@ -375,41 +369,69 @@ __global__ __launch_bounds__(256) void decode_attend_kernel(
             pml[2 * hh] = M;
             pml[2 * hh + 1] = l;
         }
+    } else {
+        // unselected slot: an empty partial (zero O, m = -inf, l = 0)
+        const int hh = tid >> 4, d0 = (tid & 15) * 8;
+        *(f32x4 *)(po + hh * kDim + d0) = f32x4{};
+        *(f32x4 *)(po + hh * kDim + d0 + 4) = f32x4{};
+        if (tid < kGroup) {
+            pml[2 * tid] = -INFINITY;
+            pml[2 * tid + 1] = 0.f;
+        }
     }
 }
 
 // ---------------------------------------------------------------------------
-// G7: combine the per-block partials
+// G7: merge the topk partials of each (request, KV head) in fixed block order
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(128) void decode_combine_kernel(const float *__restrict__ part_o,
+__global__ __launch_bounds__(256) void decode_combine_kernel(const float *__restrict__ part_o,
                                                              const float *__restrict__ part_ml,
                                                              int topk, uint16_t *__restrict__ out) {
-    const int h = blockIdx.x, r = blockIdx.y, dd = threadIdx.x;
-    const int g = h / kGroup, hh = h % kGroup;
+    const int g = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
     const size_t base = (size_t(r) * kKvHeads + g) * topk;
-    float M = -INFINITY;
-    for (int s = 0; s < topk; ++s) M = fmaxf(M, part_ml[(base + s) * (kGroup * 2) + 2 * hh]);
-    float num = 0.f, den = 0.f;
-    if (M != -INFINITY) {
-        for (int s = 0; s < topk; ++s) {
-            const float m = part_ml[(base + s) * (kGroup * 2) + 2 * hh];
-            if (m == -INFINITY) continue;
-            const float w = __builtin_amdgcn_exp2f(m - M);
-            den += w * part_ml[(base + s) * (kGroup * 2) + 2 * hh + 1];
-            num += w * part_o[(base + s) * (kGroup * kDim) + hh * kDim + dd];
-        }
+    const int hh = tid >> 4, d0 = (tid & 15) * 8;  // head, 8 d
+    // every load independent of the others (no data-dependent branches)
+    float mt[kMaxTopk], lt[kMaxTopk];
+    f32x4 oa[kMaxTopk], ob[kMaxTopk];
+#pragma unroll
+    for (int t = 0; t < kMaxTopk; ++t) {
+        const bool ok = t < topk;
+        const float *ml = part_ml + (base + t) * (kGroup * 2) + 2 * hh;
+        const float *src = part_o + (base + t) * (kGroup * kDim) + hh * kDim + d0;
+        mt[t] = ok ? ml[0] : -INFINITY;
+        lt[t] = ok ? ml[1] : 0.f;
+        oa[t] = ok ? *(const f32x4 *)src : f32x4{};
+        ob[t] = ok ? *(const f32x4 *)(src + 4) : f32x4{};
     }
-    const float o = den > 0.f ? num / den : 0.f;
-    out[(size_t(r) * kHeads + h) * kDim + dd] = __builtin_bit_cast(uint16_t, (__bf16)o);
+    float M = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < kMaxTopk; ++t) M = fmaxf(M, mt[t]);
+    const float baseM = M == -INFINITY ? 0.f : M;
+    f32x4 na = {}, nb = {};
+    float den = 0.f;
+#pragma unroll
+    for (int t = 0; t < kMaxTopk; ++t) {
+        const float w = mt[t] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mt[t] - baseM);
+        den += w * lt[t];
+        na += w * oa[t];
+        nb += w * ob[t];
+    }
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+    bf16x8 o8;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        o8[e] = (__bf16)(na[e] * inv);
+        o8[4 + e] = (__bf16)(nb[e] * inv);
+    }
+    *(bf16x8 *)(out + (size_t(r) * kHeads + g * kGroup + hh) * kDim + d0) = o8;
 }
 
 hipError_t launch_decode_attend(const uint16_t *q, const uint16_t *kc, const uint16_t *vc,
                                 const int32_t *pt, int max_pages, const int32_t *ctx, int max_ctx, int B,
                                 const int32_t *q2k, int topk, float scale, float *partial,
-                                uint16_t *out, hipStream_t stream) {
+                                hipStream_t stream) {
     float *part_o = partial;
     float *part_ml = partial + size_t(B) * kKvHeads * topk * kGroup * kDim;
-    (void)out;
     hipLaunchKernelGGL(decode_attend_kernel, dim3(topk, kKvHeads, B), dim3(256), 0, stream, q, kc, vc,
                        pt, max_pages, ctx, max_ctx, B, q2k, topk, scale * kLog2e, part_o, part_ml);
     return hipGetLastError();
@@ -419,7 +441,7 @@ hipError_t launch_decode_combine(const float *partial, int B, int topk, uint16_t
                                  hipStream_t stream) {
     const float *part_o = partial;
     const float *part_ml = partial + size_t(B) * kKvHeads * topk * kGroup * kDim;
-    hipLaunchKernelGGL(decode_combine_kernel, dim3(kHeads, B), dim3(128), 0, stream, part_o, part_ml,
+    hipLaunchKernelGGL(decode_combine_kernel, dim3(kKvHeads, B), dim3(256), 0, stream, part_o, part_ml,
                        topk, out);
     return hipGetLastError();
 }

@@ -290,7 +290,7 @@ msa_status msa_sparse_attend_decode_paged(
     if (e != hipSuccess) return hip_fail(e, "decode_topk");
     tm.mark(s, "decode_attend");
     e = launch_decode_attend(q, k_cache, v_cache, page_table, max_pages_per_seq, context_lens,
-                             max_context_len, batch, q2k, topk, softmax_scale, part, out, s);
+                             max_context_len, batch, q2k, topk, softmax_scale, part, s);
     if (e != hipSuccess) return hip_fail(e, "decode_attend");
     tm.mark(s, "decode_combine");
     e = launch_decode_combine(part, batch, topk, out, s);

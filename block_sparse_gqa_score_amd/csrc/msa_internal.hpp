@@ -45,7 +45,7 @@ hipError_t launch_decode_topk(const float *S, const int32_t *ctx, int B, int max
 hipError_t launch_decode_attend(const uint16_t *q, const uint16_t *kc, const uint16_t *vc,
                                 const int32_t *pt, int max_pages, const int32_t *ctx, int max_ctx, int B,
                                 const int32_t *q2k, int topk, float scale, float *partial,
-                                uint16_t *out, hipStream_t stream);
+                                hipStream_t stream);
 hipError_t launch_decode_combine(const float *partial, int B, int topk, uint16_t *out,
                                  hipStream_t stream);
 
