@@ -9,9 +9,13 @@ the 32768-token planted prefill (select + attend) is attached under
 timing; L2 and the 256 MB MALL are flushed before every step (outside the
 timed span) by READING a 1 GiB buffer: a write-based flush would leave the
 Infinity Cache full of dirty lines whose write-back the next step's reads
-would pay for (measured: 2.6 vs 5.5 TB/s on a 168 MB paged read).  Each step is timed with HIP events on the stream
-the kernels run on; per-kernel times come from events the library records
-around each of its launches (msa_set_timing_events).
+would pay for (measured: 2.6 vs 5.5 TB/s on a 168 MB paged read).
+
+Each step is timed with HIP events on the stream the kernels run on.  The
+decode step is timed twice: with direct launches, where per-kernel times
+come from events the library records around each of its launches
+(msa_set_timing_events), and replayed from a captured HIP graph, whose time
+is the headline value.
 
 Prints ONE JSON line.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -40,6 +44,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-flush", action="store_true", help="do not flush L2/MALL between steps")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time direct launches only (default: the decode step is also captured "
+                         "into a HIP graph and the replay time is the headline value)")
     return ap.parse_args()
 
 
@@ -163,6 +170,29 @@ def bench_decode(args, hip, flush):
 
     step_ms, evs, names = timed_steps(run, args.steps, args.warmup, hip, stream, flush, 5)
     kt = kernel_times(evs, [names], hip)
+    graph_ms = None
+    if not args.no_graph:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            gstream = torch.cuda.current_stream().cuda_stream
+            with torch.cuda.graph(g, stream=s):
+                st = L.msa_sparse_attend_decode_paged(
+                    P(dq), P(diq), P(dk), P(dv), P(dik), 0, P(dpt), d.max_pages, P(dctx), d.B,
+                    d.max_context_len, d.topk, d.init_blocks, d.local_blocks, d.scale, P(out), None,
+                    P(ws), ws.numel(), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+                assert st == 0
+        torch.cuda.current_stream().wait_stream(s)
+        ga, gb = hip.events(args.steps), hip.events(args.steps)
+        for i in range(args.steps):
+            if flush is not None:
+                flush.sum()
+            hip.record(ga[i], stream)
+            g.replay()
+            hip.record(gb[i], stream)
+        torch.cuda.synchronize()
+        graph_ms = stats([hip.elapsed_ms(ga[i], gb[i]) for i in range(args.steps)])
 
     # algorithmic bytes (per request: index-K rows, selected K/V rows, q/iq/out, page table)
     lens = d.context_lens.astype(np.int64)
@@ -175,7 +205,7 @@ def bench_decode(args, hip, flush):
     alg = {"decode_scores": idx_bytes, "decode_attend": kv_bytes + d.B * 64 * 128 * 2}
     dom = max(alg, key=lambda k: per_kernel.get(k, 0.0))
     return dict(d=d, gen_s=gen_s, step=stats(step_ms), per_kernel_ms=per_kernel, alg_bytes=alg,
-                dominant=dom, total_bytes=total_bytes, out=out)
+                dominant=dom, total_bytes=total_bytes, out=out, graph=graph_ms)
 
 
 def bench_prefill(args, hip, flush):
@@ -279,7 +309,9 @@ def main():
 
     dres = bench_decode(args, hip, flush)
     d = dres["d"]
-    step_ms = dres["step"]["mean"]
+    # headline: the step replayed from a HIP graph (how a serving loop issues
+    # decode); direct-launch times are reported beside it
+    step_ms = dres["graph"]["mean"] if dres["graph"] is not None else dres["step"]["mean"]
     dom = dres["dominant"]
     dom_ms = dres["per_kernel_ms"][dom]
     achieved = dres["alg_bytes"][dom] / (dom_ms * 1e-3) / 1e9
@@ -305,7 +337,9 @@ def main():
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": None, "alg_bytes_per_launch": dres["alg_bytes"][dom],
                      "avg_launch_us": round(dom_ms * 1e3, 3)},
-        "step_stats_ms": {k: round(v, 6) for k, v in dres["step"].items()},
+        "launch": "hip_graph_replay" if dres["graph"] is not None else "direct",
+        "step_stats_ms": {k: round(v, 6) for k, v in (dres["graph"] or dres["step"]).items()},
+        "direct_launch_step_ms": {k: round(v, 6) for k, v in dres["step"].items()},
         "per_kernel_us": {k: round(v * 1e3, 3) for k, v in dres["per_kernel_ms"].items()},
         "path_bytes_per_step": dres["total_bytes"],
         "path_hbm_frac": round(dres["total_bytes"] / (step_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),

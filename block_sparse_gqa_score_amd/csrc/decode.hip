@@ -384,12 +384,14 @@ __global__ __launch_bounds__(256) void decode_attend_kernel(
 // ---------------------------------------------------------------------------
 // G7: merge the topk partials of each (request, KV head) in fixed block order
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void decode_combine_kernel(const float *__restrict__ part_o,
-                                                             const float *__restrict__ part_ml,
-                                                             int topk, uint16_t *__restrict__ out) {
-    const int g = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
+// One 64-thread workgroup per (d quarter, KV head, request): thread ->
+// (head tid/4, 8 of the quarter's 32 d).
+__global__ __launch_bounds__(64) void decode_combine_kernel(const float *__restrict__ part_o,
+                                                            const float *__restrict__ part_ml,
+                                                            int topk, uint16_t *__restrict__ out) {
+    const int dq = blockIdx.x, g = blockIdx.y, r = blockIdx.z, tid = threadIdx.x;
     const size_t base = (size_t(r) * kKvHeads + g) * topk;
-    const int hh = tid >> 4, d0 = (tid & 15) * 8;  // head, 8 d
+    const int hh = tid >> 2, d0 = 32 * dq + (tid & 3) * 8;  // head, 8 d
     // every load independent of the others (no data-dependent branches)
     float mt[kMaxTopk], lt[kMaxTopk];
     f32x4 oa[kMaxTopk], ob[kMaxTopk];
@@ -441,7 +443,7 @@ hipError_t launch_decode_combine(const float *partial, int B, int topk, uint16_t
                                  hipStream_t stream) {
     const float *part_o = partial;
     const float *part_ml = partial + size_t(B) * kKvHeads * topk * kGroup * kDim;
-    hipLaunchKernelGGL(decode_combine_kernel, dim3(kKvHeads, B), dim3(256), 0, stream, part_o, part_ml,
+    hipLaunchKernelGGL(decode_combine_kernel, dim3(4, kKvHeads, B), dim3(64), 0, stream, part_o, part_ml,
                        topk, out);
     return hipGetLastError();
 }
