@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-flush", action="store_true", help="do not flush L2/MALL between steps")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (reference dispatch for scaling the "
+                         "FETCH_SIZE / WRITE_SIZE counters) and exit")
     ap.add_argument("--no-graph", action="store_true",
                     help="time direct launches only (default: the decode step is also captured "
                          "into a HIP graph and the replay time is the headline value)")
@@ -293,8 +296,46 @@ def cpu_baseline_prefill(w, seconds):
                 sample=f"{done} tokens drawn uniformly from the 32768-token document")
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+CSRC = os.path.join(ROOT, "block_sparse_gqa_score_amd", "csrc")
+
+
+def source_digest(filename):
+    import hashlib
+    with open(os.path.join(CSRC, filename), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or
+    None when absent or when the kernel's source changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        e = t["kernels"][kernel]
+        if source_digest(e["source"]) != e["source_sha"]:
+            return None
+        return int(round(e["fetch_kib"] * t["fetch_scale"] * 1024 + e["write_kib"] * t["write_scale"] * 1024))
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def calibrate_copy():
+    import torch
+    n = 1 << 30
+    x = torch.ones(n, dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n, "dispatches": 3}))
+
+
 def main():
     args = parse()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
               f"multi-GPU path: run with --gpus 1", file=sys.stderr)
@@ -335,7 +376,7 @@ def main():
                    "heads": "64q/4kv/4idx x 128", "l2_mall_flushed": flush is not None},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": None, "alg_bytes_per_launch": dres["alg_bytes"][dom],
+                     "traffic": measured_traffic(dom), "alg_bytes_per_launch": dres["alg_bytes"][dom],
                      "avg_launch_us": round(dom_ms * 1e3, 3)},
         "launch": "hip_graph_replay" if dres["graph"] is not None else "direct",
         "step_stats_ms": {k: round(v, 6) for k, v in (dres["graph"] or dres["step"]).items()},
@@ -360,7 +401,7 @@ def main():
                          "achieved": round(pres["attn_flops"] / (a_ms * 1e-3) / 1e12, 2),
                          "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(pres["attn_flops"] / (a_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                         "traffic": None, "alg_flops_per_launch": pres["attn_flops"],
+                         "traffic": measured_traffic("attend_prefill"), "alg_flops_per_launch": pres["attn_flops"],
                          "avg_launch_us": round(a_ms * 1e3, 3)},
             "block_scores": {"achieved_tflops": round(pres["score_flops"] / (s_ms * 1e-3) / 1e12, 2),
                              "frac": round(pres["score_flops"] / (s_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
