@@ -240,19 +240,19 @@ def bench_prefill(args, hip, flush):
         if st != 0:
             raise RuntimeError(L.msa_last_error().decode())
         if events is not None:
-            L.msa_set_timing_events(ctypes.c_void_p(ctypes.addressof(events) + 4 * 8), 3)
+            L.msa_set_timing_events(ctypes.c_void_p(ctypes.addressof(events) + 4 * 8), 4)
         st = L.msa_sparse_attend_prefill(P(q), P(k), P(v), P(q2k), w.topk, P(cu), w.num_docs, w.T,
                                          w.max_seqlen, w.scale, P(out), P(ws_a), ws_a.numel(),
                                          ctypes.c_void_p(stream))
         if st != 0:
             raise RuntimeError(L.msa_last_error().decode())
 
-    names_per_call = [["doc_setup", "block_scores", "topk_prefill"], ["doc_setup", "attend_prefill"]]
-    step_ms, evs, _ = timed_steps(run, args.prefill_steps, args.warmup, hip, stream, flush, 7)
+    step_ms, evs, _ = timed_steps(run, args.prefill_steps, args.warmup, hip, stream, flush, 8)
     kt = {}
     for arr in evs:
         for nm, (a, b) in {"doc_setup(select)": (0, 1), "block_scores": (1, 2), "topk_prefill": (2, 3),
-                           "doc_setup(attend)": (4, 5), "attend_prefill": (5, 6)}.items():
+                           "doc_setup(attend)": (4, 5), "vt_transpose": (5, 6),
+                           "attend_prefill": (6, 7)}.items():
             kt.setdefault(nm, []).append(hip.elapsed_ms(arr[a], arr[b]))
     # algorithmic flops (causal index dots + selected-key attention)
     T = w.T

@@ -6,83 +6,285 @@
 // t's document at or before t whose document-local 128-key block appears in
 // q2k row (h/16, t).
 //
-// Workgroup = (KV head g, 16 consecutive tokens of one document inside one
-// 128-token block, so all share the query block c); 8 waves, each owning
-// 2 tokens x 16 heads = 32 query columns.  The workgroup walks the UNION of
-// its tokens' selected blocks in ascending order.  Each block's K and V
-// (128 x 128 bf16 each, natural [key][d] layout, 16-byte chunks XOR-swizzled
-// per row) are copied HBM -> LDS by global_load_lds_dwordx4 into a 2-stage
-// ring: block u+1 streams in while block u is computed, with no register
-// staging.  A wave whose two tokens did not select the block skips it.
+// Two kernels:
+//   vt_transpose_kernel - V of every document re-laid per 32-key unit as
+//       V^T [unit][KV head][d][32 keys] (keys past the document end are 0),
+//       so that the PV operand is read from LDS with plain 16-byte reads.
+//   attend_prefill_kernel - workgroup = (KV head g, 16 consecutive tokens of
+//       one document inside one 128-token block, so all share the query
+//       block c); 8 waves, each owning 2 tokens x 16 heads.  The workgroup
+//       walks the UNION of its tokens' selected blocks in ascending order as
+//       32-key units (K rows 8 KiB + V^T rows 8 KiB), copied HBM -> LDS by
+//       global_load_lds_dwordx4 into a 9-slot ring; the waves meet at one
+//       barrier per union block, while the next five units stream in.  A
+//       wave computes a block only for those of its two tokens that selected
+//       it, as one chain over the block's 128 keys (one softmax step); the K
+//       and V^T fragments it reads from LDS serve both tokens.
 //
-// Per wave and block (key rows m, query columns n):
-//   S^T[128 x 32] = K . Q^T   4 M-tiles x 8 k-steps of MFMA 32x32x16; the K
-//                              operand is a 16-byte LDS read per lane.
-//   mask (selected by the column's token; key <= query in the own block),
-//   online softmax in the exp2 domain with lazy rescaling (the reference max
-//   only moves when it grows by more than 2^8), P^T packed to bf16 from the
-//   S^T accumulators,
-//   O^T[128 x 32] += V^T . P^T   4 d-tiles x 8 k-steps of MFMA 32x32x16; the
-//                              V^T operand comes from two ds_read_b64_tr_b16.
-// The S^T accumulator gives lane (n, hb) the keys 8*(r/4) + 4*hb + r%4 of
-// each 32-key tile, so PV step s consumes registers 8*(s%2)..8*(s%2)+7 of
-// tile s/2: keys 16s + 4hb + e and 16s + 8 + 4hb + e (e < 4), exactly the
-// two 4-row groups each transposing read returns for lane (d, hb).
+// Per wave, token and 32-key unit (MFMA 16x16x32 bf16, key rows m, head
+// columns n):
+//   S^T[32 x 16] = K . Q^T       2 M-tiles x 4 k-steps; M-tile mt row i is key
+//                                 8(i/4) + 4mt + i%4, so lane (n, grp) holds
+//                                 keys 8grp..8grp+7 of column n in order;
+//   causal mask in the query's own block, online softmax in the exp2 domain
+//   with lazy rescaling (the reference max only moves when it grows by more
+//   than 2^8), P^T packed to bf16 straight from the accumulators,
+//   O^T[128 x 16] += V^T . P^T   8 d-tiles x 1 k-step.
 #include "msa_internal.hpp"
 
 namespace msa {
 
 namespace {
-constexpr int kTok = kAttnTile;        // 16 tokens per workgroup
-constexpr int kWaves = kTok / 2;       // 8 waves
-constexpr int kThreads = 64 * kWaves;  // 512
-constexpr int kRowBytes = kDim * 2;    // 256
-constexpr int kTileBytes = kBlock * kRowBytes;  // 32 KiB (K or V block)
-constexpr int kStageBytes = 2 * kTileBytes;     // K + V
-constexpr int kStages = 2;
-constexpr int kLoadsPerWave = kStageBytes / 1024 / kWaves;  // 1 KiB per wave instruction
+constexpr int kTok = kAttnTile;                        // 16 tokens per workgroup
+constexpr int kWaves = kTok / 2;                       // 8 waves, 2 tokens each
+constexpr int kThreads = 64 * kWaves;                  // 512
+constexpr int kUnitsPerBlock = kBlock / kAttnUnit;     // 4
+constexpr int kKUnitBytes = kAttnUnit * kDim * 2;      // 8 KiB of K rows
+constexpr int kVUnitBytes = kDim * kAttnUnit * 2;      // 8 KiB of V^T rows
+constexpr int kUnitBytes = kKUnitBytes + kVUnitBytes;  // 16 KiB
+constexpr int kRing = 9;  // LDS ring slots of one unit each (144 KiB)
+constexpr int kLoadsPerWave = kUnitBytes / 1024 / kWaves;  // 2 one-KiB copies
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazyLog2 = 8.f;  // rescale only when the max grows by > 2^8
 
-// Chunk position of 16-byte chunk c in row r is c ^ swz(r): 16 consecutive
-// rows hit 16 distinct positions (K operand reads), and 8 consecutive rows x
-// 4 consecutive chunks hit every position exactly twice (V^T reads).
-__device__ __forceinline__ int swz(int r) {
-    return (((r >> 1) & 3) << 2) | ((r & 1) << 1) | ((r >> 3) & 1);
-}
+static_assert(kLoadsPerWave == 2, "unit copy split assumes 2 copies per wave");
+static_assert(kRing == 2 * kUnitsPerBlock + 1, "one unit of the block after next streams ahead");
+static_assert(kRing * kUnitBytes <= 144 * 1024, "ring must leave LDS for the union tables");
 
-__device__ __forceinline__ int tile_doc(const int32_t *off, int ndocs, int t) {
-    int lo = 0, hi = ndocs - 1;
-    while (lo < hi) {
-        int mid = (lo + hi + 1) >> 1;
-        if (off[mid] <= t) lo = mid; else hi = mid - 1;
-    }
-    return lo;
-}
-
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 // Workgroup barrier that drains this wave's LDS operations but leaves its
 // global->LDS prefetch in flight (a plain __syncthreads would also wait for
-// every outstanding vector-memory operation).  Callers wait for the block
+// every outstanding vector-memory operation).  Callers wait for the unit
 // they are about to read with an explicit vmcnt first.
 __device__ __forceinline__ void barrier_keep_prefetch() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-__device__ __forceinline__ i16x4 ds_read_tr16(const uint8_t *p) {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p));
+// Wait until at most n of this wave's copies are outstanding (copies
+// complete in issue order).  n > 16 falls back to a full wait.
+__device__ __forceinline__ void wait_copies(int n) {
+#define MSA_WAIT_CASE(i) \
+    case i: asm volatile("s_waitcnt vmcnt(" #i ")" ::: "memory"); break;
+    switch (n) {
+        MSA_WAIT_CASE(1) MSA_WAIT_CASE(2) MSA_WAIT_CASE(3) MSA_WAIT_CASE(4)
+        MSA_WAIT_CASE(5) MSA_WAIT_CASE(6) MSA_WAIT_CASE(7) MSA_WAIT_CASE(8)
+        MSA_WAIT_CASE(9) MSA_WAIT_CASE(10) MSA_WAIT_CASE(11) MSA_WAIT_CASE(12)
+        MSA_WAIT_CASE(13) MSA_WAIT_CASE(14) MSA_WAIT_CASE(15) MSA_WAIT_CASE(16)
+        default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    }
+#undef MSA_WAIT_CASE
+}
+
+// HBM -> LDS copy of 16 bytes per lane (lane l writes lds_dst + 16l).  It is
+// issued from asm so that the compiler does not hold later LDS reads of
+// other ring slots behind it (it cannot tell the slots apart and would wait
+// for every copy in flight); completion is awaited with explicit vmcnt.
+__device__ __forceinline__ void copy_to_lds(const void *src, uint8_t *lds_dst) {
+    const uint32_t m0 = (uint32_t)reinterpret_cast<uintptr_t>((lds_void *)lds_dst);
+    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0) : "memory");
+}
+
+// Max over the four 16-lane rows of a wave, for each lane position: each
+// swap of a register with itself returns, at every lane, the lane's own
+// value and that of its partner row (rows r, r^2 for the 32-lane swap;
+// r, r^1 for the 16-lane swap).
+__device__ __forceinline__ float row_max4(float x) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float row_sum4(float x) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// K unit in LDS: row r (key), 16-byte chunk c (d 8c..8c+7) at slot
+// 16r + (c ^ kswz(r)).  The 16 lanes of an operand read hold rows
+// 8a + 4mt + b (a, b < 4), whose kswz values are the 16 distinct 4a + b.
+__device__ __forceinline__ int kswz(int r) { return (((r >> 3) & 3) << 2) | (r & 3); }
+// V^T unit in LDS: row d, chunk c (keys 8c..8c+7) at slot 4d + (c ^ vswz(d));
+// 16 consecutive rows at one chunk cover all 16 chunk positions of 256 B.
+__device__ __forceinline__ int vswz(int d) { return (d >> 2) & 3; }
+
+// Per-wave state: query operands and running softmax of the wave's two
+// tokens (column n of each is head n of the KV group).
+struct WaveState {
+    bf16x8 qb[2][4];
+    f32x4 acc_o[2][8];
+    float m_ref[2];  // raw-score reference of the exponentials
+    float l_run[2];
+};
+
+// One union block for one wave.  kA0/kA1: which tokens compute (fixed at
+// compile time, so the whole chain is straight-line code the scheduler can
+// overlap: LDS reads of unit q+1 run under the MFMAs of unit q).  kDiag:
+// the query's own block, with nq <= 4 units, the causal mask, and the
+// active tokens taken from act_rt at run time.
+template <bool kA0, bool kA1, bool kDiag>
+__device__ __forceinline__ void attend_block(WaveState &st, const uint8_t *smem, int ustart, int nq,
+                                             const int (&k_row_off)[2], int v_off, int n, int grp,
+                                             int keyb, const bool (&act_rt)[2],
+                                             const int (&my_p)[2], float scale_log2) {
+    const bool act[2] = {kDiag ? act_rt[0] : kA0, kDiag ? act_rt[1] : kA1};
+    // S^T for the block: unit q, M-tile mt of token t
+    f32x4 sacc[2][kUnitsPerBlock][2];
+#pragma unroll
+    for (int q = 0; q < kUnitsPerBlock; ++q) {
+        if (kDiag && q >= nq) break;
+        const uint8_t *Ku = smem + ((ustart + q) % kRing) * kUnitBytes;
+        bf16x8 ka[4][2];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+                ka[ks][mt] = __builtin_bit_cast(
+                    bf16x8, *(const u32x4 *)(Ku + k_row_off[mt] + (((4 * ks + grp) ^ n) << 4)));
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            if (!act[t]) continue;
+            sacc[t][q][0] = f32x4{};
+            sacc[t][q][1] = f32x4{};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt)
+                    sacc[t][q][mt] = mfma_16x16x32(ka[ks][mt], st.qb[t][ks], sacc[t][q][mt]);
+        }
+    }
+
+    // online softmax over the block's keys; this lane holds keys
+    // keyb + 32q + e (e < 8) of head column n
+    bf16x8 pb[2][kUnitsPerBlock];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        if (!act[t]) continue;
+        float sv[kUnitsPerBlock][8];
+#pragma unroll
+        for (int q = 0; q < kUnitsPerBlock; ++q)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sv[q][e] = sacc[t][q][e >> 2][e & 3];
+        if (kDiag) {  // causal mask; also drops units q >= nq
+#pragma unroll
+            for (int q = 0; q < kUnitsPerBlock; ++q)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    sv[q][e] = keyb + kAttnUnit * q + e <= my_p[t] ? sv[q][e] : -INFINITY;
+        }
+        float mloc = sv[0][0];
+#pragma unroll
+        for (int q = 0; q < kUnitsPerBlock; ++q)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) mloc = fmaxf(mloc, sv[q][e]);
+        mloc = row_max4(mloc);
+        // lazy reference: move it (and rescale) only on a large increase
+        const bool grow = mloc > st.m_ref[t] &&
+                          (st.m_ref[t] == -INFINITY || (mloc - st.m_ref[t]) * scale_log2 > kLazyLog2);
+        if (__ballot(grow)) {
+            const float m_new = grow ? mloc : st.m_ref[t];
+            const float alpha = st.m_ref[t] == -INFINITY
+                                    ? 0.f
+                                    : __builtin_amdgcn_exp2f((st.m_ref[t] - m_new) * scale_log2);
+            st.l_run[t] *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) st.acc_o[t][dt] *= alpha;
+            st.m_ref[t] = m_new;
+        }
+        const float mb = st.m_ref[t] == -INFINITY ? 0.f : st.m_ref[t] * scale_log2;
+        float psum = 0.f;
+#pragma unroll
+        for (int q = 0; q < kUnitsPerBlock; ++q)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float pv = __builtin_amdgcn_exp2f(sv[q][e] * scale_log2 - mb);
+                psum += pv;
+                pb[t][q][e] = (__bf16)pv;
+            }
+        st.l_run[t] += psum;
+    }
+
+    // O^T += V^T . P^T, unit by unit
+#pragma unroll
+    for (int q = 0; q < kUnitsPerBlock; ++q) {
+        if (kDiag && q >= nq) break;
+        const uint8_t *Vu = smem + ((ustart + q) % kRing) * kUnitBytes + kKUnitBytes;
+        bf16x8 va[8];
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+            va[dt] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(Vu + 1024 * dt + v_off));
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            if (!act[t]) continue;
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt)
+                st.acc_o[t][dt] = mfma_16x16x32(va[dt], pb[t][q], st.acc_o[t][dt]);
+        }
+    }
+}
+
+// Index d with off[d] <= x < off[d+1] of a prefix-count array off[0..ndocs].
+__device__ __forceinline__ int prefix_doc(const int32_t *off, int ndocs, int x) {
+    int lo = 0, hi = ndocs - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (off[mid] <= x) lo = mid; else hi = mid - 1;
+    }
+    return lo;
 }
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// V -> per-unit V^T
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void vt_transpose_kernel(const uint16_t *__restrict__ v,
+                                                           const DocSpan *__restrict__ docs,
+                                                           const int32_t *__restrict__ unit_off,
+                                                           int ndocs, uint16_t *__restrict__ vt) {
+    __shared__ uint16_t tile[kAttnUnit][kDim + 2];
+    const int U = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
+    if (U >= unit_off[ndocs]) return;
+    const int d = prefix_doc(unit_off, ndocs, U);
+    const DocSpan doc = docs[d];
+    const int key0 = (U - unit_off[d]) * kAttnUnit;
+    // 32 rows x 16 chunks of 16 bytes, 2 per thread
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int id = tid + 256 * i, r = id >> 4, ch = id & 15;
+        u32x4 x = {0u, 0u, 0u, 0u};
+        if (key0 + r < doc.len)
+            x = *(const u32x4 *)(v + (size_t(doc.start + key0 + r) * kKvHeads + g) * kDim + 8 * ch);
+        uint32_t *dst = (uint32_t *)&tile[r][8 * ch];  // 4-byte aligned (row pitch 260 B)
+        dst[0] = x[0];
+        dst[1] = x[1];
+        dst[2] = x[2];
+        dst[3] = x[3];
+    }
+    __syncthreads();
+    // 128 rows (d) x 4 chunks (8 keys) of 16 bytes, 2 per thread; a wave
+    // writes 1 KiB contiguous
+    uint16_t *dst = vt + (size_t(U) * kKvHeads + g) * kDim * kAttnUnit;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int id = tid + 256 * i, dd = id >> 2, ch = id & 3;
+        u32x4 o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            o[j] = uint32_t(tile[8 * ch + 2 * j][dd]) | (uint32_t(tile[8 * ch + 2 * j + 1][dd]) << 16);
+        *(u32x4 *)(dst + dd * kAttnUnit + 8 * ch) = o;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// attention
+// ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void attend_prefill_kernel(
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ vt,
     const int32_t *__restrict__ q2k, int topk, const DocSpan *__restrict__ docs,
-    const int32_t *__restrict__ tile_off, int ndocs, int T, float scale_log2,
-    uint16_t *__restrict__ out) {
+    const int32_t *__restrict__ tile_off, const int32_t *__restrict__ unit_off, int ndocs, int T,
+    float scale_log2, uint16_t *__restrict__ out) {
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
     constexpr int kEntries = kTok * kMaxTopk;  // 256 (token, slot) pairs
     __shared__ int s_id[kEntries];
@@ -101,10 +303,11 @@ __global__ __launch_bounds__(kThreads) void attend_prefill_kernel(
     const int g = xcd >> 1;
     const int tile = 16 * (xslot >> 3) + 8 * (xcd & 1) + (xslot & 7);
     if (tile >= tile_off[ndocs]) return;
-    const int d = tile_doc(tile_off, ndocs, tile);
+    const int d = prefix_doc(tile_off, ndocs, tile);
     const int nt_doc = tile_off[d + 1] - tile_off[d];
     const int local_tile = nt_doc - 1 - (tile - tile_off[d]);
     const DocSpan doc = docs[d];
+    const int uoff = unit_off[d];
     const int p0 = local_tile * kTok;
     const int c = p0 / kBlock;
     const int ntok = min(kTok, doc.len - p0);
@@ -112,7 +315,27 @@ __global__ __launch_bounds__(kThreads) void attend_prefill_kernel(
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
-    const int n = lane & 31, hb = lane >> 5;
+    const int n = lane & 15, grp = lane >> 4;
+
+    // ---- this wave's tokens and their query operands (column n = head n)
+    const int head = g * kGroup + n;
+    int my_p[2];
+    bool tok_ok[2];
+    WaveState st;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        my_p[t] = p0 + 2 * wave + t;
+        tok_ok[t] = 2 * wave + t < ntok;
+        const uint16_t *src =
+            q + (size_t(doc.start + (tok_ok[t] ? my_p[t] : p0)) * kHeads + head) * kDim;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            st.qb[t][ks] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(src + 32 * ks + 8 * grp));
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) st.acc_o[t][dt] = f32x4{};
+        st.m_ref[t] = -INFINITY;
+        st.l_run[t] = 0.f;
+    }
 
     // ---- union of the tile's selected blocks (ascending, with token masks)
     if (tid == 0) s_nu = 0;
@@ -146,200 +369,126 @@ __global__ __launch_bounds__(kThreads) void attend_prefill_kernel(
     }
     __syncthreads();
     const int nu = s_nu;
+    // 32-key units: 4 per union block, except that the query's own block c
+    // (always last when present) stops at the unit holding p_last.
+    const int last_units =
+        (nu > 0 && s_ublk[nu - 1] == c) ? (p_last - c * kBlock) / kAttnUnit + 1 : kUnitsPerBlock;
+    const int nunits = nu > 0 ? kUnitsPerBlock * (nu - 1) + last_units : 0;
 
-    // ---- this wave's query operand: column n = (token 2*wave + n/16, head n%16)
-    const int my_tok = 2 * wave + (n >> 4);
-    const int my_p = p0 + my_tok;
-    const bool tok_ok = my_tok < ntok;
-    const int head = g * kGroup + (n & 15);
-    bf16x8 qb[8];
-    {
-        const uint16_t *src = q + (size_t(doc.start + (tok_ok ? my_p : p0)) * kHeads + head) * kDim;
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks)
-            qb[ks] = tok_ok ? __builtin_bit_cast(bf16x8, *(const u32x4 *)(src + 16 * ks + 8 * hb))
-                            : bf16x8{};
-    }
-
-    // ---- HBM -> LDS block copy: 64 one-KiB instructions per block (K then V),
-    // kLoadsPerWave per wave.  Instruction j' fills rows 4j'..4j'+3 of its tile;
-    // lane l writes position l%16 of row 4j' + l/16, i.e. chunk (l%16)^swz(row).
-    // Rows past the last query of the tile are never attended: they re-read
-    // row p_last so that no load leaves the document.
-    auto issue_block = [&](int b, int stage) {
-        uint8_t *base = smem + stage * kStageBytes;
-#pragma unroll
-        for (int j = 0; j < kLoadsPerWave; ++j) {
-            const int id = kLoadsPerWave * wave + j;  // 0..63
-            const int part = id >> 5, row4 = id & 31;
-            const int r = 4 * row4 + (lane >> 4);
-            const int chunk = (lane & 15) ^ swz(r);
-            const int kp = min(b * kBlock + r, p_last);
-            const uint16_t *src = (part ? v : k) +
-                                  (size_t(doc.start + kp) * kKvHeads + g) * kDim + 8 * chunk;
-            __builtin_amdgcn_global_load_lds((const void *)src,
-                                             (lds_void *)(base + part * kTileBytes + row4 * 1024),
-                                             16, 0, 0);
+    // ---- HBM -> LDS unit copies: 16 one-KiB copies per unit.  Copy i < 8
+    // fills K rows 4i..4i+3 (lane l: row 4i + l/16, slot position l%16, i.e.
+    // chunk (l%16) ^ kswz(row)); copy i >= 8 fills V^T rows 16(i-8)..+15
+    // (lane l: row 16(i-8) + l/4, chunk (l%4) ^ vswz(row)).  K rows past the
+    // last query of the tile are never attended: they re-read row p_last so
+    // that no load leaves the document.
+    auto issue_copy = [&](int vu, int ub, int i) {
+        const int qq = vu & 3;
+        uint8_t *slot = smem + (vu % kRing) * kUnitBytes;
+        if (i < 8) {
+            const int r = 4 * i + (lane >> 4);
+            const int ch = (lane & 15) ^ kswz(r);
+            const int kp = min(ub * kBlock + qq * kAttnUnit + r, p_last);
+            const uint16_t *src = k + (size_t(doc.start + kp) * kKvHeads + g) * kDim + 8 * ch;
+            copy_to_lds(src, slot + i * 1024);
+        } else {
+            const int jv = i - 8;
+            const int dd = 16 * jv + (lane >> 2);
+            const int ch = (lane & 3) ^ vswz(dd);
+            const size_t unit = size_t(uoff + ub * kUnitsPerBlock + qq);
+            const uint16_t *src = vt + ((unit * kKvHeads + g) * kDim + dd) * kAttnUnit + 8 * ch;
+            copy_to_lds(src, slot + kKUnitBytes + jv * 1024);
         }
     };
+    // Wave w issues copies 2w and 2w+1 of every unit.
+    auto issue_unit = [&](int vu) {
+        const int ub = __builtin_amdgcn_readfirstlane(s_ublk[vu >> 2]);
+        issue_copy(vu, ub, 2 * wave);
+        issue_copy(vu, ub, 2 * wave + 1);
+    };
 
-    f32x16 acc_o[4];
+    // Lane-constant LDS byte offsets of the operand reads.
+    // K: M-tile mt row n is key 8(n/4) + 4mt + n%4, whose kswz is n.
+    int k_row_off[2];
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) acc_o[dt] = f32x16{};
-    float m_ref = -INFINITY;  // raw-score reference of the exponentials
-    float l_run = 0.f;
+    for (int mt = 0; mt < 2; ++mt) k_row_off[mt] = (8 * (n >> 2) + 4 * mt + (n & 3)) * (kDim * 2);
+    // V^T: d-tile dt reads row 16dt + n, chunk grp.
+    const int v_off = 64 * n + 16 * (grp ^ vswz(n));
 
-    // Lane-constant LDS byte offsets; the row parts that vary with the
-    // unrolled loop indices (32mt, 64hf rows; 16s rows) are compile-time
-    // immediates because swz() only depends on a row's low 4 bits.
-    int k_off[8];                  // K operand: row n, chunk 2ks+hb
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) k_off[ks] = n * kRowBytes + (((2 * ks + hb) ^ swz(n)) << 4);
-    int v_off[4][2];               // V^T operand: row 4*(G/2) + gi/4 (+8 h2), column 32dt + ...
-    {
-        const int G = lane >> 4, gi = lane & 15;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-                const int row = 8 * h2 + 4 * (G >> 1) + (gi >> 2);
-                const int col = 32 * dt + 16 * (G & 1) + 4 * (gi & 3);
-                v_off[dt][h2] = row * kRowBytes + ((((col >> 3) ^ swz(row))) << 4) + ((col & 7) << 1);
-            }
-    }
-
-    if (nu > 0) issue_block(s_ublk[0], 0);
+    // Block loop: union block u occupies units 4u..4u+nq-1 (nq < 4 only for
+    // the query's own block).  At the barrier of block u its units have
+    // landed (each wave waited for its own copies of them) and every wave is
+    // done with block u-1; the ring then takes every unit up to 4u + 8, so
+    // five units stream in during the compute.
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): query operands are in (no copy issued yet)
+    int issued = min(nunits, kRing);
+    for (int vu = 0; vu < issued; ++vu) issue_unit(vu);
     for (int u = 0; u < nu; ++u) {
-        if (u + 1 < nu) {
-            issue_block(s_ublk[u + 1], (u + 1) & 1);
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoadsPerWave) : "memory");
-        } else {
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        }
-        barrier_keep_prefetch();  // block u is in LDS for every wave
+        const int ustart = kUnitsPerBlock * u;
+        const int nq = u == nu - 1 ? nunits - ustart : kUnitsPerBlock;
+        wait_copies(2 * (issued - (ustart + nq)));  // copies complete in issue order
+        barrier_keep_prefetch();
 
-        const int b = s_ublk[u];
-        const int umask = s_umask[u];
-        const uint8_t *Kt = smem + (u & 1) * kStageBytes;
-        const uint8_t *Vt = Kt + kTileBytes;
-        if ((umask >> (2 * wave)) & 3) {
-            const bool sel = tok_ok && ((umask >> my_tok) & 1);
-            // two 64-key halves, each a full S / softmax / PV round
-#pragma unroll 1
-            for (int hf = 0; hf < 2; ++hf) {
-                const uint8_t *Kh = Kt + 64 * hf * kRowBytes;
-                const uint8_t *Vh = Vt + 64 * hf * kRowBytes;
-                f32x16 acc_s[2];
-#pragma unroll
-                for (int mt = 0; mt < 2; ++mt) acc_s[mt] = f32x16{};
-#pragma unroll
-                for (int ks = 0; ks < 8; ++ks) {
-                    bf16x8 a[2];
-#pragma unroll
-                    for (int mt = 0; mt < 2; ++mt)
-                        a[mt] = __builtin_bit_cast(
-                            bf16x8, *(const u32x4 *)(Kh + 32 * mt * kRowBytes + k_off[ks]));
-#pragma unroll
-                    for (int mt = 0; mt < 2; ++mt) acc_s[mt] = mfma_32x32x16(a[mt], qb[ks], acc_s[mt]);
-                }
-
-                // Column mask (token did not select b) goes into the exp2
-                // offset; the per-key causal mask is only needed in the
-                // query's own block.
-                float mloc = -INFINITY;
-                if (b == c) {
-#pragma unroll
-                    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int kp = b * kBlock + 64 * hf + 32 * mt + 8 * (r >> 2) + 4 * hb + (r & 3);
-                            const float sv = kp <= my_p ? acc_s[mt][r] : -INFINITY;
-                            acc_s[mt][r] = sv;
-                            mloc = fmaxf(mloc, sv);
-                        }
-                } else {
-#pragma unroll
-                    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, acc_s[mt][r]);
-                }
-                mloc = sel ? mloc : -INFINITY;
-                mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-                // lazy reference: move it (and rescale) only on a large increase
-                const bool grow = mloc > m_ref &&
-                                  (m_ref == -INFINITY || (mloc - m_ref) * scale_log2 > kLazyLog2);
-                if (__ballot(grow)) {
-                    const float m_new = grow ? mloc : m_ref;
-                    const float alpha = m_ref == -INFINITY
-                                            ? 0.f
-                                            : __builtin_amdgcn_exp2f((m_ref - m_new) * scale_log2);
-                    l_run *= alpha;
-#pragma unroll
-                    for (int dt = 0; dt < 4; ++dt) acc_o[dt] *= alpha;
-                    m_ref = m_new;
-                }
-                // unselected columns: offset +inf makes every exponential 0
-                const float mb = !sel ? INFINITY : (m_ref == -INFINITY ? 0.f : m_ref * scale_log2);
-                float psum = 0.f;
-#pragma unroll
-                for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const float pv = __builtin_amdgcn_exp2f(acc_s[mt][r] * scale_log2 - mb);
-                        acc_s[mt][r] = pv;
-                        psum += pv;
-                    }
-                l_run += psum;
-
-#pragma unroll
-                for (int s4 = 0; s4 < 4; ++s4) {  // 16-key PV steps of this half
-                    bf16x8 pb;
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) pb[i] = (__bf16)acc_s[s4 >> 1][8 * (s4 & 1) + i];
-#pragma unroll
-                    for (int dt = 0; dt < 4; ++dt) {
-                        i16x4 t[2];
-#pragma unroll
-                        for (int h2 = 0; h2 < 2; ++h2)
-                            t[h2] = ds_read_tr16(Vh + 16 * s4 * kRowBytes + v_off[dt][h2]);
-                        const i16x8 ab = {t[0][0], t[0][1], t[0][2], t[0][3],
-                                          t[1][0], t[1][1], t[1][2], t[1][3]};
-                        acc_o[dt] = mfma_32x32x16(__builtin_bit_cast(bf16x8, ab), pb, acc_o[dt]);
-                    }
-                }
-            }
-        }
-        barrier_keep_prefetch();  // stage u&1 is refilled by the next iteration's prefetch
+        const int b = __builtin_amdgcn_readfirstlane(s_ublk[u]);
+        const int umask = __builtin_amdgcn_readfirstlane(s_umask[u]);
+        const bool act[2] = {tok_ok[0] && ((umask >> (2 * wave)) & 1),
+                             tok_ok[1] && ((umask >> (2 * wave + 1)) & 1)};
+        // refill the slots of block u-1 (every wave is past it)
+        for (const int ifront = min(nunits, ustart + kRing); issued < ifront; ++issued)
+            issue_unit(issued);
+        const int keyb = b * kBlock + 8 * grp;
+        if (b == c)
+            attend_block<true, true, true>(st, smem, ustart, nq, k_row_off, v_off, n, grp, keyb, act, my_p,
+                                           scale_log2);
+        else if (act[0] && act[1])
+            attend_block<true, true, false>(st, smem, ustart, kUnitsPerBlock, k_row_off, v_off, n, grp, keyb,
+                                            act, my_p, scale_log2);
+        else if (act[0])
+            attend_block<true, false, false>(st, smem, ustart, kUnitsPerBlock, k_row_off, v_off, n, grp,
+                                             keyb, act, my_p, scale_log2);
+        else if (act[1])
+            attend_block<false, true, false>(st, smem, ustart, kUnitsPerBlock, k_row_off, v_off, n, grp,
+                                             keyb, act, my_p, scale_log2);
     }
 
-    // ---- epilogue: normalise and store bf16
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    if (tok_ok) {
-        uint16_t *dst = out + (size_t(doc.start + my_p) * kHeads + head) * kDim;
+    // ---- epilogue: normalise and store bf16 (lane holds d = 16dt + 4grp + i)
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
+    for (int t = 0; t < 2; ++t) {
+        const float l_tot = row_sum4(st.l_run[t]);
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        if (tok_ok[t]) {
+            uint16_t *dst = out + (size_t(doc.start + my_p[t]) * kHeads + head) * kDim;
 #pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const int d0 = 32 * dt + 8 * r4 + 4 * hb;
+            for (int dt = 0; dt < 8; ++dt) {
                 bf16x4 o;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) o[i] = (__bf16)(acc_o[dt][4 * r4 + i] * inv);
-                *(bf16x4 *)(dst + d0) = o;
+                for (int i = 0; i < 4; ++i) o[i] = (__bf16)(st.acc_o[t][dt][i] * inv);
+                *(bf16x4 *)(dst + 16 * dt + 4 * grp) = o;
             }
+        }
     }
 }
 
-hipError_t launch_attend_prefill(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+size_t prefill_vt_bytes(int T, int ndocs) {
+    return (size_t(ceil_div(T, kAttnUnit)) + size_t(ndocs)) * kKvHeads * kDim * kAttnUnit * 2;
+}
+
+hipError_t launch_vt_transpose(const uint16_t *v, const DocSpan *docs, const int32_t *unit_off,
+                               int ndocs, int T, uint16_t *vt, hipStream_t stream) {
+    const int max_units = ceil_div(T, kAttnUnit) + ndocs;  // document-aligned units (upper bound)
+    hipLaunchKernelGGL(vt_transpose_kernel, dim3(max_units, kKvHeads), dim3(256), 0, stream, v, docs,
+                       unit_off, ndocs, vt);
+    return hipGetLastError();
+}
+
+hipError_t launch_attend_prefill(const uint16_t *q, const uint16_t *k, const uint16_t *vt,
                                  const int32_t *q2k, int topk, const DocSpan *docs,
-                                 const int32_t *tile_off, int ndocs, int T, int max_seqlen,
+                                 const int32_t *tile_off, const int32_t *unit_off, int ndocs, int T,
                                  float scale, uint16_t *out, hipStream_t stream) {
-    (void)max_seqlen;
     const int max_tiles = ceil_div(T, kTok) + ndocs;  // document-aligned tiles (upper bound)
     const int grid = 8 * 8 * ceil_div(max_tiles, 16);  // 8 XCDs x slots
-    const size_t lds = size_t(kStages) * kStageBytes;
-    hipLaunchKernelGGL(attend_prefill_kernel, dim3(grid), dim3(kThreads), lds, stream, q, k, v, q2k,
-                       topk, docs, tile_off, ndocs, T, scale * kLog2e, out);
+    const size_t lds = size_t(kRing) * kUnitBytes;
+    hipLaunchKernelGGL(attend_prefill_kernel, dim3(grid), dim3(kThreads), lds, stream, q, k, vt, q2k,
+                       topk, docs, tile_off, unit_off, ndocs, T, scale * kLog2e, out);
     return hipGetLastError();
 }
 

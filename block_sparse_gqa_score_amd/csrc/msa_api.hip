@@ -75,14 +75,16 @@ SelectWs select_layout(int T, int ndocs, int max_seqlen) {
 }
 
 struct PrefillWs {
-    size_t docs, off, total;
+    size_t docs, off, uoff, vt, total;
 };
 
-PrefillWs prefill_layout(int ndocs) {
+PrefillWs prefill_layout(int T, int ndocs) {
     PrefillWs w;
     w.docs = 0;
     w.off = align256(sizeof(DocSpan) * size_t(ndocs));
-    w.total = align256(w.off + sizeof(int32_t) * (size_t(ndocs) + 1));
+    w.uoff = align256(w.off + sizeof(int32_t) * (size_t(ndocs) + 1));
+    w.vt = align256(w.uoff + sizeof(int32_t) * (size_t(ndocs) + 1));
+    w.total = align256(w.vt + prefill_vt_bytes(T, ndocs));
     return w;
 }
 
@@ -165,7 +167,7 @@ size_t msa_prefill_workspace_bytes(int total_tokens, int num_docs, int max_seqle
     if (total_tokens < 1 || num_docs < 1 || num_docs > total_tokens || max_seqlen < 1 ||
         max_seqlen > total_tokens)
         return 0;
-    return prefill_layout(num_docs).total;
+    return prefill_layout(total_tokens, num_docs).total;
 }
 
 size_t msa_decode_workspace_bytes(int batch, int max_context_len, int topk) {
@@ -225,7 +227,7 @@ msa_status msa_sparse_attend_prefill(const uint16_t *q, const uint16_t *k, const
     if (st != MSA_OK) return st;
     if (!(softmax_scale > 0.f) || softmax_scale > 1e30f)
         return fail(MSA_ERR_INVALID_ARG, "softmax_scale must be a positive finite number");
-    const PrefillWs ws = prefill_layout(num_docs);
+    const PrefillWs ws = prefill_layout(total_tokens, num_docs);
     if (!workspace || workspace_bytes < ws.total)
         return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", ws.total,
                     workspace ? workspace_bytes : size_t(0));
@@ -233,13 +235,18 @@ msa_status msa_sparse_attend_prefill(const uint16_t *q, const uint16_t *k, const
     uint8_t *base = (uint8_t *)workspace;
     DocSpan *docs = (DocSpan *)(base + ws.docs);
     int32_t *off = (int32_t *)(base + ws.off);
+    int32_t *uoff = (int32_t *)(base + ws.uoff);
+    uint16_t *vt = (uint16_t *)(base + ws.vt);
     TimingScope tm;
     tm.mark(s, "doc_setup");
-    hipError_t e = launch_doc_setup(cu_seqlens, num_docs, total_tokens, max_seqlen, kAttnTile, 0,
-                                    docs, off, nullptr, s);
+    hipError_t e = launch_doc_setup(cu_seqlens, num_docs, total_tokens, max_seqlen, kAttnTile,
+                                    kAttnUnit, docs, off, uoff, s);
     if (e != hipSuccess) return hip_fail(e, "doc_setup");
+    tm.mark(s, "vt_transpose");
+    e = launch_vt_transpose(v, docs, uoff, num_docs, total_tokens, vt, s);
+    if (e != hipSuccess) return hip_fail(e, "vt_transpose");
     tm.mark(s, "attend_prefill");
-    e = launch_attend_prefill(q, k, v, q2k, topk, docs, off, num_docs, total_tokens, max_seqlen,
+    e = launch_attend_prefill(q, k, vt, q2k, topk, docs, off, uoff, num_docs, total_tokens,
                               softmax_scale, out, s);
     if (e != hipSuccess) return hip_fail(e, "attend_prefill");
     tm.mark(s, nullptr);

@@ -11,6 +11,7 @@ namespace msa {
 
 constexpr int kScoreTile = 64;   // query tokens per block-scorer workgroup
 constexpr int kAttnTile = 16;    // query tokens per prefill-attention workgroup
+constexpr int kAttnUnit = 32;    // keys per prefill-attention pipeline unit
 
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -30,10 +31,15 @@ hipError_t launch_block_scores(const void *iq, const void *ik, bool fp8, const D
 hipError_t launch_topk_prefill(const float *S, const DocSpan *docs, int ndocs, int T, int nb_max,
                                int topk, int init, int local, int32_t *q2k, hipStream_t stream);
 
-// Sparse GQA prefill attention.
-hipError_t launch_attend_prefill(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+// Sparse GQA prefill attention: V re-laid as per-unit V^T (unit_off = prefix
+// count of kAttnUnit-key units per document; vt holds prefill_vt_bytes),
+// then the attention kernel over K and V^T.
+size_t prefill_vt_bytes(int T, int ndocs);
+hipError_t launch_vt_transpose(const uint16_t *v, const DocSpan *docs, const int32_t *unit_off,
+                               int ndocs, int T, uint16_t *vt, hipStream_t stream);
+hipError_t launch_attend_prefill(const uint16_t *q, const uint16_t *k, const uint16_t *vt,
                                  const int32_t *q2k, int topk, const DocSpan *docs,
-                                 const int32_t *tile_off, int ndocs, int T, int max_seqlen,
+                                 const int32_t *tile_off, const int32_t *unit_off, int ndocs, int T,
                                  float scale, uint16_t *out, hipStream_t stream);
 
 // Paged decode.
