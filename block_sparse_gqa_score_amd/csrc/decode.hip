@@ -38,11 +38,15 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(
     const int r = blockIdx.y;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int pi = blockIdx.x * kDecPagesPerWg + wave;
+    // the page-table entry is fetched together with the context length (an
+    // entry past the context is in bounds and simply unused)
+    const int page = pt[size_t(r) * max_pages + min(pi, max_pages - 1)];
     const int L = min(max(ctx[r], 1), max_ctx);
+    asm volatile("" ::"v"(page), "v"(L));  // keep the two loads ahead of the branch
     const int nb = (L + kBlock - 1) / kBlock;
     if (pi >= nb) return;
     const int n = lane & 15, qd = lane >> 4;
-    const size_t slot0 = size_t(pt[size_t(r) * max_pages + pi]) * kBlock;
+    const size_t slot0 = size_t(page) * kBlock;
     constexpr int kRowBytes = kFp8 ? 128 : 256;
     const uint8_t *kbase = ikc + slot0 * kRowBytes;
     const uint8_t *qrow = iq + (size_t(r) * kIdxHeads + (n & 3)) * kRowBytes;
@@ -123,20 +127,14 @@ hipError_t launch_decode_scores(const void *iq, const void *ikc, bool fp8, const
 // Number of lanes whose predicate holds, summed over the wave (scalar).
 __device__ __forceinline__ int wave_count(bool pred) { return __popcll(__ballot(pred)); }
 
+// Selection for one (request, index head) row by one wave: forced blocks
+// plus the R = topk - forced highest-scoring candidates (ties to the lower
+// block id), ascending, then -1.  The R-th largest order value is found by
+// bisection on its bits with wave-wide counts; out may be global or LDS.
 template <int kCpl>  // candidates per lane: blocks lane + 64*i
-__global__ __launch_bounds__(256) void decode_topk_kernel(const float *__restrict__ S,
-                                                          const int32_t *__restrict__ ctx, int B,
-                                                          int max_ctx, int nb_max, int topk, int init, int local,
-                                                          int32_t *__restrict__ q2k) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int row = blockIdx.x * 4 + wave;  // (r, h) with h fastest
-    if (row >= B * kIdxHeads) return;
-    const int r = row / kIdxHeads, h = row % kIdxHeads;
-    const int c = (min(max(ctx[r], 1), max_ctx) - 1) / kBlock;
+__device__ __forceinline__ void select_row(const float *__restrict__ srow, int c, int topk, int init,
+                                           int local, int lane, int32_t *out) {
     const int R = topk - forced_count(c, init, local);
-    const float *srow = S + (size_t(r) * kIdxHeads + h) * nb_max;
-    int32_t *out = q2k + (size_t(h) * B + r) * topk;
-
     // order bits of each non-forced candidate; 0 marks "not a candidate"
     uint32_t u[kCpl];
 #pragma unroll
@@ -178,6 +176,20 @@ __global__ __launch_bounds__(256) void decode_topk_kernel(const float *__restric
         emitted += __popcll(take_mask);
     }
     for (int i = emitted + lane; i < topk; i += 64) out[i] = -1;
+}
+
+template <int kCpl>
+__global__ __launch_bounds__(256) void decode_topk_kernel(const float *__restrict__ S,
+                                                          const int32_t *__restrict__ ctx, int B,
+                                                          int max_ctx, int nb_max, int topk, int init, int local,
+                                                          int32_t *__restrict__ q2k) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + wave;  // (r, h) with h fastest
+    if (row >= B * kIdxHeads) return;
+    const int r = row / kIdxHeads, h = row % kIdxHeads;
+    const int c = (min(max(ctx[r], 1), max_ctx) - 1) / kBlock;
+    select_row<kCpl>(S + (size_t(r) * kIdxHeads + h) * nb_max, c, topk, init, local, lane,
+                     q2k + (size_t(h) * B + r) * topk);
 }
 
 hipError_t launch_decode_topk(const float *S, const int32_t *ctx, int B, int max_ctx, int nb_max, int topk,

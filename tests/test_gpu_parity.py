@@ -115,6 +115,11 @@ DECODE_CASES = [
     ("local2_topk3_bf16", [700, 4097], 3, 0, 2, "bf16"),
     ("mixed_lengths_fp8", [1, 129, 3000, 20000], 16, 0, 1, "fp8"),
     ("topk6_init2_fp8", [5000, 777], 6, 2, 1, "fp8"),
+    # larger batches: many requests per launch, mixed and short contexts
+    ("batch16_mixed_bf16", [1, 2, 127, 128, 129, 255, 256, 257, 1000, 3000, 5000, 8191, 8192, 8193,
+                            12000, 20000], 16, 0, 1, "bf16"),
+    ("batch20_topk5_init1_fp8", [64 + 997 * i for i in range(20)], 5, 1, 1, "fp8"),
+    ("batch24_short_local2_topk3_bf16", [1 + 37 * i for i in range(24)], 3, 0, 2, "bf16"),
 ]
 
 
