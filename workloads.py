@@ -329,6 +329,37 @@ def make_decode(context_lens, seed: int, *, topk=16, init_blocks=0, local_blocks
 # --------------------------------------------------------------------------
 # the five named workloads
 # --------------------------------------------------------------------------
+def mx_matrix(seed: int, rows: int, cols: int) -> np.ndarray:
+    """bf16 bit patterns [rows, cols] (cols % 32 == 0) for the MXFP8 quantiser
+    tests, built at the bit level in blocks of 32 of mixed kinds: random
+    values over a wide exponent range; all zeros (either sign); values with at
+    most 3 mantissa bits (on the E4M3 grid after a power-of-two scale); values
+    with mantissa pattern 1xxx1000 (half-way points of that grid); a block whose
+    largest value has a mantissa of 1.75 or more (the saturation range); bf16
+    subnormals; and blocks spanning ~40 binades."""
+    if cols % 32:
+        raise ValueError("cols must be a multiple of 32")
+    g = np.random.default_rng(np.random.SeedSequence(seed).spawn(9)[8])
+    nb = cols // 32
+    kind = g.integers(0, 7, size=(rows, nb, 1))
+    sign = g.integers(0, 2, size=(rows, nb, 32)).astype(np.uint32) << 15
+    base = g.integers(20, 240, size=(rows, nb, 1))  # block's top biased exponent
+    span = np.where(kind == 6, 40, 12)
+    expo = np.clip(base - g.integers(0, 41, size=(rows, nb, 32)) % (span + 1), 1, 254)
+    man = g.integers(0, 128, size=(rows, nb, 32))
+    man = np.where(kind == 2, man & 0x70, man)
+    man = np.where(kind == 3, (man & 0x70) | 0x08, man)
+    # saturation kind: element 0 carries the block's top exponent and a mantissa >= 0x60
+    first = np.zeros((1, 1, 32), dtype=bool)
+    first[..., 0] = True
+    expo = np.where((kind == 4) & first, base, expo)
+    man = np.where((kind == 4) & first, 0x60 | (man & 0x1F), man)
+    bits = sign | (expo.astype(np.uint32) << 7) | man.astype(np.uint32)
+    bits = np.where(kind == 1, sign, bits)
+    bits = np.where(kind == 5, sign | man.astype(np.uint32), bits)  # exponent field 0
+    return bits.reshape(rows, cols).astype(np.uint16)
+
+
 CONFIG_NAMES = (
     "prefill_2k_topk4",              # one causal document of 2048 tokens, topk=4
     "decode_b32_ctx8k-32k",          # paged decode, batch 32, L ~ U[8192, 32768]
