@@ -173,7 +173,7 @@ def bench_decode(args, hip, flush):
 
     step_ms, evs, names = timed_steps(run, args.steps, args.warmup, hip, stream, flush, 5)
     kt = kernel_times(evs, [names], hip)
-    graph_ms = None
+    graph_ms = mx_graph_ms = None
     if not args.no_graph:
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
@@ -196,6 +196,26 @@ def bench_decode(args, hip, flush):
             hip.record(gb[i], stream)
         torch.cuda.synchronize()
         graph_ms = stats([hip.elapsed_ms(ga[i], gb[i]) for i in range(args.steps)])
+        # the same step with the output emitted as MXFP8 (E4M3 + E8M0 per 32)
+        oq = torch.empty((d.B, 64 * 128), dtype=torch.uint8, device="cuda")
+        osc = torch.empty((d.B, 64 * 128 // 32), dtype=torch.uint8, device="cuda")
+        g2 = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g2, stream=s):
+                st = L.msa_sparse_attend_decode_paged_mxfp8(
+                    P(dq), P(diq), P(dk), P(dv), P(dik), 0, P(dpt), d.max_pages, P(dctx), d.B,
+                    d.max_context_len, d.topk, d.init_blocks, d.local_blocks, d.scale, P(oq), P(osc),
+                    None, P(ws), ws.numel(), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+                assert st == 0
+        torch.cuda.current_stream().wait_stream(s)
+        for i in range(args.steps):
+            if flush is not None:
+                flush.sum()
+            hip.record(ga[i], stream)
+            g2.replay()
+            hip.record(gb[i], stream)
+        torch.cuda.synchronize()
+        mx_graph_ms = stats([hip.elapsed_ms(ga[i], gb[i]) for i in range(args.steps)])
 
     # algorithmic bytes (per request: index-K rows, selected K/V rows, q/iq/out, page table)
     lens = d.context_lens.astype(np.int64)
@@ -208,7 +228,7 @@ def bench_decode(args, hip, flush):
     alg = {"decode_scores": idx_bytes, "decode_attend": kv_bytes + d.B * 64 * 128 * 2}
     dom = max(alg, key=lambda k: per_kernel.get(k, 0.0))
     return dict(d=d, gen_s=gen_s, step=stats(step_ms), per_kernel_ms=per_kernel, alg_bytes=alg,
-                dominant=dom, total_bytes=total_bytes, out=out, graph=graph_ms)
+                dominant=dom, total_bytes=total_bytes, out=out, graph=graph_ms, mx_graph=mx_graph_ms)
 
 
 def bench_prefill(args, hip, flush):
@@ -381,6 +401,8 @@ def main():
         "launch": "hip_graph_replay" if dres["graph"] is not None else "direct",
         "step_stats_ms": {k: round(v, 6) for k, v in (dres["graph"] or dres["step"]).items()},
         "direct_launch_step_ms": {k: round(v, 6) for k, v in dres["step"].items()},
+        "mxfp8_output_step_us": (round(dres["mx_graph"]["median"] * 1e3, 3)
+                                 if dres["mx_graph"] is not None else None),
         "per_kernel_us": {k: round(v * 1e3, 3) for k, v in dres["per_kernel_ms"].items()},
         "path_bytes_per_step": dres["total_bytes"],
         "path_hbm_frac": round(dres["total_bytes"] / (step_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),

@@ -15,6 +15,9 @@ Entry points (names follow the C ABI):
                 page_table, context_lens, max_context_len, topk=16,
                 init_blocks=0, local_blocks=1, softmax_scale=None,
                 return_q2k=False) -> out [B,64,128] (, q2k [4,B,topk])
+  sparse_attend_decode_paged_mxfp8(same arguments)
+                -> (out_q uint8 [B,8192] E4M3, out_scale uint8 [B,256] E8M0)
+  mxfp8_quantize(x bf16 [rows, cols]) -> (q uint8 [rows, cols], scale uint8 [rows, cols/32])
 """
 from __future__ import annotations
 
@@ -26,6 +29,7 @@ import torch
 
 __all__ = [
     "select_blocks", "sparse_attend_prefill", "sparse_attend_decode_paged",
+    "sparse_attend_decode_paged_mxfp8", "mxfp8_quantize",
     "unsupported_reason", "library_path", "MsaError",
     "select_blocks_workspace_bytes", "prefill_workspace_bytes", "decode_workspace_bytes",
 ]
@@ -81,6 +85,11 @@ def lib():
         L.msa_sparse_attend_decode_paged.restype = i
         L.msa_sparse_attend_decode_paged.argtypes = [P, P, P, P, P, i, P, i, P, i, i, i, i, i, f,
                                                      P, P, P, sz, P]
+        L.msa_sparse_attend_decode_paged_mxfp8.restype = i
+        L.msa_sparse_attend_decode_paged_mxfp8.argtypes = [P, P, P, P, P, i, P, i, P, i, i, i, i, i, f,
+                                                           P, P, P, P, sz, P]
+        L.msa_mxfp8_quantize.restype = i
+        L.msa_mxfp8_quantize.argtypes = [P, i, i, P, P, P]
         _lib = L
     return _lib
 
@@ -204,6 +213,39 @@ def sparse_attend_decode_paged(q, index_q, k_cache, v_cache, index_k_cache, page
                                local_blocks=1, softmax_scale=None, return_q2k=False,
                                workspace=None):
     """One decode step over the paged caches -> bf16 out [B,64,128] (, q2k [4,B,topk])."""
+    return _decode(q, index_q, k_cache, v_cache, index_k_cache, page_table, context_lens,
+                   max_context_len, topk, init_blocks, local_blocks, softmax_scale, return_q2k,
+                   workspace, mxfp8=False)
+
+
+def sparse_attend_decode_paged_mxfp8(q, index_q, k_cache, v_cache, index_k_cache, page_table,
+                                     context_lens, max_context_len, topk=16, init_blocks=0,
+                                     local_blocks=1, softmax_scale=None, return_q2k=False,
+                                     workspace=None):
+    """One decode step with the output as MXFP8 -> (out_q uint8 [B, 8192] E4M3,
+    out_scale uint8 [B, 256] E8M0) (, q2k [4,B,topk])."""
+    return _decode(q, index_q, k_cache, v_cache, index_k_cache, page_table, context_lens,
+                   max_context_len, topk, init_blocks, local_blocks, softmax_scale, return_q2k,
+                   workspace, mxfp8=True)
+
+
+def mxfp8_quantize(x):
+    """MXFP8 of a bf16 matrix [rows, cols] (cols % 32 == 0) -> (q uint8 [rows, cols] E4M3,
+    scale uint8 [rows, cols/32] E8M0)."""
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [rows, cols]")
+    rows, cols = int(x.shape[0]), int(x.shape[1])
+    _dev_tensor("x", x, (rows, cols), (torch.bfloat16,))
+    if cols % 32 or cols == 0:
+        raise ValueError(f"cols must be a positive multiple of 32 (got {cols})")
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    scale = torch.empty((rows, cols // 32), dtype=torch.uint8, device=x.device)
+    _check(lib().msa_mxfp8_quantize(_ptr(x), rows, cols, _ptr(q), _ptr(scale), _stream(x.device)))
+    return q, scale
+
+
+def _decode(q, index_q, k_cache, v_cache, index_k_cache, page_table, context_lens, max_context_len,
+            topk, init_blocks, local_blocks, softmax_scale, return_q2k, workspace, mxfp8):
     device = q.device
     B = int(q.shape[0])
     _dev_tensor("q", q, (B, 64, 128), (torch.bfloat16,))
@@ -218,15 +260,21 @@ def sparse_attend_decode_paged(q, index_q, k_cache, v_cache, index_k_cache, page
     _dev_tensor("context_lens", context_lens, (B,), (torch.int32,), device)
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(128.0)
-    out = torch.empty((B, 64, 128), dtype=torch.bfloat16, device=device)
     q2k = torch.empty((4, B, topk), dtype=torch.int32, device=device) if return_q2k else None
     need = decode_workspace_bytes(B, int(max_context_len), int(topk))
     if workspace is None:
         workspace = _workspace(need, device)
-    _check(lib().msa_sparse_attend_decode_paged(
-        _ptr(q), _ptr(index_q), _ptr(k_cache), _ptr(v_cache), _ptr(index_k_cache),
-        _index_code(index_q), _ptr(page_table), int(page_table.shape[1]), _ptr(context_lens), B,
-        int(max_context_len), int(topk), int(init_blocks), int(local_blocks),
-        float(softmax_scale), _ptr(out), _ptr(q2k), _ptr(workspace), workspace.numel(),
-        _stream(device)))
+    head = (_ptr(q), _ptr(index_q), _ptr(k_cache), _ptr(v_cache), _ptr(index_k_cache),
+            _index_code(index_q), _ptr(page_table), int(page_table.shape[1]), _ptr(context_lens), B,
+            int(max_context_len), int(topk), int(init_blocks), int(local_blocks),
+            float(softmax_scale))
+    tail = (_ptr(q2k), _ptr(workspace), workspace.numel(), _stream(device))
+    if mxfp8:
+        out_q = torch.empty((B, 64 * 128), dtype=torch.uint8, device=device)
+        out_scale = torch.empty((B, 64 * 128 // 32), dtype=torch.uint8, device=device)
+        _check(lib().msa_sparse_attend_decode_paged_mxfp8(*head, _ptr(out_q), _ptr(out_scale), *tail))
+        out = (out_q, out_scale)
+    else:
+        out = torch.empty((B, 64, 128), dtype=torch.bfloat16, device=device)
+        _check(lib().msa_sparse_attend_decode_paged(*head, _ptr(out), *tail))
     return (out, q2k) if return_q2k else out

@@ -18,8 +18,10 @@
 //       16x16x32 (16 query heads = N), partial softmax merged across waves in
 //       LDS, one (O, m, l) partial per selected block written to workspace.
 //   decode_combine_kernel - per (request, KV head): log-sum-exp merge of the
-//       topk partials in fixed block order, bf16 output.
+//       topk partials in fixed block order, bf16 output (or, for the MXFP8
+//       variant, that bf16 output encoded as E4M3 + E8M0 per 32 values).
 #include "msa_internal.hpp"
+#include "mxfp8.hpp"
 
 namespace msa {
 
@@ -398,9 +400,15 @@ __global__ __launch_bounds__(256) void decode_attend_kernel(
 // ---------------------------------------------------------------------------
 // One 64-thread workgroup per (d quarter, KV head, request): thread ->
 // (head tid/4, 8 of the quarter's 32 d).
+// The thread's 8 d of one head, with the 3 neighbouring lanes (tid/4 equal),
+// are exactly one 32-value MXFP8 block of the output row [64 * 128]: block
+// (head, d quarter).
+template <bool kMx>
 __global__ __launch_bounds__(64) void decode_combine_kernel(const float *__restrict__ part_o,
                                                             const float *__restrict__ part_ml,
-                                                            int topk, uint16_t *__restrict__ out) {
+                                                            int topk, uint16_t *__restrict__ out,
+                                                            uint8_t *__restrict__ out_q,
+                                                            uint8_t *__restrict__ out_scale) {
     const int dq = blockIdx.x, g = blockIdx.y, r = blockIdx.z, tid = threadIdx.x;
     const size_t base = (size_t(r) * kKvHeads + g) * topk;
     const int hh = tid >> 2, d0 = 32 * dq + (tid & 3) * 8;  // head, 8 d
@@ -437,7 +445,22 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float *__restr
         o8[e] = (__bf16)(na[e] * inv);
         o8[4 + e] = (__bf16)(nb[e] * inv);
     }
-    *(bf16x8 *)(out + (size_t(r) * kHeads + g * kGroup + hh) * kDim + d0) = o8;
+    const size_t row = size_t(r) * kHeads + g * kGroup + hh;  // (request, query head)
+    if constexpr (kMx) {
+        const u32x4 w = __builtin_bit_cast(u32x4, o8);  // element 2j in the low half of word j
+        uint16_t bits[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            bits[2 * j] = uint16_t(w[j] & 0xFFFFu);
+            bits[2 * j + 1] = uint16_t(w[j] >> 16);
+        }
+        uint32_t sc;
+        const uint64_t codes = mxfp8_encode8(bits, sc);
+        *(uint64_t *)(out_q + row * kDim + d0) = codes;
+        if ((tid & 3) == 0) out_scale[row * (kDim / 32) + dq] = uint8_t(sc);
+    } else {
+        *(bf16x8 *)(out + row * kDim + d0) = o8;
+    }
 }
 
 hipError_t launch_decode_attend(const uint16_t *q, const uint16_t *kc, const uint16_t *vc,
@@ -451,12 +474,16 @@ hipError_t launch_decode_attend(const uint16_t *q, const uint16_t *kc, const uin
     return hipGetLastError();
 }
 
-hipError_t launch_decode_combine(const float *partial, int B, int topk, uint16_t *out,
-                                 hipStream_t stream) {
+hipError_t launch_decode_combine(const float *partial, int B, int topk, uint16_t *out, uint8_t *out_q,
+                                 uint8_t *out_scale, hipStream_t stream) {
     const float *part_o = partial;
     const float *part_ml = partial + size_t(B) * kKvHeads * topk * kGroup * kDim;
-    hipLaunchKernelGGL(decode_combine_kernel, dim3(4, kKvHeads, B), dim3(64), 0, stream, part_o, part_ml,
-                       topk, out);
+    if (out_q)
+        hipLaunchKernelGGL(decode_combine_kernel<true>, dim3(4, kKvHeads, B), dim3(64), 0, stream, part_o,
+                           part_ml, topk, out, out_q, out_scale);
+    else
+        hipLaunchKernelGGL(decode_combine_kernel<false>, dim3(4, kKvHeads, B), dim3(64), 0, stream, part_o,
+                           part_ml, topk, out, out_q, out_scale);
     return hipGetLastError();
 }
 

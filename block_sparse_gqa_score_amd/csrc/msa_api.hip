@@ -253,13 +253,16 @@ msa_status msa_sparse_attend_prefill(const uint16_t *q, const uint16_t *k, const
     return MSA_OK;
 }
 
-msa_status msa_sparse_attend_decode_paged(
+// One decode step; the output is bf16 `out`, or its MXFP8 encoding when
+// out_q / out_scale are given instead.
+static msa_status decode_paged_impl(
     const uint16_t *q, const void *index_q, const uint16_t *k_cache, const uint16_t *v_cache,
     const void *index_k_cache, int index_dtype, const int32_t *page_table, int max_pages_per_seq,
     const int32_t *context_lens, int batch, int max_context_len, int topk, int init_blocks,
-    int local_blocks, float softmax_scale, uint16_t *out, int32_t *q2k_out, void *workspace,
-    size_t workspace_bytes, void *stream) {
-    if (!q || !index_q || !k_cache || !v_cache || !index_k_cache || !page_table || !context_lens || !out)
+    int local_blocks, float softmax_scale, uint16_t *out, uint8_t *out_q, uint8_t *out_scale,
+    int32_t *q2k_out, void *workspace, size_t workspace_bytes, void *stream) {
+    if (!q || !index_q || !k_cache || !v_cache || !index_k_cache || !page_table || !context_lens ||
+        !(out || (out_q && out_scale)))
         return fail(MSA_ERR_INVALID_ARG, "tensor arguments must be non-NULL (q2k_out may be NULL)");
     if (index_dtype != MSA_INDEX_BF16 && index_dtype != MSA_INDEX_FP8_E4M3)
         return fail(MSA_ERR_UNSUPPORTED, "index_dtype must be MSA_INDEX_BF16 or MSA_INDEX_FP8_E4M3");
@@ -300,9 +303,46 @@ msa_status msa_sparse_attend_decode_paged(
                              max_context_len, batch, q2k, topk, softmax_scale, part, s);
     if (e != hipSuccess) return hip_fail(e, "decode_attend");
     tm.mark(s, "decode_combine");
-    e = launch_decode_combine(part, batch, topk, out, s);
+    e = launch_decode_combine(part, batch, topk, out, out_q, out_scale, s);
     if (e != hipSuccess) return hip_fail(e, "decode_combine");
     tm.mark(s, nullptr);
+    return MSA_OK;
+}
+
+msa_status msa_sparse_attend_decode_paged(
+    const uint16_t *q, const void *index_q, const uint16_t *k_cache, const uint16_t *v_cache,
+    const void *index_k_cache, int index_dtype, const int32_t *page_table, int max_pages_per_seq,
+    const int32_t *context_lens, int batch, int max_context_len, int topk, int init_blocks,
+    int local_blocks, float softmax_scale, uint16_t *out, int32_t *q2k_out, void *workspace,
+    size_t workspace_bytes, void *stream) {
+    if (!out) return fail(MSA_ERR_INVALID_ARG, "out must be non-NULL");
+    return decode_paged_impl(q, index_q, k_cache, v_cache, index_k_cache, index_dtype, page_table,
+                             max_pages_per_seq, context_lens, batch, max_context_len, topk, init_blocks,
+                             local_blocks, softmax_scale, out, nullptr, nullptr, q2k_out, workspace,
+                             workspace_bytes, stream);
+}
+
+msa_status msa_sparse_attend_decode_paged_mxfp8(
+    const uint16_t *q, const void *index_q, const uint16_t *k_cache, const uint16_t *v_cache,
+    const void *index_k_cache, int index_dtype, const int32_t *page_table, int max_pages_per_seq,
+    const int32_t *context_lens, int batch, int max_context_len, int topk, int init_blocks,
+    int local_blocks, float softmax_scale, uint8_t *out_q, uint8_t *out_scale, int32_t *q2k_out,
+    void *workspace, size_t workspace_bytes, void *stream) {
+    if (!out_q || !out_scale) return fail(MSA_ERR_INVALID_ARG, "out_q and out_scale must be non-NULL");
+    return decode_paged_impl(q, index_q, k_cache, v_cache, index_k_cache, index_dtype, page_table,
+                             max_pages_per_seq, context_lens, batch, max_context_len, topk, init_blocks,
+                             local_blocks, softmax_scale, nullptr, out_q, out_scale, q2k_out, workspace,
+                             workspace_bytes, stream);
+}
+
+msa_status msa_mxfp8_quantize(const uint16_t *in, int rows, int cols, uint8_t *out_q, uint8_t *out_scale,
+                              void *stream) {
+    if (!in || !out_q || !out_scale) return fail(MSA_ERR_INVALID_ARG, "in, out_q and out_scale must be non-NULL");
+    if (rows < 1 || cols < 32 || cols % 32)
+        return fail(MSA_ERR_INVALID_ARG, "rows must be >= 1 and cols a positive multiple of 32 (got %d x %d)",
+                    rows, cols);
+    const hipError_t e = launch_mxfp8_quantize(in, int64_t(rows) * cols, out_q, out_scale, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "mxfp8_quantize");
     return MSA_OK;
 }
 

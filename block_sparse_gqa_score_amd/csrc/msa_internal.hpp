@@ -52,7 +52,13 @@ hipError_t launch_decode_attend(const uint16_t *q, const uint16_t *kc, const uin
                                 const int32_t *pt, int max_pages, const int32_t *ctx, int max_ctx, int B,
                                 const int32_t *q2k, int topk, float scale, float *partial,
                                 hipStream_t stream);
-hipError_t launch_decode_combine(const float *partial, int B, int topk, uint16_t *out,
+// bf16 output, or (out_q != NULL) its MXFP8 encoding: E4M3 [B, 64*128] and
+// E8M0 scales [B, 64*128/32].
+hipError_t launch_decode_combine(const float *partial, int B, int topk, uint16_t *out, uint8_t *out_q,
+                                 uint8_t *out_scale, hipStream_t stream);
+
+// MXFP8 encoding of n bf16 values (n a multiple of 32): q [n] E4M3, scale [n/32] E8M0.
+hipError_t launch_mxfp8_quantize(const uint16_t *in, int64_t n, uint8_t *q, uint8_t *scale,
                                  hipStream_t stream);
 
 }  // namespace msa

@@ -164,6 +164,40 @@ msa_status msa_sparse_attend_decode_paged(
     int32_t *q2k_out, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * The same decode step with its output emitted as MXFP8 for the projection
+ * that follows (vLLM MiniMax-M3 page, MiniMaxM3SparseRocmNvfp4Impl,
+ * forward_decode_mxfp8): equal to msa_mxfp8_quantize of the bf16 output
+ * that msa_sparse_attend_decode_paged returns for the same inputs.
+ *
+ *  out_q     [B, 64*128] E4M3FN bytes, row-major (query head, then d).
+ *  out_scale [B, 64*128/32] E8M0 bytes: scale of out_q[r, 32k..32k+31].
+ *  Every other argument, the workspace size and the errors are those of
+ *  msa_sparse_attend_decode_paged.
+ */
+msa_status msa_sparse_attend_decode_paged_mxfp8(
+    const uint16_t *q, const void *index_q, const uint16_t *k_cache, const uint16_t *v_cache,
+    const void *index_k_cache, int index_dtype, const int32_t *page_table,
+    int max_pages_per_seq, const int32_t *context_lens, int batch, int max_context_len,
+    int topk, int init_blocks, int local_blocks, float softmax_scale, uint8_t *out_q,
+    uint8_t *out_scale, int32_t *q2k_out, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * MXFP8 quantisation of bf16 values (the encoding of the decode output
+ * above; OCP Microscaling blocks of 32 consecutive values along a row).
+ *
+ *  in        [rows, cols] bf16 bits, finite; cols a positive multiple of 32.
+ *  out_q     [rows, cols] E4M3FN bytes: the value nearest to x / 2^s (ties
+ *            to the even code, magnitudes past 448 saturate to 448, the
+ *            sign of x kept).
+ *  out_scale [rows, cols/32] E8M0 bytes s + 127 per block, where
+ *            s = floor(log2(max |x| over the block)) - 8, clamped to
+ *            [-127, 127]; an all-zero block gets code 0.
+ *  No workspace.  MSA_ERR_INVALID_ARG for NULL pointers or bad sizes.
+ */
+msa_status msa_mxfp8_quantize(const uint16_t *in, int rows, int cols, uint8_t *out_q,
+                              uint8_t *out_scale, void *stream);
+
+/*
  * Benchmark instrumentation (not part of the method).  Arms the NEXT
  * entry-point call on this thread to record caller-created hipEvent_t
  * handles on its stream: events[0] before its first kernel, events[i]

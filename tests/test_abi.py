@@ -145,3 +145,37 @@ def test_product_path_does_not_import_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 for needle in ("import oracle", "from oracle", "msa_oracle", "libmsa_oracle"):
                     assert needle not in text, (f, needle)
+
+
+def _decode_mx(**kw):
+    a = dict(q=FAKE, iq=FAKE, kc=FAKE, vc=FAKE, ikc=FAKE, dtype=0, pt=FAKE, max_pages=256, ctx=FAKE,
+             B=32, max_ctx=32768, topk=16, init=0, local=1, scale=0.088, oq=FAKE, os=FAKE, q2k=None,
+             ws=FAKE, ws_bytes=1 << 40)
+    a.update(kw)
+    return msa.lib().msa_sparse_attend_decode_paged_mxfp8(
+        a["q"], a["iq"], a["kc"], a["vc"], a["ikc"], a["dtype"], a["pt"], a["max_pages"], a["ctx"],
+        a["B"], a["max_ctx"], a["topk"], a["init"], a["local"], a["scale"], a["oq"], a["os"], a["q2k"],
+        a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(oq=None), 1, "out_q"),
+    (dict(os=None), 1, "out_scale"),
+    (dict(pt=None), 1, "non-NULL"),
+    (dict(topk=0), 2, "topk"),
+    (dict(ws_bytes=100), 3, "workspace"),
+])
+def test_decode_mxfp8_rejects(kw, status, needle):
+    assert _decode_mx(**kw) == status
+    assert needle in msa.lib().msa_last_error().decode()
+
+
+@pytest.mark.parametrize("args,needle", [
+    ((None, 4, 64, FAKE, FAKE), "non-NULL"),
+    ((FAKE, 4, 48, FAKE, FAKE), "multiple of 32"),
+    ((FAKE, 0, 64, FAKE, FAKE), "rows"),
+    ((FAKE, 4, 0, FAKE, FAKE), "multiple of 32"),
+])
+def test_mxfp8_quantize_rejects(args, needle):
+    assert msa.lib().msa_mxfp8_quantize(*args, None) == 1
+    assert needle in msa.lib().msa_last_error().decode()
