@@ -18,6 +18,7 @@ Entry points (names follow the C ABI):
   sparse_attend_decode_paged_mxfp8(same arguments)
                 -> (out_q uint8 [B,8192] E4M3, out_scale uint8 [B,256] E8M0)
   mxfp8_quantize(x bf16 [rows, cols]) -> (q uint8 [rows, cols], scale uint8 [rows, cols/32])
+  cache_insert(k, v, index_k, slot_mapping, k_cache, v_cache, index_k_cache) -> None (in place)
 """
 from __future__ import annotations
 
@@ -29,7 +30,7 @@ import torch
 
 __all__ = [
     "select_blocks", "sparse_attend_prefill", "sparse_attend_decode_paged",
-    "sparse_attend_decode_paged_mxfp8", "mxfp8_quantize",
+    "sparse_attend_decode_paged_mxfp8", "mxfp8_quantize", "cache_insert",
     "unsupported_reason", "library_path", "MsaError",
     "select_blocks_workspace_bytes", "prefill_workspace_bytes", "decode_workspace_bytes",
 ]
@@ -90,6 +91,8 @@ def lib():
                                                            P, P, P, P, sz, P]
         L.msa_mxfp8_quantize.restype = i
         L.msa_mxfp8_quantize.argtypes = [P, i, i, P, P, P]
+        L.msa_cache_insert.restype = i
+        L.msa_cache_insert.argtypes = [P, P, P, P, i, i, P, P, P, i, P]
         _lib = L
     return _lib
 
@@ -242,6 +245,25 @@ def mxfp8_quantize(x):
     scale = torch.empty((rows, cols // 32), dtype=torch.uint8, device=x.device)
     _check(lib().msa_mxfp8_quantize(_ptr(x), rows, cols, _ptr(q), _ptr(scale), _stream(x.device)))
     return q, scale
+
+
+def cache_insert(k, v, index_k, slot_mapping, k_cache, v_cache, index_k_cache):
+    """Write tokens' K/V [N,4,128] and index-K [N,1,128] rows (bf16, normed and RoPE'd) into
+    the paged caches at slot_mapping[n] (negative = skip).  index_k_cache is bf16, or
+    E4M3 (torch.float8_e4m3fn / uint8) to store unscaled E4M3.  In place."""
+    device = k.device
+    N = int(k.shape[0])
+    _dev_tensor("k", k, (N, 4, 128), (torch.bfloat16,))
+    _dev_tensor("v", v, (N, 4, 128), (torch.bfloat16,), device)
+    _dev_tensor("index_k", index_k, (N, 1, 128), (torch.bfloat16,), device)
+    _dev_tensor("slot_mapping", slot_mapping, (N,), (torch.int32,), device)
+    slots = int(k_cache.shape[0])
+    _dev_tensor("k_cache", k_cache, (slots, 4, 128), (torch.bfloat16,), device)
+    _dev_tensor("v_cache", v_cache, (slots, 4, 128), (torch.bfloat16,), device)
+    _dev_tensor("index_k_cache", index_k_cache, (slots, 1, 128), _INDEX_DTYPES, device)
+    _check(lib().msa_cache_insert(_ptr(k), _ptr(v), _ptr(index_k), _ptr(slot_mapping), N,
+                                  _index_code(index_k_cache), _ptr(k_cache), _ptr(v_cache),
+                                  _ptr(index_k_cache), slots, _stream(device)))
 
 
 def _decode(q, index_q, k_cache, v_cache, index_k_cache, page_table, context_lens, max_context_len,

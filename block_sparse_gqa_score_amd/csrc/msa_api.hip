@@ -335,6 +335,23 @@ msa_status msa_sparse_attend_decode_paged_mxfp8(
                              workspace_bytes, stream);
 }
 
+msa_status msa_cache_insert(const uint16_t *k, const uint16_t *v, const uint16_t *index_k,
+                            const int32_t *slot_mapping, int num_tokens, int index_dtype, uint16_t *k_cache,
+                            uint16_t *v_cache, void *index_k_cache, int num_slots, void *stream) {
+    if (!k || !v || !index_k || !slot_mapping || !k_cache || !v_cache || !index_k_cache)
+        return fail(MSA_ERR_INVALID_ARG, "tensor arguments must be non-NULL");
+    if (index_dtype != MSA_INDEX_BF16 && index_dtype != MSA_INDEX_FP8_E4M3)
+        return fail(MSA_ERR_UNSUPPORTED, "index_dtype must be MSA_INDEX_BF16 or MSA_INDEX_FP8_E4M3");
+    if (num_tokens < 0) return fail(MSA_ERR_INVALID_ARG, "num_tokens must be >= 0 (got %d)", num_tokens);
+    if (num_slots < 1) return fail(MSA_ERR_INVALID_ARG, "num_slots must be >= 1 (got %d)", num_slots);
+    if (num_tokens == 0) return MSA_OK;
+    const hipError_t e = launch_cache_insert(k, v, index_k, slot_mapping, num_tokens, num_slots,
+                                             index_dtype == MSA_INDEX_FP8_E4M3, k_cache, v_cache,
+                                             index_k_cache, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "cache_insert");
+    return MSA_OK;
+}
+
 msa_status msa_mxfp8_quantize(const uint16_t *in, int rows, int cols, uint8_t *out_q, uint8_t *out_scale,
                               void *stream) {
     if (!in || !out_q || !out_scale) return fail(MSA_ERR_INVALID_ARG, "in, out_q and out_scale must be non-NULL");

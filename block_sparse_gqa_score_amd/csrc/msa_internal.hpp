@@ -57,6 +57,12 @@ hipError_t launch_decode_attend(const uint16_t *q, const uint16_t *kc, const uin
 hipError_t launch_decode_combine(const float *partial, int B, int topk, uint16_t *out, uint8_t *out_q,
                                  uint8_t *out_scale, hipStream_t stream);
 
+// Paged-cache insertion of n tokens' K, V and index-K rows (index-K stored
+// as bf16, or as unscaled E4M3 when fp8).
+hipError_t launch_cache_insert(const uint16_t *k, const uint16_t *v, const uint16_t *ik, const int32_t *slots,
+                               int n, int num_slots, bool fp8, uint16_t *kc, uint16_t *vc, void *ikc,
+                               hipStream_t stream);
+
 // MXFP8 encoding of n bf16 values (n a multiple of 32): q [n] E4M3, scale [n/32] E8M0.
 hipError_t launch_mxfp8_quantize(const uint16_t *in, int64_t n, uint8_t *q, uint8_t *scale,
                                  hipStream_t stream);

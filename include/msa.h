@@ -182,6 +182,28 @@ msa_status msa_sparse_attend_decode_paged_mxfp8(
     uint8_t *out_scale, int32_t *q2k_out, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Paged-cache insertion: the write that precedes decode (TensorRT-LLM config
+ * class description, fuse_qkv_index_projection: the norm/RoPE/cache-insertion
+ * producer; the side index-K cache parallel to the main K/V cache, same
+ * slot).  Only the write: the rows arrive normed and RoPE'd.
+ *
+ *  k, v          [num_tokens, 4, 128] bf16 bits; index_k [num_tokens, 1, 128]
+ *                bf16 bits.
+ *  slot_mapping  int32 [num_tokens]: token n goes to slot slot_mapping[n]
+ *                (= page * 128 + offset); negative slots, and slots
+ *                >= num_slots, are skipped.  Slots must be distinct.
+ *  k_cache, v_cache [num_slots, 4, 128] bf16; index_k_cache
+ *                [num_slots, 1, 128] in index_dtype: bf16 rows are copied,
+ *                MSA_INDEX_FP8_E4M3 stores unscaled E4M3FN (nearest value,
+ *                ties to the even code, magnitudes past 448 saturate).
+ *  Slots not named are left untouched.  No workspace.
+ */
+msa_status msa_cache_insert(const uint16_t *k, const uint16_t *v, const uint16_t *index_k,
+                            const int32_t *slot_mapping, int num_tokens, int index_dtype,
+                            uint16_t *k_cache, uint16_t *v_cache, void *index_k_cache,
+                            int num_slots, void *stream);
+
+/*
  * MXFP8 quantisation of bf16 values (the encoding of the decode output
  * above; OCP Microscaling blocks of 32 consecutive values along a row).
  *

@@ -179,3 +179,22 @@ def test_decode_mxfp8_rejects(kw, status, needle):
 def test_mxfp8_quantize_rejects(args, needle):
     assert msa.lib().msa_mxfp8_quantize(*args, None) == 1
     assert needle in msa.lib().msa_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(k=None), 1, "non-NULL"),
+    (dict(dtype=5), 2, "index_dtype"),
+    (dict(n=-1), 1, "num_tokens"),
+    (dict(slots=0), 1, "num_slots"),
+])
+def test_cache_insert_rejects(kw, status, needle):
+    a = dict(k=FAKE, v=FAKE, ik=FAKE, sm=FAKE, n=4, dtype=0, kc=FAKE, vc=FAKE, ikc=FAKE, slots=128)
+    a.update(kw)
+    st = msa.lib().msa_cache_insert(a["k"], a["v"], a["ik"], a["sm"], a["n"], a["dtype"], a["kc"], a["vc"],
+                                    a["ikc"], a["slots"], None)
+    assert st == status
+    assert needle in msa.lib().msa_last_error().decode()
+
+
+def test_cache_insert_of_nothing_is_a_no_op():
+    assert msa.lib().msa_cache_insert(FAKE, FAKE, FAKE, FAKE, 0, 0, FAKE, FAKE, FAKE, 128, None) == 0
