@@ -187,6 +187,9 @@ class Decode:
     local_blocks: int = 1
     scale: float = 1.0 / math.sqrt(128.0)
     meta: dict = field(default_factory=dict)
+    kv_dtype: str = "bf16"           # "fp8": k/v caches hold E4M3FN bytes of x / k_scale, x / v_scale
+    k_scale: float = 1.0
+    v_scale: float = 1.0
 
     @property
     def B(self) -> int:
@@ -278,10 +281,12 @@ def packed_doc_lengths(seed: int, rows: int = 2, seq: int = 16384,
 
 def make_decode(context_lens, seed: int, *, topk=16, init_blocks=0, local_blocks=1,
                 index_dtype="bf16", name="decode", identity_pages=False,
-                poison_tail=True) -> Decode:
+                poison_tail=True, kv_dtype="bf16", k_scale=0.5, v_scale=0.25) -> Decode:
     """Paged decode step: pages of 128 slots, physical page ids a random
     permutation of all pages (identity when ``identity_pages``).  Slots past
-    each request's context length are filled with NaN when ``poison_tail``."""
+    each request's context length are filled with NaN when ``poison_tail``.
+    With ``kv_dtype="fp8"`` the main K/V caches hold E4M3FN bytes of the same
+    N(0,1) values divided by ``k_scale`` / ``v_scale`` (per-tensor scales)."""
     L = np.asarray(context_lens, dtype=np.int32)
     if L.min() < 1:
         raise ValueError("context lengths must be >= 1")
@@ -293,8 +298,14 @@ def make_decode(context_lens, seed: int, *, topk=16, init_blocks=0, local_blocks
     q = normal_bf16(s_q, (B, NUM_HEADS, HEAD_DIM))
     iq = encode_index(rms_normalise(normal_f32(s_iq, (B, NUM_INDEX_HEADS, HEAD_DIM))),
                       index_dtype)
-    k_cache = normal_bf16(s_k, (P * BLOCK, NUM_KV_HEADS, HEAD_DIM))
-    v_cache = normal_bf16(s_v, (P * BLOCK, NUM_KV_HEADS, HEAD_DIM))
+    if kv_dtype == "fp8":
+        k_cache = e4m3_bytes(normal_f32(s_k, (P * BLOCK, NUM_KV_HEADS, HEAD_DIM)) / np.float32(k_scale))
+        v_cache = e4m3_bytes(normal_f32(s_v, (P * BLOCK, NUM_KV_HEADS, HEAD_DIM)) / np.float32(v_scale))
+    elif kv_dtype == "bf16":
+        k_cache = normal_bf16(s_k, (P * BLOCK, NUM_KV_HEADS, HEAD_DIM))
+        v_cache = normal_bf16(s_v, (P * BLOCK, NUM_KV_HEADS, HEAD_DIM))
+    else:
+        raise ValueError(kv_dtype)
     ik_cache = encode_index(rms_normalise(normal_f32(s_ik, (P * BLOCK, 1, HEAD_DIM))),
                             index_dtype)
     if identity_pages:
@@ -317,13 +328,15 @@ def make_decode(context_lens, seed: int, *, topk=16, init_blocks=0, local_blocks
             page = int(page_table[r, nb[r] - 1])
             s0 = page * BLOCK + (BLOCK - tail)
             s1 = (page + 1) * BLOCK
-            k_cache[s0:s1] = nan_bits
-            v_cache[s0:s1] = nan_bits
+            k_cache[s0:s1] = fp8_nan if kv_dtype == "fp8" else nan_bits
+            v_cache[s0:s1] = fp8_nan if kv_dtype == "fp8" else nan_bits
             ik_cache[s0:s1] = fp8_nan if index_dtype == "fp8" else nan_bits
     return Decode(name=name, q=q, iq=iq, k_cache=k_cache, v_cache=v_cache,
                   ik_cache=ik_cache, page_table=page_table, context_lens=L,
                   index_dtype=index_dtype, topk=topk, init_blocks=init_blocks,
-                  local_blocks=local_blocks)
+                  local_blocks=local_blocks, kv_dtype=kv_dtype,
+                  k_scale=float(k_scale) if kv_dtype == "fp8" else 1.0,
+                  v_scale=float(v_scale) if kv_dtype == "fp8" else 1.0)
 
 
 # --------------------------------------------------------------------------
