@@ -143,6 +143,29 @@ def stats(xs):
                 p90=float(np.percentile(a, 90)))
 
 
+def graph_replay_ms(issue, s, steps, hip, stream, flush):
+    """Capture one call (issue() launches on torch's current stream and returns
+    its status) into a HIP graph on side stream s; time `steps` replays on
+    `stream` with HIP events."""
+    import torch
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            st = issue()
+            assert st == 0, st
+    torch.cuda.current_stream().wait_stream(s)
+    ga, gb = hip.events(steps), hip.events(steps)
+    for i in range(steps):
+        if flush is not None:
+            flush.sum()
+        hip.record(ga[i], stream)
+        g.replay()
+        hip.record(gb[i], stream)
+    torch.cuda.synchronize()
+    return stats([hip.elapsed_ms(ga[i], gb[i]) for i in range(steps)])
+
+
 def bench_decode(args, hip, flush):
     import numpy as np
     import torch
@@ -176,46 +199,45 @@ def bench_decode(args, hip, flush):
     graph_ms = mx_graph_ms = None
     if not args.no_graph:
         s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(s):
-            gstream = torch.cuda.current_stream().cuda_stream
-            with torch.cuda.graph(g, stream=s):
-                st = L.msa_sparse_attend_decode_paged(
-                    P(dq), P(diq), P(dk), P(dv), P(dik), 0, P(dpt), d.max_pages, P(dctx), d.B,
-                    d.max_context_len, d.topk, d.init_blocks, d.local_blocks, d.scale, P(out), None,
-                    P(ws), ws.numel(), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
-                assert st == 0
-        torch.cuda.current_stream().wait_stream(s)
-        ga, gb = hip.events(args.steps), hip.events(args.steps)
-        for i in range(args.steps):
-            if flush is not None:
-                flush.sum()
-            hip.record(ga[i], stream)
-            g.replay()
-            hip.record(gb[i], stream)
-        torch.cuda.synchronize()
-        graph_ms = stats([hip.elapsed_ms(ga[i], gb[i]) for i in range(args.steps)])
+
+        def gstream():
+            return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+        graph_ms = graph_replay_ms(lambda: L.msa_sparse_attend_decode_paged(
+            P(dq), P(diq), P(dk), P(dv), P(dik), 0, P(dpt), d.max_pages, P(dctx), d.B,
+            d.max_context_len, d.topk, d.init_blocks, d.local_blocks, d.scale, P(out), None,
+            P(ws), ws.numel(), gstream()), s, args.steps, hip, stream, flush)
         # the same step with the output emitted as MXFP8 (E4M3 + E8M0 per 32)
         oq = torch.empty((d.B, 64 * 128), dtype=torch.uint8, device="cuda")
         osc = torch.empty((d.B, 64 * 128 // 32), dtype=torch.uint8, device="cuda")
-        g2 = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(s):
-            with torch.cuda.graph(g2, stream=s):
-                st = L.msa_sparse_attend_decode_paged_mxfp8(
-                    P(dq), P(diq), P(dk), P(dv), P(dik), 0, P(dpt), d.max_pages, P(dctx), d.B,
-                    d.max_context_len, d.topk, d.init_blocks, d.local_blocks, d.scale, P(oq), P(osc),
-                    None, P(ws), ws.numel(), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
-                assert st == 0
-        torch.cuda.current_stream().wait_stream(s)
-        for i in range(args.steps):
-            if flush is not None:
-                flush.sum()
-            hip.record(ga[i], stream)
-            g2.replay()
-            hip.record(gb[i], stream)
-        torch.cuda.synchronize()
-        mx_graph_ms = stats([hip.elapsed_ms(ga[i], gb[i]) for i in range(args.steps)])
+        mx_graph_ms = graph_replay_ms(lambda: L.msa_sparse_attend_decode_paged_mxfp8(
+            P(dq), P(diq), P(dk), P(dv), P(dik), 0, P(dpt), d.max_pages, P(dctx), d.B,
+            d.max_context_len, d.topk, d.init_blocks, d.local_blocks, d.scale, P(oq), P(osc),
+            None, P(ws), ws.numel(), gstream()), s, args.steps, hip, stream, flush)
+
+    # the same step over E4M3 K/V caches with per-tensor scales (caches made
+    # from the bf16 ones before timing; NaN tails stay NaN)
+    ks, vs = 1.0 / 32, 1.0 / 32  # N(0,1) rows: |x|/scale stays far below 448
+    fk = (dk.float() / ks).to(torch.float8_e4m3fn).view(torch.uint8)
+    fv = (dv.float() / vs).to(torch.float8_e4m3fn).view(torch.uint8)
+    out8 = torch.empty_like(out)
+
+    def run8(events):
+        if events is not None:
+            L.msa_set_timing_events(ctypes.c_void_p(ctypes.addressof(events)), len(events))
+        st = L.msa_sparse_attend_decode_paged_fp8kv(
+            P(dq), P(diq), P(fk), P(fv), ks, vs, P(dik), 0, P(dpt), d.max_pages, P(dctx), d.B,
+            d.max_context_len, d.topk, d.init_blocks, d.local_blocks, d.scale, P(out8), None, P(ws),
+            ws.numel(), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        if st != 0:
+            raise RuntimeError(L.msa_last_error().decode())
+
+    fp8_step, evs8, names8 = timed_steps(run8, args.steps, args.warmup, hip, stream, flush, 5)
+    fp8_kt = {k: stats(v)["mean"] for k, v in kernel_times(evs8, [names8], hip).items()}
+    fp8_graph = None
+    if not args.no_graph:
+        fp8_graph = graph_replay_ms(lambda: run8(None) or 0, s, args.steps, hip, stream, flush)
+    fp8kv = dict(step=stats(fp8_step), graph=fp8_graph, per_kernel_ms=fp8_kt, k_scale=ks, v_scale=vs)
 
     # algorithmic bytes (per request: index-K rows, selected K/V rows, q/iq/out, page table)
     lens = d.context_lens.astype(np.int64)
@@ -226,9 +248,11 @@ def bench_decode(args, hip, flush):
     total_bytes = idx_bytes + kv_bytes + qo_bytes
     per_kernel = {k: stats(v)["mean"] for k, v in kt.items()}
     alg = {"decode_scores": idx_bytes, "decode_attend": kv_bytes + d.B * 64 * 128 * 2}
+    fp8kv["attend_alg_bytes"] = kv_bytes // 2 + d.B * 64 * 128 * 2
     dom = max(alg, key=lambda k: per_kernel.get(k, 0.0))
     return dict(d=d, gen_s=gen_s, step=stats(step_ms), per_kernel_ms=per_kernel, alg_bytes=alg,
-                dominant=dom, total_bytes=total_bytes, out=out, graph=graph_ms, mx_graph=mx_graph_ms)
+                dominant=dom, total_bytes=total_bytes, out=out, graph=graph_ms, mx_graph=mx_graph_ms,
+                fp8kv=fp8kv)
 
 
 def bench_prefill(args, hip, flush):
@@ -351,6 +375,21 @@ def calibrate_copy():
     print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n, "dispatches": 3}))
 
 
+def fp8kv_summary(dres):
+    f = dres["fp8kv"]
+    a_ms = f["per_kernel_ms"]["decode_attend"]
+    bw = f["attend_alg_bytes"] / (a_ms * 1e-3) / 1e9
+    return {"step_us": round((f["graph"] or f["step"])["median"] * 1e3, 3),
+            "launch": "hip_graph_replay" if f["graph"] is not None else "direct",
+            "per_kernel_us": {k: round(v * 1e3, 3) for k, v in f["per_kernel_ms"].items()},
+            "k_scale": f["k_scale"], "v_scale": f["v_scale"],
+            "attend_roofline": {"bound": "hbm", "achieved": round(bw, 1), "peak": PEAK_HBM_GBS,
+                                "unit": "GB/s", "frac": round(bw / PEAK_HBM_GBS, 4),
+                                "alg_bytes_per_launch": f["attend_alg_bytes"],
+                                "traffic": measured_traffic("decode_attend_fp8kv"),
+                                "avg_launch_us": round(a_ms * 1e3, 3)}}
+
+
 def main():
     args = parse()
     if args.calibrate_copy:
@@ -403,6 +442,7 @@ def main():
         "direct_launch_step_ms": {k: round(v, 6) for k, v in dres["step"].items()},
         "mxfp8_output_step_us": (round(dres["mx_graph"]["median"] * 1e3, 3)
                                  if dres["mx_graph"] is not None else None),
+        "fp8_kv_cache": fp8kv_summary(dres),
         "per_kernel_us": {k: round(v * 1e3, 3) for k, v in dres["per_kernel_ms"].items()},
         "path_bytes_per_step": dres["total_bytes"],
         "path_hbm_frac": round(dres["total_bytes"] / (step_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),

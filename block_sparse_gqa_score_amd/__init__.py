@@ -18,6 +18,9 @@ Entry points (names follow the C ABI):
   sparse_attend_decode_paged_mxfp8(same arguments)
                 -> (out_q uint8 [B,8192] E4M3, out_scale uint8 [B,256] E8M0)
   mxfp8_quantize(x bf16 [rows, cols]) -> (q uint8 [rows, cols], scale uint8 [rows, cols/32])
+  sparse_attend_decode_paged_fp8kv(q, index_q, k_cache, v_cache, k_scale, v_scale, index_k_cache,
+                page_table, context_lens, max_context_len, ...) -> out [B,64,128]
+                (K/V caches as E4M3 bytes with per-tensor scales)
   cache_insert(k, v, index_k, slot_mapping, k_cache, v_cache, index_k_cache) -> None (in place)
 """
 from __future__ import annotations
@@ -30,7 +33,8 @@ import torch
 
 __all__ = [
     "select_blocks", "sparse_attend_prefill", "sparse_attend_decode_paged",
-    "sparse_attend_decode_paged_mxfp8", "mxfp8_quantize", "cache_insert",
+    "sparse_attend_decode_paged_mxfp8", "sparse_attend_decode_paged_fp8kv", "mxfp8_quantize",
+    "cache_insert",
     "unsupported_reason", "library_path", "MsaError",
     "select_blocks_workspace_bytes", "prefill_workspace_bytes", "decode_workspace_bytes",
 ]
@@ -91,6 +95,9 @@ def lib():
                                                            P, P, P, P, sz, P]
         L.msa_mxfp8_quantize.restype = i
         L.msa_mxfp8_quantize.argtypes = [P, i, i, P, P, P]
+        L.msa_sparse_attend_decode_paged_fp8kv.restype = i
+        L.msa_sparse_attend_decode_paged_fp8kv.argtypes = [P, P, P, P, f, f, P, i, P, i, P, i, i, i, i, i,
+                                                           f, P, P, P, sz, P]
         L.msa_cache_insert.restype = i
         L.msa_cache_insert.argtypes = [P, P, P, P, i, i, P, P, P, i, P]
         _lib = L
@@ -232,6 +239,17 @@ def sparse_attend_decode_paged_mxfp8(q, index_q, k_cache, v_cache, index_k_cache
                    workspace, mxfp8=True)
 
 
+def sparse_attend_decode_paged_fp8kv(q, index_q, k_cache, v_cache, k_scale, v_scale, index_k_cache,
+                                     page_table, context_lens, max_context_len, topk=16, init_blocks=0,
+                                     local_blocks=1, softmax_scale=None, return_q2k=False,
+                                     workspace=None):
+    """One decode step over E4M3 K/V caches [slots,4,128] (torch.float8_e4m3fn or uint8) with
+    per-tensor scales (K = e4m3 * k_scale, V = e4m3 * v_scale) -> bf16 out [B,64,128]."""
+    return _decode(q, index_q, k_cache, v_cache, index_k_cache, page_table, context_lens,
+                   max_context_len, topk, init_blocks, local_blocks, softmax_scale, return_q2k,
+                   workspace, mxfp8=False, kv_scales=(float(k_scale), float(v_scale)))
+
+
 def mxfp8_quantize(x):
     """MXFP8 of a bf16 matrix [rows, cols] (cols % 32 == 0) -> (q uint8 [rows, cols] E4M3,
     scale uint8 [rows, cols/32] E8M0)."""
@@ -258,8 +276,9 @@ def cache_insert(k, v, index_k, slot_mapping, k_cache, v_cache, index_k_cache):
     _dev_tensor("index_k", index_k, (N, 1, 128), (torch.bfloat16,), device)
     _dev_tensor("slot_mapping", slot_mapping, (N,), (torch.int32,), device)
     slots = int(k_cache.shape[0])
-    _dev_tensor("k_cache", k_cache, (slots, 4, 128), (torch.bfloat16,), device)
-    _dev_tensor("v_cache", v_cache, (slots, 4, 128), (torch.bfloat16,), device)
+    kv_types = (torch.bfloat16,) if kv_scales is None else (torch.float8_e4m3fn, torch.uint8)
+    _dev_tensor("k_cache", k_cache, (slots, 4, 128), kv_types, device)
+    _dev_tensor("v_cache", v_cache, (slots, 4, 128), kv_types, device)
     _dev_tensor("index_k_cache", index_k_cache, (slots, 1, 128), _INDEX_DTYPES, device)
     _check(lib().msa_cache_insert(_ptr(k), _ptr(v), _ptr(index_k), _ptr(slot_mapping), N,
                                   _index_code(index_k_cache), _ptr(k_cache), _ptr(v_cache),
@@ -267,14 +286,16 @@ def cache_insert(k, v, index_k, slot_mapping, k_cache, v_cache, index_k_cache):
 
 
 def _decode(q, index_q, k_cache, v_cache, index_k_cache, page_table, context_lens, max_context_len,
-            topk, init_blocks, local_blocks, softmax_scale, return_q2k, workspace, mxfp8):
+            topk, init_blocks, local_blocks, softmax_scale, return_q2k, workspace, mxfp8,
+            kv_scales=None):
     device = q.device
     B = int(q.shape[0])
     _dev_tensor("q", q, (B, 64, 128), (torch.bfloat16,))
     _dev_tensor("index_q", index_q, (B, 4, 128), _INDEX_DTYPES, device)
     slots = int(k_cache.shape[0])
-    _dev_tensor("k_cache", k_cache, (slots, 4, 128), (torch.bfloat16,), device)
-    _dev_tensor("v_cache", v_cache, (slots, 4, 128), (torch.bfloat16,), device)
+    kv_types = (torch.bfloat16,) if kv_scales is None else (torch.float8_e4m3fn, torch.uint8)
+    _dev_tensor("k_cache", k_cache, (slots, 4, 128), kv_types, device)
+    _dev_tensor("v_cache", v_cache, (slots, 4, 128), kv_types, device)
     _dev_tensor("index_k_cache", index_k_cache, (slots, 1, 128), (index_q.dtype,), device)
     if page_table.dim() != 2 or page_table.shape[0] != B:
         raise ValueError(f"page_table must have shape [{B}, max_pages]")
@@ -286,12 +307,17 @@ def _decode(q, index_q, k_cache, v_cache, index_k_cache, page_table, context_len
     need = decode_workspace_bytes(B, int(max_context_len), int(topk))
     if workspace is None:
         workspace = _workspace(need, device)
-    head = (_ptr(q), _ptr(index_q), _ptr(k_cache), _ptr(v_cache), _ptr(index_k_cache),
-            _index_code(index_q), _ptr(page_table), int(page_table.shape[1]), _ptr(context_lens), B,
-            int(max_context_len), int(topk), int(init_blocks), int(local_blocks),
+    rest = (_ptr(index_k_cache), _index_code(index_q), _ptr(page_table), int(page_table.shape[1]),
+            _ptr(context_lens), B, int(max_context_len), int(topk), int(init_blocks), int(local_blocks),
             float(softmax_scale))
+    head = (_ptr(q), _ptr(index_q), _ptr(k_cache), _ptr(v_cache)) + rest
     tail = (_ptr(q2k), _ptr(workspace), workspace.numel(), _stream(device))
-    if mxfp8:
+    if kv_scales is not None:
+        out = torch.empty((B, 64, 128), dtype=torch.bfloat16, device=device)
+        _check(lib().msa_sparse_attend_decode_paged_fp8kv(_ptr(q), _ptr(index_q), _ptr(k_cache),
+                                                          _ptr(v_cache), *kv_scales, *rest, _ptr(out),
+                                                          *tail))
+    elif mxfp8:
         out_q = torch.empty((B, 64 * 128), dtype=torch.uint8, device=device)
         out_scale = torch.empty((B, 64 * 128 // 32), dtype=torch.uint8, device=device)
         _check(lib().msa_sparse_attend_decode_paged_mxfp8(*head, _ptr(out_q), _ptr(out_scale), *tail))

@@ -233,17 +233,29 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 __device__ __forceinline__ int vswz(int r) { return r & 15; }
 }  // namespace
 
+// Two E4M3FN bytes (the low or high 16 bits of w) -> two bf16, packed (exact:
+// every E4M3 value is a bf16 value).
+template <bool kHi>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, kHi));
+}
+
 // Workgroup (s, g, r): selected block s of KV head g for request r; 4 waves,
 // wave w owns keys 32w..32w+31 of the block.
 //   S^T[32 keys x 16 heads] = K . Q^T   (MFMA 16x16x32, K straight from HBM)
 //   per-wave softmax partial, V rows copied HBM -> LDS (global_load_lds),
 //   O^T[128 x 16] = V^T . P^T with V^T from ds_read_b64_tr_b16,
 //   the 4 waves merged in LDS into one (O, m, l) partial of the block.
+// kFp8Kv: K/V caches hold E4M3FN bytes.  E4M3 values are exact in bf16, so
+// K and V are converted exactly (V into the bf16 LDS layout of the other
+// variant); the K scale is folded into scale_log2 by the caller and the V
+// scale multiplies the block's partial O.
+template <bool kFp8Kv>
 __global__ __launch_bounds__(256) void decode_attend_kernel(
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc, const uint16_t *__restrict__ vc,
+    const uint16_t *__restrict__ q, const void *__restrict__ kc_, const void *__restrict__ vc_,
     const int32_t *__restrict__ pt, int max_pages, const int32_t *__restrict__ ctx, int max_ctx,
-    int B, const int32_t *__restrict__ q2k, int topk, float scale_log2, float *__restrict__ part_o,
-    float *__restrict__ part_ml) {
+    int B, const int32_t *__restrict__ q2k, int topk, float scale_log2, float v_scale,
+    float *__restrict__ part_o, float *__restrict__ part_ml) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * kWaveVBytes];  // V, then O^T
     __shared__ float s_m[4][16], s_l[4][16];
     const int s = blockIdx.x, g = blockIdx.y, r = blockIdx.z;
@@ -263,15 +275,39 @@ __global__ __launch_bounds__(256) void decode_attend_kernel(
         const int kmax = L - 1 - b * kBlock;  // last valid key of the block
         uint8_t *vt = smem + wave * kWaveVBytes;
 
-        // V rows key0..key0+31 -> LDS (8 one-KiB copies); rows past L re-read
-        // the last valid row (their probabilities are 0).
+        // V rows key0..key0+31 -> LDS; rows past L re-read the last valid row
+        // (their probabilities are 0).
+        if constexpr (!kFp8Kv) {
+            // 8 one-KiB copies straight into the swizzled bf16 layout
+            const uint16_t *vc = (const uint16_t *)vc_;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int rr = 4 * j + (lane >> 4);  // row within the wave's 32
-            const int chunk = (lane & 15) ^ vswz(rr);
-            const int key = min(key0 + rr, kmax);
-            const uint16_t *src = vc + ((slot0 + key) * kKvHeads + g) * kDim + 8 * chunk;
-            __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(vt + j * 1024), 16, 0, 0);
+            for (int j = 0; j < 8; ++j) {
+                const int rr = 4 * j + (lane >> 4);  // row within the wave's 32
+                const int chunk = (lane & 15) ^ vswz(rr);
+                const int key = min(key0 + rr, kmax);
+                const uint16_t *src = vc + ((slot0 + key) * kKvHeads + g) * kDim + 8 * chunk;
+                __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(vt + j * 1024), 16, 0, 0);
+            }
+        } else {
+            // lane: 16 E4M3 values (d 16c..16c+15) of row 8j + lane/8, written
+            // as the two bf16 chunks 2c, 2c+1 of that row
+            const uint8_t *vc = (const uint8_t *)vc_;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int rr = 8 * j + (lane >> 3), c = lane & 7;
+                const int key = min(key0 + rr, kmax);
+                const u32x4 x = *(const u32x4 *)(vc + ((slot0 + key) * kKvHeads + g) * kDim + 16 * c);
+                u32x4 lo, hi;
+#pragma unroll
+                for (int w = 0; w < 2; ++w) {
+                    lo[2 * w] = e4m3x2_to_bf16x2<false>(x[w]);
+                    lo[2 * w + 1] = e4m3x2_to_bf16x2<true>(x[w]);
+                    hi[2 * w] = e4m3x2_to_bf16x2<false>(x[2 + w]);
+                    hi[2 * w + 1] = e4m3x2_to_bf16x2<true>(x[2 + w]);
+                }
+                *(u32x4 *)(vt + rr * kRowB + (((2 * c) ^ vswz(rr)) << 4)) = lo;
+                *(u32x4 *)(vt + rr * kRowB + (((2 * c + 1) ^ vswz(rr)) << 4)) = hi;
+            }
         }
         // Q^T operand: lane (n = head, qd), step ks: 16-byte chunk 4ks + qd
         const uint16_t *qrow = q + (size_t(r) * kHeads + g * kGroup + n) * kDim;
@@ -284,9 +320,19 @@ __global__ __launch_bounds__(256) void decode_attend_kernel(
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
             const int key = min(key0 + 16 * mt + n, kmax);
-            const uint16_t *src = kc + ((slot0 + key) * kKvHeads + g) * kDim;
+            if constexpr (!kFp8Kv) {
+                const uint16_t *src = (const uint16_t *)kc_ + ((slot0 + key) * kKvHeads + g) * kDim;
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) ka[mt][ks] = *(const u32x4 *)(src + 8 * (4 * ks + qd));
+                for (int ks = 0; ks < 4; ++ks) ka[mt][ks] = *(const u32x4 *)(src + 8 * (4 * ks + qd));
+            } else {
+                const uint8_t *src = (const uint8_t *)kc_ + ((slot0 + key) * kKvHeads + g) * kDim;
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    const u32x2 x = *(const u32x2 *)(src + 8 * (4 * ks + qd));
+                    ka[mt][ks] = u32x4{e4m3x2_to_bf16x2<false>(x[0]), e4m3x2_to_bf16x2<true>(x[0]),
+                                       e4m3x2_to_bf16x2<false>(x[1]), e4m3x2_to_bf16x2<true>(x[1])};
+                }
+            }
         }
         f32x4 sacc[2];
 #pragma unroll
@@ -377,6 +423,10 @@ __global__ __launch_bounds__(256) void decode_attend_kernel(
                 acc += sc[w] * ((const float *)(smem + w * kWaveVBytes))[hh * kDim + d0 + e];
             o[e] = acc;
         }
+        if constexpr (kFp8Kv) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] *= v_scale;
+        }
         *(f32x4 *)(po + hh * kDim + d0) = f32x4{o[0], o[1], o[2], o[3]};
         *(f32x4 *)(po + hh * kDim + d0 + 4) = f32x4{o[4], o[5], o[6], o[7]};
         if ((tid & 15) == 0) {
@@ -463,14 +513,19 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float *__restr
     }
 }
 
-hipError_t launch_decode_attend(const uint16_t *q, const uint16_t *kc, const uint16_t *vc,
-                                const int32_t *pt, int max_pages, const int32_t *ctx, int max_ctx, int B,
-                                const int32_t *q2k, int topk, float scale, float *partial,
-                                hipStream_t stream) {
+hipError_t launch_decode_attend(const uint16_t *q, const void *kc, const void *vc, bool fp8kv, float k_scale,
+                                float v_scale, const int32_t *pt, int max_pages, const int32_t *ctx,
+                                int max_ctx, int B, const int32_t *q2k, int topk, float scale,
+                                float *partial, hipStream_t stream) {
     float *part_o = partial;
     float *part_ml = partial + size_t(B) * kKvHeads * topk * kGroup * kDim;
-    hipLaunchKernelGGL(decode_attend_kernel, dim3(topk, kKvHeads, B), dim3(256), 0, stream, q, kc, vc,
-                       pt, max_pages, ctx, max_ctx, B, q2k, topk, scale * kLog2e, part_o, part_ml);
+    const dim3 grid(topk, kKvHeads, B);
+    if (fp8kv)
+        hipLaunchKernelGGL(decode_attend_kernel<true>, grid, dim3(256), 0, stream, q, kc, vc, pt, max_pages,
+                           ctx, max_ctx, B, q2k, topk, scale * kLog2e * k_scale, v_scale, part_o, part_ml);
+    else
+        hipLaunchKernelGGL(decode_attend_kernel<false>, grid, dim3(256), 0, stream, q, kc, vc, pt, max_pages,
+                           ctx, max_ctx, B, q2k, topk, scale * kLog2e, 1.0f, part_o, part_ml);
     return hipGetLastError();
 }
 

@@ -256,8 +256,9 @@ msa_status msa_sparse_attend_prefill(const uint16_t *q, const uint16_t *k, const
 // One decode step; the output is bf16 `out`, or its MXFP8 encoding when
 // out_q / out_scale are given instead.
 static msa_status decode_paged_impl(
-    const uint16_t *q, const void *index_q, const uint16_t *k_cache, const uint16_t *v_cache,
-    const void *index_k_cache, int index_dtype, const int32_t *page_table, int max_pages_per_seq,
+    const uint16_t *q, const void *index_q, const void *k_cache, const void *v_cache, bool kv_fp8,
+    float k_scale, float v_scale, const void *index_k_cache, int index_dtype, const int32_t *page_table,
+    int max_pages_per_seq,
     const int32_t *context_lens, int batch, int max_context_len, int topk, int init_blocks,
     int local_blocks, float softmax_scale, uint16_t *out, uint8_t *out_q, uint8_t *out_scale,
     int32_t *q2k_out, void *workspace, size_t workspace_bytes, void *stream) {
@@ -299,8 +300,8 @@ static msa_status decode_paged_impl(
                            local_blocks, q2k, s);
     if (e != hipSuccess) return hip_fail(e, "decode_topk");
     tm.mark(s, "decode_attend");
-    e = launch_decode_attend(q, k_cache, v_cache, page_table, max_pages_per_seq, context_lens,
-                             max_context_len, batch, q2k, topk, softmax_scale, part, s);
+    e = launch_decode_attend(q, k_cache, v_cache, kv_fp8, k_scale, v_scale, page_table, max_pages_per_seq,
+                             context_lens, max_context_len, batch, q2k, topk, softmax_scale, part, s);
     if (e != hipSuccess) return hip_fail(e, "decode_attend");
     tm.mark(s, "decode_combine");
     e = launch_decode_combine(part, batch, topk, out, out_q, out_scale, s);
@@ -316,7 +317,7 @@ msa_status msa_sparse_attend_decode_paged(
     int local_blocks, float softmax_scale, uint16_t *out, int32_t *q2k_out, void *workspace,
     size_t workspace_bytes, void *stream) {
     if (!out) return fail(MSA_ERR_INVALID_ARG, "out must be non-NULL");
-    return decode_paged_impl(q, index_q, k_cache, v_cache, index_k_cache, index_dtype, page_table,
+    return decode_paged_impl(q, index_q, k_cache, v_cache, false, 1.f, 1.f, index_k_cache, index_dtype, page_table,
                              max_pages_per_seq, context_lens, batch, max_context_len, topk, init_blocks,
                              local_blocks, softmax_scale, out, nullptr, nullptr, q2k_out, workspace,
                              workspace_bytes, stream);
@@ -329,9 +330,24 @@ msa_status msa_sparse_attend_decode_paged_mxfp8(
     int local_blocks, float softmax_scale, uint8_t *out_q, uint8_t *out_scale, int32_t *q2k_out,
     void *workspace, size_t workspace_bytes, void *stream) {
     if (!out_q || !out_scale) return fail(MSA_ERR_INVALID_ARG, "out_q and out_scale must be non-NULL");
-    return decode_paged_impl(q, index_q, k_cache, v_cache, index_k_cache, index_dtype, page_table,
+    return decode_paged_impl(q, index_q, k_cache, v_cache, false, 1.f, 1.f, index_k_cache, index_dtype, page_table,
                              max_pages_per_seq, context_lens, batch, max_context_len, topk, init_blocks,
                              local_blocks, softmax_scale, nullptr, out_q, out_scale, q2k_out, workspace,
+                             workspace_bytes, stream);
+}
+
+msa_status msa_sparse_attend_decode_paged_fp8kv(
+    const uint16_t *q, const void *index_q, const uint8_t *k_cache, const uint8_t *v_cache, float k_scale,
+    float v_scale, const void *index_k_cache, int index_dtype, const int32_t *page_table,
+    int max_pages_per_seq, const int32_t *context_lens, int batch, int max_context_len, int topk,
+    int init_blocks, int local_blocks, float softmax_scale, uint16_t *out, int32_t *q2k_out,
+    void *workspace, size_t workspace_bytes, void *stream) {
+    if (!out) return fail(MSA_ERR_INVALID_ARG, "out must be non-NULL");
+    if (!(k_scale > 0.f) || !(v_scale > 0.f) || k_scale > 1e30f || v_scale > 1e30f)
+        return fail(MSA_ERR_INVALID_ARG, "k_scale and v_scale must be positive finite numbers");
+    return decode_paged_impl(q, index_q, k_cache, v_cache, true, k_scale, v_scale, index_k_cache, index_dtype,
+                             page_table, max_pages_per_seq, context_lens, batch, max_context_len, topk,
+                             init_blocks, local_blocks, softmax_scale, out, nullptr, nullptr, q2k_out, workspace,
                              workspace_bytes, stream);
 }
 

@@ -48,10 +48,11 @@ hipError_t launch_decode_scores(const void *iq, const void *ikc, bool fp8, const
                                 float *S, hipStream_t stream);
 hipError_t launch_decode_topk(const float *S, const int32_t *ctx, int B, int max_ctx, int nb_max, int topk,
                               int init, int local, int32_t *q2k, hipStream_t stream);
-hipError_t launch_decode_attend(const uint16_t *q, const uint16_t *kc, const uint16_t *vc,
-                                const int32_t *pt, int max_pages, const int32_t *ctx, int max_ctx, int B,
-                                const int32_t *q2k, int topk, float scale, float *partial,
-                                hipStream_t stream);
+// kc/vc: bf16 caches, or (fp8kv) E4M3FN caches dequantised as byte * k_scale / v_scale.
+hipError_t launch_decode_attend(const uint16_t *q, const void *kc, const void *vc, bool fp8kv, float k_scale,
+                                float v_scale, const int32_t *pt, int max_pages, const int32_t *ctx,
+                                int max_ctx, int B, const int32_t *q2k, int topk, float scale,
+                                float *partial, hipStream_t stream);
 // bf16 output, or (out_q != NULL) its MXFP8 encoding: E4M3 [B, 64*128] and
 // E8M0 scales [B, 64*128/32].
 hipError_t launch_decode_combine(const float *partial, int B, int topk, uint16_t *out, uint8_t *out_q,

@@ -182,6 +182,25 @@ msa_status msa_sparse_attend_decode_paged_mxfp8(
     uint8_t *out_scale, int32_t *q2k_out, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * The decode step over an FP8 main K/V cache (TensorRT-LLM config class
+ * description, fuse_qkv_index_projection: the MiniMax-M3 MSA path runs with
+ * an FP8 main KV cache).  Per-tensor scales: key j's K row is
+ * e4m3(k_cache byte) * k_scale and its V row e4m3(v_cache byte) * v_scale.
+ *
+ *  k_cache, v_cache [num_pages*128, 4, 128] E4M3FN bytes (slots past L are
+ *  never used and may hold anything, NaN included).
+ *  k_scale, v_scale > 0, finite.
+ *  Every other argument, the workspace size and the errors are those of
+ *  msa_sparse_attend_decode_paged.
+ */
+msa_status msa_sparse_attend_decode_paged_fp8kv(
+    const uint16_t *q, const void *index_q, const uint8_t *k_cache, const uint8_t *v_cache,
+    float k_scale, float v_scale, const void *index_k_cache, int index_dtype,
+    const int32_t *page_table, int max_pages_per_seq, const int32_t *context_lens, int batch,
+    int max_context_len, int topk, int init_blocks, int local_blocks, float softmax_scale,
+    uint16_t *out, int32_t *q2k_out, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Paged-cache insertion: the write that precedes decode (TensorRT-LLM config
  * class description, fuse_qkv_index_projection: the norm/RoPE/cache-insertion
  * producer; the side index-K cache parallel to the main K/V cache, same

@@ -198,3 +198,28 @@ def test_cache_insert_rejects(kw, status, needle):
 
 def test_cache_insert_of_nothing_is_a_no_op():
     assert msa.lib().msa_cache_insert(FAKE, FAKE, FAKE, FAKE, 0, 0, FAKE, FAKE, FAKE, 128, None) == 0
+
+
+def _decode_fp8kv(**kw):
+    a = dict(q=FAKE, iq=FAKE, kc=FAKE, vc=FAKE, ks=0.5, vs=0.25, ikc=FAKE, dtype=0, pt=FAKE,
+             max_pages=256, ctx=FAKE, B=32, max_ctx=32768, topk=16, init=0, local=1, scale=0.088,
+             out=FAKE, q2k=None, ws=FAKE, ws_bytes=1 << 40)
+    a.update(kw)
+    return msa.lib().msa_sparse_attend_decode_paged_fp8kv(
+        a["q"], a["iq"], a["kc"], a["vc"], a["ks"], a["vs"], a["ikc"], a["dtype"], a["pt"],
+        a["max_pages"], a["ctx"], a["B"], a["max_ctx"], a["topk"], a["init"], a["local"], a["scale"],
+        a["out"], a["q2k"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(ks=0.0), 1, "k_scale"),
+    (dict(vs=-1.0), 1, "v_scale"),
+    (dict(ks=float("nan")), 1, "k_scale"),
+    (dict(vs=float("inf")), 1, "v_scale"),
+    (dict(kc=None), 1, "non-NULL"),
+    (dict(topk=17), 2, "topk"),
+    (dict(ws_bytes=100), 3, "workspace"),
+])
+def test_decode_fp8kv_rejects(kw, status, needle):
+    assert _decode_fp8kv(**kw) == status
+    assert needle in msa.lib().msa_last_error().decode()
