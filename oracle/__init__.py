@@ -53,6 +53,10 @@ def lib():
         L.oracle_scores.argtypes = [P, P, i, P, i, P, i, i, P]
         L.oracle_select.argtypes = [P, P, i, i, i, i, i, P, P]
         L.oracle_attend.argtypes = [P, P, P, P, i, P, i, P, i, ctypes.c_double, P]
+        L.oracle_attend_backward_rows.argtypes = [P, P, P, P, P, i, P, i, P, i, ctypes.c_double,
+                                                  P, P, P]
+        L.oracle_attend_backward_keys.argtypes = [P, P, P, P, P, i, P, i, P, P, ctypes.c_double,
+                                                  P, i, P, P]
         L.oracle_decode_query_blocks.argtypes = [P, i, P]
         L.oracle_decode_scores.argtypes = [P, P, i, P, i, P, i, i, P]
         L.oracle_decode_attend.argtypes = [P, P, P, P, i, P, i, P, i, ctypes.c_double, P]
@@ -124,6 +128,54 @@ def attend(q, k, v, q2k_rows, cu, tokens, scale) -> np.ndarray:
                                len(cu) - 1, _p(tokens), len(tokens), float(scale), _p(out)),
            "attend")
     return out
+
+
+def attend_backward_rows(q, k, v, dout, q2k_full, cu, tokens, scale):
+    """Backward phase 1 for the listed tokens: (lse, D) fp64 [n,64] and dq
+    fp64 [n,64,128].  ``q2k_full`` is token-major [T,4,topk] (every token)."""
+    q, k, v, dout = (np.ascontiguousarray(a) for a in (q, k, v, dout))
+    q2k_full = np.ascontiguousarray(q2k_full, dtype=np.int32)
+    cu = np.ascontiguousarray(cu, dtype=np.int32)
+    tokens = np.ascontiguousarray(tokens, dtype=np.int32)
+    n = len(tokens)
+    lse = np.empty((n, 64), dtype=np.float64)
+    D = np.empty((n, 64), dtype=np.float64)
+    dq = np.empty((n, 64, 128), dtype=np.float64)
+    _check(lib().oracle_attend_backward_rows(_p(q), _p(k), _p(v), _p(dout), _p(q2k_full),
+                                             q2k_full.shape[2], _p(cu), len(cu) - 1, _p(tokens), n,
+                                             float(scale), _p(lse), _p(D), _p(dq)), "backward rows")
+    return lse, D, dq
+
+
+def attend_backward_keys(q, k, v, dout, q2k_full, cu, lse_full, D_full, keys, scale):
+    """Backward phase 2 for the listed keys: dk, dv fp64 [n,4,128].  ``lse_full``
+    and ``D_full`` are [T,64]; only rows of tokens that attend to the keys are read."""
+    q, k, v, dout = (np.ascontiguousarray(a) for a in (q, k, v, dout))
+    q2k_full = np.ascontiguousarray(q2k_full, dtype=np.int32)
+    cu = np.ascontiguousarray(cu, dtype=np.int32)
+    lse_full = np.ascontiguousarray(lse_full, dtype=np.float64)
+    D_full = np.ascontiguousarray(D_full, dtype=np.float64)
+    keys = np.ascontiguousarray(keys, dtype=np.int32)
+    n = len(keys)
+    dk = np.empty((n, 4, 128), dtype=np.float64)
+    dv = np.empty((n, 4, 128), dtype=np.float64)
+    _check(lib().oracle_attend_backward_keys(_p(q), _p(k), _p(v), _p(dout), _p(q2k_full),
+                                             q2k_full.shape[2], _p(cu), len(cu) - 1, _p(lse_full),
+                                             _p(D_full), float(scale), _p(keys), n, _p(dk), _p(dv)),
+           "backward keys")
+    return dk, dv
+
+
+def attend_backward(q, k, v, dout, q2k_full, cu, scale, keys=None):
+    """Whole backward over every token: dict(lse, D [T,64], dq [T,64,128],
+    dk, dv [T,4,128] (or [len(keys),4,128] for the listed keys))."""
+    T = int(np.asarray(cu)[-1])
+    tokens = np.arange(T, dtype=np.int32)
+    lse, D, dq = attend_backward_rows(q, k, v, dout, q2k_full, cu, tokens, scale)
+    if keys is None:
+        keys = tokens
+    dk, dv = attend_backward_keys(q, k, v, dout, q2k_full, cu, lse, D, keys, scale)
+    return dict(lse=lse, D=D, dq=dq, dk=dk, dv=dv)
 
 
 def prefill(w, tokens=None, q2k_override=None):

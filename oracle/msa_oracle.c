@@ -25,7 +25,9 @@
  *          [4, tokens, 16] document-local ids padded with -1), the document-map
  *          classmethod (0 = padding, each document one contiguous run),
  *          MSAMicrobatch.build (causal only), sparse_attention (bf16 q
- *          [tokens,64,128], k/v [tokens,4,128] -> bf16 out [tokens,64,128]).
+ *          [tokens,64,128], k/v [tokens,4,128] -> bf16 out [tokens,64,128]),
+ *          _SparseAttention.backward (grad_out -> dq, dk, dv; no gradient
+ *          for the selection).
  *
  * Readings where the pages leave a step open (each also listed in the design
  * notes): raw dot products for scores (no 1/sqrt(d)); keys j <= t only, in
@@ -286,6 +288,154 @@ int oracle_attend(const uint16_t *q, const uint16_t *k, const uint16_t *v,
         free((void *)vrows);
         free(z);
     }
+    return bad ? 2 : 0;
+}
+
+/* ---- step 3, backward: gradients of the sparse attention ------------------ */
+
+/* The selection is a hard top-k and carries no gradient ([MSA] select_blocks
+ * runs under no_grad); the backward differentiates step 3 alone for a fixed
+ * q2k ([MSA] _SparseAttention.backward: bf16 grad_out [tokens,64,128] ->
+ * dq [tokens,64,128], dk and dv [tokens,4,128]).  With K(t,g) the key set of
+ * oracle_attend, z_tj = scale q_th.k_j, lse_th = log sum_{j in K} e^z_tj,
+ * P_tj = e^(z_tj - lse_th) and dO = d(loss)/d(out):
+ *   dP_tj = dO_th . v_j        D_th = sum_j P_tj dP_tj
+ *   dS_tj = P_tj (dP_tj - D_th)
+ *   dq_th = scale sum_{j in K(t,g)} dS_tj k_j
+ *   dk_jg = scale sum over (t, h in group g) with j in K(t,g) of dS_tj q_th
+ *   dv_jg =       sum over the same rows of P_tj dO_th
+ * q2k is token-major [T][4][topk] here (row of token t, KV head g). */
+
+/* Whether key j (document start `start`) is in K(t,g): j <= t, same
+ * document, block (j - start) div 128 listed in the row. */
+static int key_selected(const int32_t *row, int topk, int start, int j, int t) {
+    if (j > t || j < start) return 0;
+    int blk = (j - start) / ORC_BS;
+    for (int s = 0; s < topk; ++s)
+        if (row[s] == blk) return 1;
+    return 0;
+}
+
+static double dot_bf16(const uint16_t *a, const uint16_t *b) {
+    double acc = 0.0;
+    for (int x = 0; x < ORC_D; ++x) acc += bf16_value(a[x]) * bf16_value(b[x]);
+    return acc;
+}
+
+/* Phase 1, per query row of the listed tokens: lse, D and dq.  A row with an
+ * empty key set has lse = -inf, D = 0, dq = 0. */
+int oracle_attend_backward_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                const uint16_t *dout, const int32_t *q2k /* [T][4][topk] */,
+                                int topk, const int32_t *cu, int ndocs, const int32_t *tokens,
+                                int ntok, double scale, double *lse /* [ntok][64] */,
+                                double *D /* [ntok][64] */, double *dq /* [ntok][64][128] */) {
+    if (check_cu(cu, ndocs) || topk < 1) return 1;
+    int bad = 0;
+#pragma omp parallel reduction(| : bad)
+    {
+        int *keys = NULL;
+        double *z = NULL, *dp = NULL;
+        size_t cap = 0;
+#pragma omp for schedule(dynamic, 1)
+        for (int i = 0; i < ntok; ++i) {
+            int t = tokens[i];
+            int d = doc_of(cu, ndocs, t);
+            if (d < 0) { bad |= 1; continue; }
+            int start = cu[d];
+            size_t need = (size_t)(t - start + 1);
+            if (need > cap) {
+                cap = need;
+                keys = (int *)realloc(keys, cap * sizeof *keys);
+                z = (double *)realloc(z, cap * sizeof *z);
+                dp = (double *)realloc(dp, cap * sizeof *dp);
+            }
+            for (int g = 0; g < ORC_KVH; ++g) {
+                const int32_t *row = q2k + ((size_t)t * ORC_KVH + g) * topk;
+                int nk = 0;
+                for (int j = start; j <= t; ++j)
+                    if (key_selected(row, topk, start, j, t)) keys[nk++] = j;
+                for (int hh = 0; hh < ORC_GROUP; ++hh) {
+                    int h = g * ORC_GROUP + hh;
+                    const uint16_t *qr = q + ((size_t)t * ORC_QH + h) * ORC_D;
+                    const uint16_t *dor = dout + ((size_t)t * ORC_QH + h) * ORC_D;
+                    double *dqr = dq + ((size_t)i * ORC_QH + h) * ORC_D;
+                    for (int x = 0; x < ORC_D; ++x) dqr[x] = 0.0;
+                    if (nk == 0) {
+                        lse[(size_t)i * ORC_QH + h] = -INFINITY;
+                        D[(size_t)i * ORC_QH + h] = 0.0;
+                        continue;
+                    }
+                    double zmax = -INFINITY;
+                    for (int a = 0; a < nk; ++a) {
+                        const uint16_t *kr = k + ((size_t)keys[a] * ORC_KVH + g) * ORC_D;
+                        z[a] = scale * dot_bf16(qr, kr);
+                        if (z[a] > zmax) zmax = z[a];
+                    }
+                    double sum = 0.0;
+                    for (int a = 0; a < nk; ++a) sum += exp(z[a] - zmax);
+                    double l = zmax + log(sum);
+                    double Dth = 0.0;
+                    for (int a = 0; a < nk; ++a) {
+                        const uint16_t *vr = v + ((size_t)keys[a] * ORC_KVH + g) * ORC_D;
+                        dp[a] = dot_bf16(dor, vr);
+                        Dth += exp(z[a] - l) * dp[a];
+                    }
+                    for (int a = 0; a < nk; ++a) {
+                        double ds = exp(z[a] - l) * (dp[a] - Dth);
+                        const uint16_t *kr = k + ((size_t)keys[a] * ORC_KVH + g) * ORC_D;
+                        for (int x = 0; x < ORC_D; ++x) dqr[x] += scale * ds * bf16_value(kr[x]);
+                    }
+                    lse[(size_t)i * ORC_QH + h] = l;
+                    D[(size_t)i * ORC_QH + h] = Dth;
+                }
+            }
+        }
+        free(keys);
+        free(z);
+        free(dp);
+    }
+    return bad ? 2 : 0;
+}
+
+/* Phase 2, per listed key j and KV head g: dk and dv summed over the query
+ * rows whose key set holds j (tokens t >= j of j's document whose row lists
+ * j's block).  lse and D are phase 1's values indexed by token [T][64]; only
+ * the rows of those tokens are read. */
+int oracle_attend_backward_keys(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                const uint16_t *dout, const int32_t *q2k /* [T][4][topk] */,
+                                int topk, const int32_t *cu, int ndocs, const double *lse,
+                                const double *D, double scale, const int32_t *keys, int nkeys,
+                                double *dk /* [nkeys][4][128] */, double *dv /* [nkeys][4][128] */) {
+    if (check_cu(cu, ndocs) || topk < 1) return 1;
+    int bad = 0;
+#pragma omp parallel for collapse(2) schedule(dynamic, 1) reduction(| : bad)
+    for (int i = 0; i < nkeys; ++i)
+        for (int g = 0; g < ORC_KVH; ++g) {
+            int j = keys[i];
+            double *dkr = dk + ((size_t)i * ORC_KVH + g) * ORC_D;
+            double *dvr = dv + ((size_t)i * ORC_KVH + g) * ORC_D;
+            for (int x = 0; x < ORC_D; ++x) dkr[x] = dvr[x] = 0.0;
+            int d = doc_of(cu, ndocs, j);
+            if (d < 0) { bad |= 1; continue; }
+            int start = cu[d], end = cu[d + 1];
+            const uint16_t *kr = k + ((size_t)j * ORC_KVH + g) * ORC_D;
+            const uint16_t *vr = v + ((size_t)j * ORC_KVH + g) * ORC_D;
+            for (int t = j; t < end; ++t) {
+                const int32_t *row = q2k + ((size_t)t * ORC_KVH + g) * topk;
+                if (!key_selected(row, topk, start, j, t)) continue;
+                for (int hh = 0; hh < ORC_GROUP; ++hh) {
+                    int h = g * ORC_GROUP + hh;
+                    const uint16_t *qr = q + ((size_t)t * ORC_QH + h) * ORC_D;
+                    const uint16_t *dor = dout + ((size_t)t * ORC_QH + h) * ORC_D;
+                    double p = exp(scale * dot_bf16(qr, kr) - lse[(size_t)t * ORC_QH + h]);
+                    double ds = p * (dot_bf16(dor, vr) - D[(size_t)t * ORC_QH + h]);
+                    for (int x = 0; x < ORC_D; ++x) {
+                        dkr[x] += scale * ds * bf16_value(qr[x]);
+                        dvr[x] += p * bf16_value(dor[x]);
+                    }
+                }
+            }
+        }
     return bad ? 2 : 0;
 }
 

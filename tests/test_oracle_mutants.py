@@ -13,6 +13,7 @@ import subprocess
 import pytest
 
 import oracle
+import test_oracle_backward as bwd_pins
 import test_oracle_pins as pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "msa_oracle.c")
@@ -42,7 +43,32 @@ MUTANTS = {
                       "return (size_t)j + 0 * (size_t)pt[0] * (size_t)max_pages * (size_t)r;"),
     # E4M3 exponent bias off by one
     "e4m3_bias": ("ldexp(8.0 + m, e - 10)", "ldexp(8.0 + m, e - 11)"),
+    # backward: softmax scale dropped from dq
+    "bwd_dq_no_scale": ("dqr[x] += scale * ds * bf16_value(kr[x]);", "dqr[x] += ds * bf16_value(kr[x]);"),
+    # backward: the D term dropped from dS (rows, then keys)
+    "bwd_rows_no_D": ("double ds = exp(z[a] - l) * (dp[a] - Dth);", "double ds = exp(z[a] - l) * dp[a];"),
+    "bwd_keys_no_D": ("double ds = p * (dot_bf16(dor, vr) - D[(size_t)t * ORC_QH + h]);",
+                      "double ds = p * dot_bf16(dor, vr);"),
+    # backward: dv weighted by dS instead of P
+    "bwd_dv_uses_ds": ("dvr[x] += p * bf16_value(dor[x]);", "dvr[x] += ds * bf16_value(dor[x]);"),
+    # backward: dk built from the key instead of the query (wrong operand)
+    "bwd_dk_wrong_operand": ("dkr[x] += scale * ds * bf16_value(qr[x]);",
+                             "dkr[x] += scale * ds * bf16_value(kr[x]);"),
+    # backward: log-sum-exp without its max shift
+    "bwd_lse_no_max": ("double l = zmax + log(sum);", "double l = log(sum);"),
+    # backward: key t excluded from its own row
+    "bwd_strict_causal": ("if (j > t || j < start) return 0;", "if (j >= t || j < start) return 0;"),
+    # backward: query head -> KV head interleaved in the per-key phase
+    "bwd_keys_gqa_interleaved": (
+        "int h = g * ORC_GROUP + hh;\n                    const uint16_t *qr = q + ((size_t)t * ORC_QH + h) * ORC_D;\n"
+        "                    const uint16_t *dor = dout + ((size_t)t * ORC_QH + h) * ORC_D;\n                    double p",
+        "int h = hh * ORC_KVH + g;\n                    const uint16_t *qr = q + ((size_t)t * ORC_QH + h) * ORC_D;\n"
+        "                    const uint16_t *dor = dout + ((size_t)t * ORC_QH + h) * ORC_D;\n                    double p"),
 }
+
+# pins of the backward oracle (tests/test_oracle_backward.py), run without arguments
+BACKWARD_PINS = ["test_dense_reduction_matches_autograd", "test_sparse_rows_match_autograd_and_forward",
+                 "test_invariants_and_single_key_row"]
 
 PIN_TESTS = [
     ("test_e4m3_decoder_matches_torch_on_all_codes", {}),
@@ -86,13 +112,15 @@ def test_mutant_fails_a_pin(name, tmp_path, monkeypatch):
     # copy argtypes/restypes of every exported oracle function
     for sym in ("oracle_bf16_value", "oracle_e4m3_value", "oracle_query_blocks", "oracle_scores",
                 "oracle_select", "oracle_attend", "oracle_decode_query_blocks",
-                "oracle_decode_scores", "oracle_decode_attend", "oracle_num_threads"):
+                "oracle_decode_scores", "oracle_decode_attend", "oracle_num_threads",
+                "oracle_attend_backward_rows", "oracle_attend_backward_keys"):
         f_real, f_mut = getattr(real, sym), getattr(mutant, sym)
         f_mut.argtypes = f_real.argtypes
         f_mut.restype = f_real.restype
     monkeypatch.setattr(oracle, "_lib", mutant)
     checks = [(n, (lambda n=n, kw=kw: getattr(pins, n)(oracle, **kw))) for n, kw in PIN_TESTS]
     checks.insert(1, ("test_selection_golden", lambda: _golden_all(oracle)))
+    checks += [(n, getattr(bwd_pins, n)) for n in BACKWARD_PINS]
     caught_by = None
     for test_name, run in checks:
         try:

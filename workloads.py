@@ -121,6 +121,12 @@ def normal_bf16(seed_seq, shape) -> np.ndarray:
     return bf16_bits(normal_f32(seed_seq, shape))
 
 
+def grad_out(seed: int, T: int) -> np.ndarray:
+    """Incoming gradient of the attention output: bf16 bits [T,64,128],
+    standard normal (a stand-in for d(loss)/d(out) of a training step)."""
+    return normal_bf16(np.random.SeedSequence([seed, 0x6472]), (T, 64, 128))
+
+
 def rms_normalise(z: np.ndarray, eps: float = 1e-6) -> np.ndarray:
     """z / sqrt(mean(z^2) + eps) along the last axis (index vectors arrive
     post-norm; this stands in for the model's norm)."""
