@@ -33,6 +33,7 @@ import torch
 
 __all__ = [
     "select_blocks", "sparse_attend_prefill", "sparse_attend_decode_paged",
+    "sparse_attend_prefill_backward", "prefill_backward_workspace_bytes",
     "sparse_attend_decode_paged_mxfp8", "sparse_attend_decode_paged_fp8kv", "mxfp8_quantize",
     "cache_insert",
     "unsupported_reason", "library_path", "MsaError",
@@ -81,6 +82,13 @@ def lib():
         L.msa_select_blocks.argtypes = [P, P, i, P, i, i, i, i, i, i, P, P, P, sz, P]
         L.msa_sparse_attend_prefill.restype = i
         L.msa_sparse_attend_prefill.argtypes = [P, P, P, P, i, P, i, i, i, f, P, P, sz, P]
+        L.msa_sparse_attend_prefill_lse.restype = i
+        L.msa_sparse_attend_prefill_lse.argtypes = [P, P, P, P, i, P, i, i, i, f, P, P, P, sz, P]
+        L.msa_prefill_backward_workspace_bytes.restype = sz
+        L.msa_prefill_backward_workspace_bytes.argtypes = [i, i, i, i]
+        L.msa_sparse_attend_prefill_backward.restype = i
+        L.msa_sparse_attend_prefill_backward.argtypes = [P, P, P, P, P, P, P, i, P, i, i, i, f, P, P, P,
+                                                         P, sz, P]
         L.msa_set_timing_events.restype = None
         L.msa_set_timing_events.argtypes = [P, i]
         L.msa_timing_kernel_count.restype = i
@@ -122,6 +130,10 @@ def select_blocks_workspace_bytes(total_tokens, num_docs, max_seqlen) -> int:
 
 def prefill_workspace_bytes(total_tokens, num_docs, max_seqlen) -> int:
     return int(lib().msa_prefill_workspace_bytes(total_tokens, num_docs, max_seqlen))
+
+
+def prefill_backward_workspace_bytes(total_tokens, num_docs, max_seqlen, topk) -> int:
+    return int(lib().msa_prefill_backward_workspace_bytes(total_tokens, num_docs, max_seqlen, topk))
 
 
 def decode_workspace_bytes(batch, max_context_len, topk) -> int:
@@ -192,9 +204,7 @@ def select_blocks(index_q, index_k, cu_seqlens, max_seqlen, topk=16, init_blocks
     return (q2k, S) if scores else q2k
 
 
-def sparse_attend_prefill(q, k, v, q2k, cu_seqlens, max_seqlen, softmax_scale=None,
-                          workspace=None):
-    """Sparse GQA attention over the selected blocks -> bf16 out [T,64,128]."""
+def _check_attention_args(q, k, v, q2k, cu_seqlens):
     device = q.device
     T = int(q.shape[0])
     _dev_tensor("q", q, (T, 64, 128), (torch.bfloat16,))
@@ -204,18 +214,55 @@ def sparse_attend_prefill(q, k, v, q2k, cu_seqlens, max_seqlen, softmax_scale=No
         raise ValueError(f"q2k must have shape [4, {T}, topk] (got {tuple(q2k.shape)})")
     _dev_tensor("q2k", q2k, None, (torch.int32,), device)
     _dev_tensor("cu_seqlens", cu_seqlens, None, (torch.int32,), device)
-    ndocs = int(cu_seqlens.numel()) - 1
+    return device, T, int(cu_seqlens.numel()) - 1
+
+
+def sparse_attend_prefill(q, k, v, q2k, cu_seqlens, max_seqlen, softmax_scale=None,
+                          workspace=None, return_lse=False):
+    """Sparse GQA attention over the selected blocks -> bf16 out [T,64,128]
+    (with ``return_lse``: (out, fp32 lse [T,64]) for the backward)."""
+    device, T, ndocs = _check_attention_args(q, k, v, q2k, cu_seqlens)
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(128.0)
     out = torch.empty((T, 64, 128), dtype=torch.bfloat16, device=device)
     need = prefill_workspace_bytes(T, max(ndocs, 1), int(max_seqlen)) if ndocs >= 1 else 0
     if workspace is None:
         workspace = _workspace(need, device)
-    _check(lib().msa_sparse_attend_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(q2k), int(q2k.shape[2]),
-                                           _ptr(cu_seqlens), ndocs, T, int(max_seqlen),
-                                           float(softmax_scale), _ptr(out), _ptr(workspace),
-                                           workspace.numel(), _stream(device)))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(q2k), int(q2k.shape[2]), _ptr(cu_seqlens), ndocs, T,
+            int(max_seqlen), float(softmax_scale), _ptr(out))
+    tail = (_ptr(workspace), workspace.numel(), _stream(device))
+    if return_lse:
+        lse = torch.empty((T, 64), dtype=torch.float32, device=device)
+        _check(lib().msa_sparse_attend_prefill_lse(*args, _ptr(lse), *tail))
+        return out, lse
+    _check(lib().msa_sparse_attend_prefill(*args, *tail))
     return out
+
+
+def sparse_attend_prefill_backward(q, k, v, out, lse, dout, q2k, cu_seqlens, max_seqlen,
+                                   softmax_scale=None, workspace=None):
+    """Gradients of the sparse prefill attention for a fixed q2k -> (dq [T,64,128],
+    dk [T,4,128], dv [T,4,128]) bf16.  ``out`` and ``lse`` come from
+    ``sparse_attend_prefill(..., return_lse=True)``; ``dout`` is d(loss)/d(out)."""
+    device, T, ndocs = _check_attention_args(q, k, v, q2k, cu_seqlens)
+    _dev_tensor("out", out, (T, 64, 128), (torch.bfloat16,), device)
+    _dev_tensor("lse", lse, (T, 64), (torch.float32,), device)
+    _dev_tensor("dout", dout, (T, 64, 128), (torch.bfloat16,), device)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(128.0)
+    topk = int(q2k.shape[2])
+    dq = torch.empty((T, 64, 128), dtype=torch.bfloat16, device=device)
+    dk = torch.empty((T, 4, 128), dtype=torch.bfloat16, device=device)
+    dv = torch.empty((T, 4, 128), dtype=torch.bfloat16, device=device)
+    need = (prefill_backward_workspace_bytes(T, max(ndocs, 1), int(max_seqlen), topk)
+            if ndocs >= 1 else 0)
+    if workspace is None:
+        workspace = _workspace(need, device)
+    _check(lib().msa_sparse_attend_prefill_backward(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), _ptr(q2k), topk,
+        _ptr(cu_seqlens), ndocs, T, int(max_seqlen), float(softmax_scale), _ptr(dq), _ptr(dk),
+        _ptr(dv), _ptr(workspace), workspace.numel(), _stream(device)))
+    return dq, dk, dv
 
 
 def sparse_attend_decode_paged(q, index_q, k_cache, v_cache, index_k_cache, page_table,

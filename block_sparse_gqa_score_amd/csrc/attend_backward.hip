@@ -1,0 +1,681 @@
+// Backward of the sparse GQA prefill attention for a fixed selection.
+//
+// Method (NeMo AutoModel minimax_m3_vl.msa, _SparseAttention.backward: bf16
+// grad_out [tokens,64,128] -> dq [tokens,64,128], dk and dv [tokens,4,128];
+// the selection is a hard top-k and carries no gradient).  With P the
+// forward's softmax rows, rebuilt from the saved log-sum-exp, dP = dO.v,
+// D = rowsum(dO * O) and dS = P (dP - D), over each row's selected keys:
+//   dq = scale dS K,   dk = scale dS^T Q,   dv = P^T dO.
+//
+// Kernels:
+//   bwd_rowdot_kernel   - D[t][h] = sum_d dO * O in fp32.
+//   bwd_list_kernel     - inverse of q2k: for every (KV head g, document
+//       block) the tokens whose row selects the block, ascending.  A count
+//       pass, a scan (bwd_scan_kernel, also of the chunk counts) and a fill
+//       pass at the scanned offsets; no atomics, so the lists, and every sum
+//       taken over them, are the same on every run.
+//   bwd_dq_kernel       - query-major, on the forward's tile / union-block /
+//       LDS-ring structure with K rows and V rows as the 32-key units: per
+//       unit S^T = K Q^T, dP^T = V dO^T, P^T and dS^T in registers, then
+//       dQ^T += K^T dS^T with K^T taken by transposing LDS reads.
+//   bwd_dkdv_kernel     - key-major: one workgroup per chunk of kBwdChunk
+//       tokens of one block's list; 4 waves x 32 keys hold their K and V rows
+//       as MFMA operands; per step of 4 tokens (64 query rows of the KV
+//       group, staged in LDS) S = Q K^T, dP = dO V^T, dS, then
+//       dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T taken by
+//       transposing LDS reads; one fp32 partial (dK, dV) per chunk.
+//   bwd_reduce_kernel   - per block, its chunk partials summed in chunk order
+//       into bf16 dk, dv (zero for keys that no query attends to).
+#include "attend_common.hpp"
+
+namespace msa {
+
+namespace {
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kRowB = kDim * 2;  // bytes of one bf16 row of 128
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// Transposing LDS read of a 4 x 16 bf16 block: lane j of each 16-lane group
+// receives column j of the 4 rows its group addressed (lane i of the group
+// supplies row i/4, columns 4(i%4)..+3).
+__device__ __forceinline__ i16x4 read_tr(const uint8_t *p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p);
+}
+
+// Two transposing reads (rows e of the first, then of the second) as one
+// 8-element bf16 MFMA operand.
+__device__ __forceinline__ bf16x8 join_tr(const i16x4 &a, const i16x4 &b) {
+    const i16x8 x = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return __builtin_bit_cast(bf16x8, x);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// D = rowsum(dO * O)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void bwd_rowdot_kernel(const uint16_t *__restrict__ o,
+                                                         const uint16_t *__restrict__ dout,
+                                                         int64_t rows, float *__restrict__ Dsum) {
+    const int64_t row = int64_t(blockIdx.x) * 16 + (threadIdx.x >> 4);
+    const int c = threadIdx.x & 15;
+    float acc = 0.f;
+    if (row < rows) {
+        const u32x4 a = *(const u32x4 *)(o + row * kDim + 8 * c);
+        const u32x4 b = *(const u32x4 *)(dout + row * kDim + 8 * c);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc += bf16_lo(a[i]) * bf16_lo(b[i]) + bf16_hi(a[i]) * bf16_hi(b[i]);
+    }
+    acc += __shfl_xor(acc, 1);
+    acc += __shfl_xor(acc, 2);
+    acc += __shfl_xor(acc, 4);
+    acc += __shfl_xor(acc, 8);
+    if (c == 0 && row < rows) Dsum[row] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// Inverse of q2k: per (KV head, document block) the selecting tokens
+// ---------------------------------------------------------------------------
+// Workgroup (Bg, g): document block Bg (blocks of all documents numbered by
+// blk_off), KV head g; list index li = g * nb_max + Bg.  Token at document
+// position p >= 128b selects block b when its row lists b (a token before
+// the block cannot: its candidates stop at its own block).
+template <bool kFill>
+__global__ __launch_bounds__(256) void bwd_list_kernel(const int32_t *__restrict__ q2k, int topk, int T,
+                                                       const DocSpan *__restrict__ docs,
+                                                       const int32_t *__restrict__ blk_off, int ndocs,
+                                                       int nb_max, int32_t *__restrict__ cnt,
+                                                       const int32_t *__restrict__ list_off,
+                                                       int32_t *__restrict__ lists) {
+    __shared__ int s_w[4];
+    const int Bg = blockIdx.x, g = blockIdx.y;
+    const int li = g * nb_max + Bg;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (Bg >= blk_off[ndocs]) {
+        if (!kFill && tid == 0) cnt[li] = 0;
+        return;
+    }
+    const int d = prefix_doc(blk_off, ndocs, Bg);
+    const DocSpan doc = docs[d];
+    const int b = Bg - blk_off[d];
+    const int32_t *rows = q2k + size_t(g) * T * topk;
+    int base = kFill ? list_off[li] : 0;
+    for (int p0 = b * kBlock; p0 < doc.len; p0 += 256) {
+        const int p = p0 + tid;
+        bool hit = false;
+        if (p < doc.len) {
+            const int32_t *r = rows + size_t(doc.start + p) * topk;
+            for (int s = 0; s < topk; ++s) hit |= r[s] == b;
+        }
+        const uint64_t m = __ballot(hit);
+        if (lane == 0) s_w[wave] = __popcll(m);
+        __syncthreads();
+        int before = 0, all = 0;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const int x = s_w[w];
+            before += w < wave ? x : 0;
+            all += x;
+        }
+        if (kFill && hit) lists[base + before + __popcll(m & ((1ull << lane) - 1ull))] = doc.start + p;
+        base += all;
+        __syncthreads();  // s_w is rewritten next round
+    }
+    if (!kFill && tid == 0) cnt[li] = base;
+}
+
+// Exclusive scans of n list lengths: list_off[0..n] and chunk_off[0..n]
+// (kBwdChunk tokens per chunk).  One workgroup.
+__global__ __launch_bounds__(1024) void bwd_scan_kernel(const int32_t *__restrict__ cnt, int n,
+                                                        int32_t *__restrict__ list_off,
+                                                        int32_t *__restrict__ chunk_off) {
+    __shared__ int wsum_a[16], wsum_b[16];
+    __shared__ int carry_a, carry_b;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (tid == 0) {
+        carry_a = carry_b = 0;
+        list_off[0] = chunk_off[0] = 0;
+    }
+    __syncthreads();
+    for (int base = 0; base < n; base += 1024) {
+        const int i = base + tid;
+        int a = i < n ? cnt[i] : 0;
+        int c = (a + kBwdChunk - 1) / kBwdChunk;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int ya = __shfl_up(a, o), yc = __shfl_up(c, o);
+            if (lane >= o) { a += ya; c += yc; }
+        }
+        if (lane == 63) { wsum_a[wave] = a; wsum_b[wave] = c; }
+        __syncthreads();
+        int pa = carry_a, pc = carry_b;
+        for (int w = 0; w < wave; ++w) { pa += wsum_a[w]; pc += wsum_b[w]; }
+        if (i < n) {
+            list_off[i + 1] = pa + a;
+            chunk_off[i + 1] = pc + c;
+        }
+        __syncthreads();
+        if (tid == 1023) { carry_a = pa + a; carry_b = pc + c; }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dQ (query-major)
+// ---------------------------------------------------------------------------
+namespace {
+constexpr int kQTok = kAttnTile;                      // 16 tokens per workgroup
+constexpr int kQWaves = kQTok / 2;                    // 8 waves, 2 tokens each
+constexpr int kQThreads = 64 * kQWaves;               // 512
+constexpr int kUnitsPerBlock = kBlock / kAttnUnit;    // 4
+constexpr int kHalfBytes = kAttnUnit * kRowB;         // 8 KiB: 32 K rows (or V rows)
+constexpr int kQUnitBytes = 2 * kHalfBytes;           // K rows, then V rows
+constexpr int kQRing = 2 * kUnitsPerBlock + 1;        // 9 slots (144 KiB)
+static_assert(kQRing * kQUnitBytes <= 144 * 1024, "ring must leave LDS for the union tables");
+
+// Row r of a 32-row half, 16-byte chunk c (d 8c..8c+7), sits at chunk
+// position c ^ swz32(r).  The 16 rows one plain operand read touches,
+// 8a + 4mt + e (a, e < 4), map to 16 distinct positions, and the 4 rows
+// 8a + 4h + e (e < 4) of one transposing read to 4 distinct position pairs.
+__device__ __forceinline__ int swz32(int r) { return ((r & 3) << 2) | ((r >> 3) & 3); }
+
+struct DqState {
+    bf16x8 qb[2][4];   // Q^T operand of each token (column n = head n)
+    bf16x8 dob[2][4];  // dO^T operand
+    f32x4 acc[2][8];   // dQ^T: lane holds d = 16dt + 4grp + i of head n
+    float lse2[2];     // log2-domain log-sum-exp of head n
+    float dsum[2];     // D of head n
+};
+
+// One union block for one wave (kA0 / kA1: which tokens compute; kDiag:
+// the query's own block, nq <= 4 units, causal mask, tokens from act_rt).
+template <bool kA0, bool kA1, bool kDiag>
+__device__ __forceinline__ void dq_block(DqState &st, const uint8_t *smem, int ustart, int nq,
+                                         const int (&k_row_off)[2], int nsw, int grp,
+                                         const int (&tr_row)[2], const int (&tr_x)[2], int tr_lo,
+                                         int keyb, const bool (&act_rt)[2], const int (&my_p)[2],
+                                         float scale_log2) {
+    const bool act[2] = {kDiag ? act_rt[0] : kA0, kDiag ? act_rt[1] : kA1};
+#pragma unroll
+    for (int q = 0; q < kUnitsPerBlock; ++q) {
+        if (kDiag && q >= nq) break;
+        const uint8_t *Ku = smem + ((ustart + q) % kQRing) * kQUnitBytes;
+        const uint8_t *Vu = Ku + kHalfBytes;
+        bf16x8 ka[4][2], va[4][2];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                const int off = k_row_off[mt] + (((4 * ks + grp) ^ nsw) << 4);
+                ka[ks][mt] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(Ku + off));
+                va[ks][mt] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(Vu + off));
+            }
+        // S^T and dP^T for this unit; lane (n, grp) holds keys 8grp + 4mt + i
+        bf16x8 dsb[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            if (!act[t]) continue;
+            f32x4 s[2] = {f32x4{}, f32x4{}}, dp[2] = {f32x4{}, f32x4{}};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt) {
+                    s[mt] = mfma_16x16x32(ka[ks][mt], st.qb[t][ks], s[mt]);
+                    dp[mt] = mfma_16x16x32(va[ks][mt], st.dob[t][ks], dp[mt]);
+                }
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const bool ok = !kDiag || keyb + kAttnUnit * q + 4 * mt + i <= my_p[t];
+                    const float p = ok ? __builtin_amdgcn_exp2f(s[mt][i] * scale_log2 - st.lse2[t]) : 0.f;
+                    dsb[t][4 * mt + i] = (__bf16)(p * (dp[mt][i] - st.dsum[t]));
+                }
+        }
+        // dQ^T += K^T dS^T: K^T rows d = 16dt + j, keys 8grp + e from two
+        // transposing reads of K rows 8grp..8grp+3 and 8grp+4..8grp+7
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+            const bf16x8 kt = join_tr(read_tr(Ku + tr_row[0] + (((2 * dt) ^ tr_x[0]) << 4) + tr_lo),
+                                      read_tr(Ku + tr_row[1] + (((2 * dt) ^ tr_x[1]) << 4) + tr_lo));
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+                if (act[t]) st.acc[t][dt] = mfma_16x16x32(kt, dsb[t], st.acc[t][dt]);
+        }
+    }
+}
+}  // namespace
+
+__global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+    const uint16_t *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ Dsum,
+    const int32_t *__restrict__ q2k, int topk, const DocSpan *__restrict__ docs,
+    const int32_t *__restrict__ tile_off, int ndocs, int T, float scale, float scale_log2,
+    uint16_t *__restrict__ dq) {
+    extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+    constexpr int kEntries = kQTok * kMaxTopk;
+    static_assert(kQThreads >= kEntries, "one thread per (token, slot) pair");
+    __shared__ int s_id[kEntries];
+    __shared__ int s_first[kEntries];
+    __shared__ int s_mask[kEntries];
+    __shared__ int s_ublk[kEntries];
+    __shared__ int s_umask[kEntries];
+    __shared__ int s_nu;
+
+    // XCD-aware order, as in the forward: XCD x serves KV head x/2.
+    const int bid = blockIdx.x;
+    const int xcd = bid & 7, xslot = bid >> 3;
+    const int g = xcd >> 1;
+    const int tile = 16 * (xslot >> 3) + 8 * (xcd & 1) + (xslot & 7);
+    if (tile >= tile_off[ndocs]) return;
+    const int d = prefix_doc(tile_off, ndocs, tile);
+    const int nt_doc = tile_off[d + 1] - tile_off[d];
+    const int local_tile = nt_doc - 1 - (tile - tile_off[d]);
+    const DocSpan doc = docs[d];
+    const int p0 = local_tile * kQTok;
+    const int c = p0 / kBlock;
+    const int ntok = min(kQTok, doc.len - p0);
+    const int p_last = p0 + ntok - 1;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 15, grp = lane >> 4;
+    const int head = g * kGroup + n;
+
+    int my_p[2];
+    bool tok_ok[2];
+    DqState st;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        my_p[t] = p0 + 2 * wave + t;
+        tok_ok[t] = 2 * wave + t < ntok;
+        const size_t row = size_t(doc.start + (tok_ok[t] ? my_p[t] : p0)) * kHeads + head;
+        const uint16_t *qs = q + row * kDim, *ds = dout + row * kDim;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            st.qb[t][ks] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qs + 32 * ks + 8 * grp));
+            st.dob[t][ks] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(ds + 32 * ks + 8 * grp));
+        }
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) st.acc[t][dt] = f32x4{};
+        st.lse2[t] = lse[row] * kLog2e;
+        st.dsum[t] = Dsum[row];
+    }
+
+    const int nu = tile_union(q2k, T, topk, g, doc.start + p0, ntok, c, tid, s_id, s_first, s_mask,
+                              s_ublk, s_umask, &s_nu);
+    const int last_units =
+        (nu > 0 && s_ublk[nu - 1] == c) ? (p_last - c * kBlock) / kAttnUnit + 1 : kUnitsPerBlock;
+    const int nunits = nu > 0 ? kUnitsPerBlock * (nu - 1) + last_units : 0;
+
+    // Unit copies: copy i < 8 fills K rows 4i..4i+3, copy i >= 8 V rows
+    // 4(i-8)..+3 (lane l: row 4i' + l/16, position l%16, i.e. chunk
+    // (l%16) ^ swz32(row)).  Rows past p_last re-read row p_last.
+    auto issue_copy = [&](int vu, int ub, int i) {
+        const int qq = vu & 3;
+        uint8_t *slot = smem + (vu % kQRing) * kQUnitBytes;
+        const int ii = i & 7;
+        const int r = 4 * ii + (lane >> 4);
+        const int ch = (lane & 15) ^ swz32(r);
+        const int kp = min(ub * kBlock + qq * kAttnUnit + r, p_last);
+        const uint16_t *src = (i < 8 ? k : v) + (size_t(doc.start + kp) * kKvHeads + g) * kDim + 8 * ch;
+        copy_to_lds(src, slot + (i < 8 ? 0 : kHalfBytes) + ii * 1024);
+    };
+    auto issue_unit = [&](int vu) {
+        const int ub = __builtin_amdgcn_readfirstlane(s_ublk[vu >> 2]);
+        issue_copy(vu, ub, 2 * wave);
+        issue_copy(vu, ub, 2 * wave + 1);
+    };
+
+    // Lane-constant LDS offsets.  Plain reads: M-tile mt row n is key
+    // 8(n/4) + 4mt + n%4, whose swz32 is nsw.  Transposing reads h = 0, 1:
+    // this lane supplies row 8grp + 4h + n/4, columns 16dt + 4(n%4)..+3.
+    int k_row_off[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) k_row_off[mt] = (8 * (n >> 2) + 4 * mt + (n & 3)) * kRowB;
+    const int nsw = swz32(8 * (n >> 2) + (n & 3));
+    int tr_row[2], tr_x[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int r = 8 * grp + 4 * h + (n >> 2);
+        tr_row[h] = r * kRowB;
+        tr_x[h] = swz32(r) ^ ((n & 3) >> 1);
+    }
+    const int tr_lo = (n & 1) * 8;
+
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): operands are in (no copy issued yet)
+    int issued = min(nunits, kQRing);
+    for (int vu = 0; vu < issued; ++vu) issue_unit(vu);
+    for (int u = 0; u < nu; ++u) {
+        const int ustart = kUnitsPerBlock * u;
+        const int nq = u == nu - 1 ? nunits - ustart : kUnitsPerBlock;
+        wait_copies(2 * (issued - (ustart + nq)));
+        barrier_keep_prefetch();
+
+        const int b = __builtin_amdgcn_readfirstlane(s_ublk[u]);
+        const int umask = __builtin_amdgcn_readfirstlane(s_umask[u]);
+        const bool act[2] = {tok_ok[0] && ((umask >> (2 * wave)) & 1),
+                             tok_ok[1] && ((umask >> (2 * wave + 1)) & 1)};
+        for (const int ifront = min(nunits, ustart + kQRing); issued < ifront; ++issued)
+            issue_unit(issued);
+        const int keyb = b * kBlock + 8 * grp;
+        if (b == c)
+            dq_block<true, true, true>(st, smem, ustart, nq, k_row_off, nsw, grp, tr_row, tr_x, tr_lo,
+                                       keyb, act, my_p, scale_log2);
+        else if (act[0] && act[1])
+            dq_block<true, true, false>(st, smem, ustart, kUnitsPerBlock, k_row_off, nsw, grp, tr_row,
+                                        tr_x, tr_lo, keyb, act, my_p, scale_log2);
+        else if (act[0])
+            dq_block<true, false, false>(st, smem, ustart, kUnitsPerBlock, k_row_off, nsw, grp, tr_row,
+                                         tr_x, tr_lo, keyb, act, my_p, scale_log2);
+        else if (act[1])
+            dq_block<false, true, false>(st, smem, ustart, kUnitsPerBlock, k_row_off, nsw, grp, tr_row,
+                                         tr_x, tr_lo, keyb, act, my_p, scale_log2);
+    }
+
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        if (!tok_ok[t]) continue;
+        uint16_t *dst = dq + (size_t(doc.start + my_p[t]) * kHeads + head) * kDim;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+            bf16x4 o;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = (__bf16)(st.acc[t][dt][i] * scale);
+            *(bf16x4 *)(dst + 16 * dt + 4 * grp) = o;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV (key-major)
+// ---------------------------------------------------------------------------
+namespace {
+constexpr int kKvTok = 4;                      // tokens per step
+constexpr int kKvRows = kKvTok * kGroup;       // 64 query rows per step
+constexpr int kStageBytes = kKvRows * kRowB;   // 16 KiB of Q (or dO) rows
+
+// Row r (0..63) of a staged Q / dO tile, chunk c at position c ^ swz16(r):
+// the 16 rows 16rt + m of a plain operand read map to 16 distinct
+// positions, and the 4 rows 4grp + e of a transposing read to 4 distinct
+// position pairs.
+__device__ __forceinline__ int swz16(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+}  // namespace
+
+__global__ __launch_bounds__(256) void bwd_dkdv_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+    const uint16_t *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ Dsum,
+    const DocSpan *__restrict__ docs, const int32_t *__restrict__ blk_off, int ndocs, int nb_max,
+    const int32_t *__restrict__ lists, const int32_t *__restrict__ list_off,
+    const int32_t *__restrict__ chunk_off, int nlists, float scale, float scale_log2,
+    float *__restrict__ part) {
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * 2 * kStageBytes];  // 2 stages x (Q, dO)
+    const int ci = blockIdx.x;
+    if (ci >= chunk_off[nlists]) return;
+    int lo = 0, hi = nlists - 1;  // list li: the last with chunk_off[li] <= ci
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (chunk_off[mid] <= ci) lo = mid; else hi = mid - 1;
+    }
+    const int li = lo;
+    const int g = li / nb_max, Bg = li - g * nb_max;
+    const int d = prefix_doc(blk_off, ndocs, Bg);
+    const DocSpan doc = docs[d];
+    const int b = Bg - blk_off[d];
+    const int e0 = list_off[li] + (ci - chunk_off[li]) * kBwdChunk;
+    const int ne = min(kBwdChunk, list_off[li + 1] - e0);
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 15, grp = lane >> 4;
+
+    // this wave's keys kb + 16kt + n as B operands (col = key, k chunk 4ks + grp)
+    const int kb = b * kBlock + 32 * wave;
+    bf16x8 kreg[2][4], vreg[2][4];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+        const int kp = min(kb + 16 * kt + n, doc.len - 1);
+        const size_t row = (size_t(doc.start + kp) * kKvHeads + g) * kDim;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            kreg[kt][ks] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(k + row + 8 * (4 * ks + grp)));
+            vreg[kt][ks] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(v + row + 8 * (4 * ks + grp)));
+        }
+    }
+    f32x4 dkt[2][8], dvt[2][8];  // [key tile][d tile]: key 16kt + n, d 16dt + 4grp + i
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) dkt[kt][dt] = dvt[kt][dt] = f32x4{};
+
+    // Stage s: tokens e0 + 4s .. +3 (past the list end: its last token,
+    // masked).  32 one-KiB copies (16 of Q, 16 of dO rows), 8 per wave;
+    // copy cc fills rows 4cc..4cc+3 = heads 4(cc%4).. of token cc/4.
+    const int nsteps = (ne + kKvTok - 1) / kKvTok;
+    auto issue_stage = [&](int s, int buf) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int c = 8 * wave + j;
+            const int cc = c & 15;
+            const int r = 4 * cc + (lane >> 4);
+            const int tok = lists[e0 + min(kKvTok * s + (cc >> 2), ne - 1)];
+            const int ch = (lane & 15) ^ swz16(r);
+            const uint16_t *src =
+                (c < 16 ? q : dout) + (size_t(tok) * kHeads + g * kGroup + (r & 15)) * kDim + 8 * ch;
+            copy_to_lds(src, smem + buf * 2 * kStageBytes + (c < 16 ? 0 : kStageBytes) + cc * 1024);
+        }
+    };
+
+    // lane-constant offsets: plain read of row 16rt + n, chunk 4ks + grp;
+    // transposing read h supplies row 16(2s2 + h) + 4grp + n/4, cols 16dt + 4(n%4)
+    const int a_off = n * kRowB;
+    const int a_sw = swz16(n);
+    int tr_row[2], tr_x[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int r = 16 * h + 4 * grp + (n >> 2);
+        tr_row[h] = r * kRowB;
+        tr_x[h] = swz16(r) ^ ((n & 3) >> 1);
+    }
+    const int tr_lo = (n & 1) * 8;
+
+    issue_stage(0, 0);
+    for (int s = 0; s < nsteps; ++s) {
+        const int buf = s & 1;
+        if (s + 1 < nsteps) {
+            issue_stage(s + 1, buf ^ 1);
+            wait_copies(8);
+        } else {
+            wait_copies(0);
+        }
+        barrier_keep_prefetch();
+        const uint8_t *Qs = smem + buf * 2 * kStageBytes;
+        const uint8_t *Ds = Qs + kStageBytes;
+
+        // per row tile rt (token 4s + rt): heads 4grp + i
+        float lse2[4][4], dsum[4][4];
+        int pos[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            const int e = kKvTok * s + rt;
+            const int tok = lists[e0 + min(e, ne - 1)];
+            pos[rt] = e < ne ? tok - doc.start : -1;  // -1: no key passes the mask
+            const size_t base = size_t(tok) * kHeads + g * kGroup + 4 * grp;
+            const f32x4 l4 = *(const f32x4 *)(lse + base);
+            const f32x4 d4 = *(const f32x4 *)(Dsum + base);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                lse2[rt][i] = l4[i] * kLog2e;
+                dsum[rt][i] = d4[i];
+            }
+        }
+        // S = Q K^T and dP = dO V^T; lane holds key 16kt + n, rows 4grp + i
+        bf16x8 pb[2][2], dsb[2][2];  // [k-step s2 = rt/2][kt]: rows 16rt + 4grp + i at 4(rt%2) + i
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            f32x4 sacc[2] = {f32x4{}, f32x4{}}, pacc[2] = {f32x4{}, f32x4{}};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const int off = 16 * rt * kRowB + a_off + (((4 * ks + grp) ^ a_sw) << 4);
+                const bf16x8 qa = __builtin_bit_cast(bf16x8, *(const u32x4 *)(Qs + off));
+                const bf16x8 da = __builtin_bit_cast(bf16x8, *(const u32x4 *)(Ds + off));
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt) {
+                    sacc[kt] = mfma_16x16x32(qa, kreg[kt][ks], sacc[kt]);
+                    pacc[kt] = mfma_16x16x32(da, vreg[kt][ks], pacc[kt]);
+                }
+            }
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const bool ok = kb + 16 * kt + n <= pos[rt];
+                    const float p = ok ? __builtin_amdgcn_exp2f(sacc[kt][i] * scale_log2 - lse2[rt][i]) : 0.f;
+                    pb[rt >> 1][kt][4 * (rt & 1) + i] = (__bf16)p;
+                    dsb[rt >> 1][kt][4 * (rt & 1) + i] = (__bf16)(p * (pacc[kt][i] - dsum[rt][i]));
+                }
+        }
+        // dV^T += dO^T P, dK^T += Q^T dS over the 64 rows (two k-steps of 32)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+                const int o0 = 32 * s2 * kRowB + tr_row[0] + (((2 * dt) ^ tr_x[0]) << 4) + tr_lo;
+                const int o1 = 32 * s2 * kRowB + tr_row[1] + (((2 * dt) ^ tr_x[1]) << 4) + tr_lo;
+                const bf16x8 doT = join_tr(read_tr(Ds + o0), read_tr(Ds + o1));
+                const bf16x8 qT = join_tr(read_tr(Qs + o0), read_tr(Qs + o1));
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt) {
+                    dvt[kt][dt] = mfma_16x16x32(doT, pb[s2][kt], dvt[kt][dt]);
+                    dkt[kt][dt] = mfma_16x16x32(qT, dsb[s2][kt], dkt[kt][dt]);
+                }
+            }
+        barrier_keep_prefetch();  // every wave is done with buf before it is refilled
+    }
+
+    float *pk = part + size_t(ci) * 2 * kBlock * kDim;
+    float *pv = pk + kBlock * kDim;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+        const int key = 32 * wave + 16 * kt + n;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+            *(f32x4 *)(pk + key * kDim + 16 * dt + 4 * grp) = dkt[kt][dt] * scale;
+            *(f32x4 *)(pv + key * kDim + 16 * dt + 4 * grp) = dvt[kt][dt];
+        }
+    }
+}
+
+// Workgroup (Bg, g): block Bg's chunk partials for KV head g summed in chunk
+// order -> bf16 dk, dv of the block's keys.
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(const float *__restrict__ part,
+                                                         const int32_t *__restrict__ chunk_off,
+                                                         const DocSpan *__restrict__ docs,
+                                                         const int32_t *__restrict__ blk_off, int ndocs,
+                                                         int nb_max, uint16_t *__restrict__ dk,
+                                                         uint16_t *__restrict__ dv) {
+    const int Bg = blockIdx.x, g = blockIdx.y;
+    if (Bg >= blk_off[ndocs]) return;
+    const int li = g * nb_max + Bg;
+    const int d = prefix_doc(blk_off, ndocs, Bg);
+    const DocSpan doc = docs[d];
+    const int b = Bg - blk_off[d];
+    const int nk = min(kBlock, doc.len - b * kBlock);
+    const int c0 = chunk_off[li], c1 = chunk_off[li + 1];
+    const int tid = threadIdx.x;
+    const int col = 4 * (tid & 31);
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+        f32x4 acc[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[j] = f32x4{};
+        for (int c = c0; c < c1; ++c) {
+            const float *src = part + (size_t(c) * 2 + which) * kBlock * kDim;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) acc[j] += *(const f32x4 *)(src + (8 * j + (tid >> 5)) * kDim + col);
+        }
+        uint16_t *dst = which == 0 ? dk : dv;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int key = 8 * j + (tid >> 5);
+            if (key < nk) {
+                bf16x4 o;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[i] = (__bf16)acc[j][i];
+                *(bf16x4 *)(dst + (size_t(doc.start + b * kBlock + key) * kKvHeads + g) * kDim + col) = o;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+BwdLayout bwd_layout(int T, int ndocs, int topk) {
+    BwdLayout L;
+    L.nb_max = ceil_div(T, kBlock) + ndocs;
+    L.nlists = kKvHeads * L.nb_max;
+    const size_t pairs = size_t(kKvHeads) * size_t(T) * size_t(topk);
+    L.max_chunks = int((pairs + kBwdChunk - 1) / kBwdChunk) + L.nlists;
+    L.list_entries = pairs;
+    return L;
+}
+
+hipError_t launch_bwd_rowdot(const uint16_t *o, const uint16_t *dout, int T, float *Dsum,
+                             hipStream_t stream) {
+    const int64_t rows = int64_t(T) * kHeads;
+    hipLaunchKernelGGL(bwd_rowdot_kernel, dim3(unsigned((rows + 15) / 16)), dim3(256), 0, stream, o, dout,
+                       rows, Dsum);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_lists(const int32_t *q2k, int topk, int T, const DocSpan *docs,
+                            const int32_t *blk_off, int ndocs, const BwdLayout &L, int32_t *cnt,
+                            int32_t *list_off, int32_t *chunk_off, int32_t *lists, hipStream_t stream) {
+    const dim3 grid(L.nb_max, kKvHeads);
+    hipLaunchKernelGGL(bwd_list_kernel<false>, grid, dim3(256), 0, stream, q2k, topk, T, docs, blk_off,
+                       ndocs, L.nb_max, cnt, (const int32_t *)nullptr, (int32_t *)nullptr);
+    hipLaunchKernelGGL(bwd_scan_kernel, dim3(1), dim3(1024), 0, stream, (const int32_t *)cnt, L.nlists,
+                       list_off, chunk_off);
+    hipLaunchKernelGGL(bwd_list_kernel<true>, grid, dim3(256), 0, stream, q2k, topk, T, docs, blk_off,
+                       ndocs, L.nb_max, (int32_t *)nullptr, (const int32_t *)list_off, lists);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *dout,
+                         const float *lse, const float *Dsum, const int32_t *q2k, int topk,
+                         const DocSpan *docs, const int32_t *tile_off, int ndocs, int T, float scale,
+                         uint16_t *dq, hipStream_t stream) {
+    const int max_tiles = ceil_div(T, kQTok) + ndocs;
+    const int grid = 8 * 8 * ceil_div(max_tiles, 16);
+    const size_t lds = size_t(kQRing) * kQUnitBytes;
+    hipLaunchKernelGGL(bwd_dq_kernel, dim3(grid), dim3(kQThreads), lds, stream, q, k, v, dout, lse, Dsum,
+                       q2k, topk, docs, tile_off, ndocs, T, scale, scale * kLog2e, dq);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkdv(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *dout,
+                           const float *lse, const float *Dsum, const DocSpan *docs,
+                           const int32_t *blk_off, int ndocs, const BwdLayout &L, const int32_t *lists,
+                           const int32_t *list_off, const int32_t *chunk_off, float scale, float *part,
+                           hipStream_t stream) {
+    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(L.max_chunks), dim3(256), 0, stream, q, k, v, dout, lse, Dsum,
+                       docs, blk_off, ndocs, L.nb_max, lists, list_off, chunk_off, L.nlists, scale,
+                       scale * kLog2e, part);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_reduce(const float *part, const int32_t *chunk_off, const DocSpan *docs,
+                             const int32_t *blk_off, int ndocs, const BwdLayout &L, uint16_t *dk,
+                             uint16_t *dv, hipStream_t stream) {
+    hipLaunchKernelGGL(bwd_reduce_kernel, dim3(L.nb_max, kKvHeads), dim3(256), 0, stream, part, chunk_off,
+                       docs, blk_off, ndocs, L.nb_max, dk, dv);
+    return hipGetLastError();
+}
+
+}  // namespace msa

@@ -30,7 +30,7 @@
 //   with lazy rescaling (the reference max only moves when it grows by more
 //   than 2^8), P^T packed to bf16 straight from the accumulators,
 //   O^T[128 x 16] += V^T . P^T   8 d-tiles x 1 k-step.
-#include "msa_internal.hpp"
+#include "attend_common.hpp"
 
 namespace msa {
 
@@ -50,57 +50,6 @@ constexpr float kLazyLog2 = 8.f;  // rescale only when the max grows by > 2^8
 static_assert(kLoadsPerWave == 2, "unit copy split assumes 2 copies per wave");
 static_assert(kRing == 2 * kUnitsPerBlock + 1, "one unit of the block after next streams ahead");
 static_assert(kRing * kUnitBytes <= 144 * 1024, "ring must leave LDS for the union tables");
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Workgroup barrier that drains this wave's LDS operations but leaves its
-// global->LDS prefetch in flight (a plain __syncthreads would also wait for
-// every outstanding vector-memory operation).  Callers wait for the unit
-// they are about to read with an explicit vmcnt first.
-__device__ __forceinline__ void barrier_keep_prefetch() {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// Wait until at most n of this wave's copies are outstanding (copies
-// complete in issue order).  n > 16 falls back to a full wait.
-__device__ __forceinline__ void wait_copies(int n) {
-#define MSA_WAIT_CASE(i) \
-    case i: asm volatile("s_waitcnt vmcnt(" #i ")" ::: "memory"); break;
-    switch (n) {
-        MSA_WAIT_CASE(1) MSA_WAIT_CASE(2) MSA_WAIT_CASE(3) MSA_WAIT_CASE(4)
-        MSA_WAIT_CASE(5) MSA_WAIT_CASE(6) MSA_WAIT_CASE(7) MSA_WAIT_CASE(8)
-        MSA_WAIT_CASE(9) MSA_WAIT_CASE(10) MSA_WAIT_CASE(11) MSA_WAIT_CASE(12)
-        MSA_WAIT_CASE(13) MSA_WAIT_CASE(14) MSA_WAIT_CASE(15) MSA_WAIT_CASE(16)
-        default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-    }
-#undef MSA_WAIT_CASE
-}
-
-// HBM -> LDS copy of 16 bytes per lane (lane l writes lds_dst + 16l).  It is
-// issued from asm so that the compiler does not hold later LDS reads of
-// other ring slots behind it (it cannot tell the slots apart and would wait
-// for every copy in flight); completion is awaited with explicit vmcnt.
-__device__ __forceinline__ void copy_to_lds(const void *src, uint8_t *lds_dst) {
-    const uint32_t m0 = (uint32_t)reinterpret_cast<uintptr_t>((lds_void *)lds_dst);
-    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0) : "memory");
-}
-
-// Max over the four 16-lane rows of a wave, for each lane position: each
-// swap of a register with itself returns, at every lane, the lane's own
-// value and that of its partner row (rows r, r^2 for the 32-lane swap;
-// r, r^1 for the 16-lane swap).
-__device__ __forceinline__ float row_max4(float x) {
-    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float row_sum4(float x) {
-    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
 
 // K unit in LDS: row r (key), 16-byte chunk c (d 8c..8c+7) at slot
 // 16r + (c ^ kswz(r)).  The 16 lanes of an operand read hold rows
@@ -225,15 +174,6 @@ __device__ __forceinline__ void attend_block(WaveState &st, const uint8_t *smem,
     }
 }
 
-// Index d with off[d] <= x < off[d+1] of a prefix-count array off[0..ndocs].
-__device__ __forceinline__ int prefix_doc(const int32_t *off, int ndocs, int x) {
-    int lo = 0, hi = ndocs - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (off[mid] <= x) lo = mid; else hi = mid - 1;
-    }
-    return lo;
-}
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -284,9 +224,10 @@ __global__ __launch_bounds__(kThreads) void attend_prefill_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ vt,
     const int32_t *__restrict__ q2k, int topk, const DocSpan *__restrict__ docs,
     const int32_t *__restrict__ tile_off, const int32_t *__restrict__ unit_off, int ndocs, int T,
-    float scale_log2, uint16_t *__restrict__ out) {
+    float scale_log2, uint16_t *__restrict__ out, float *__restrict__ lse) {
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
     constexpr int kEntries = kTok * kMaxTopk;  // 256 (token, slot) pairs
+    static_assert(kThreads >= kEntries, "one thread per (token, slot) pair");
     __shared__ int s_id[kEntries];
     __shared__ int s_first[kEntries];
     __shared__ int s_mask[kEntries];
@@ -338,37 +279,8 @@ __global__ __launch_bounds__(kThreads) void attend_prefill_kernel(
     }
 
     // ---- union of the tile's selected blocks (ascending, with token masks)
-    if (tid == 0) s_nu = 0;
-    if (tid < kEntries) {
-        const int tok = tid >> 4, sl = tid & 15;
-        int id = -1;
-        if (tok < ntok && sl < topk) id = q2k[(size_t(g) * T + doc.start + p0 + tok) * topk + sl];
-        s_id[tid] = (id >= 0 && id <= c) ? id : -1;
-    }
-    __syncthreads();
-    if (tid < kEntries) {
-        const int my = s_id[tid];
-        int first = my >= 0, mask = 0;
-        for (int j = 0; j < kEntries; ++j) {
-            if (s_id[j] == my) {
-                mask |= 1 << (j >> 4);
-                if (j < tid) first = 0;
-            }
-        }
-        s_first[tid] = first;
-        s_mask[tid] = mask;
-    }
-    __syncthreads();
-    if (tid < kEntries && s_first[tid]) {
-        const int my = s_id[tid];
-        int pos = 0;
-        for (int j = 0; j < kEntries; ++j) pos += (s_first[j] && s_id[j] < my);
-        s_ublk[pos] = my;
-        s_umask[pos] = s_mask[tid];
-        atomicAdd(&s_nu, 1);
-    }
-    __syncthreads();
-    const int nu = s_nu;
+    const int nu = tile_union(q2k, T, topk, g, doc.start + p0, ntok, c, tid, s_id, s_first, s_mask,
+                              s_ublk, s_umask, &s_nu);
     // 32-key units: 4 per union block, except that the query's own block c
     // (always last when present) stops at the unit holding p_last.
     const int last_units =
@@ -455,6 +367,12 @@ __global__ __launch_bounds__(kThreads) void attend_prefill_kernel(
     for (int t = 0; t < 2; ++t) {
         const float l_tot = row_sum4(st.l_run[t]);
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        if (lse && tok_ok[t] && grp == 0) {
+            // sum_j e^(scale s_j) = 2^(m_ref * scale_log2) * l_tot
+            const float mb = st.m_ref[t] == -INFINITY ? 0.f : st.m_ref[t] * scale_log2;
+            lse[size_t(doc.start + my_p[t]) * kHeads + head] =
+                l_tot > 0.f ? (mb + __log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
+        }
         if (tok_ok[t]) {
             uint16_t *dst = out + (size_t(doc.start + my_p[t]) * kHeads + head) * kDim;
 #pragma unroll
@@ -483,12 +401,12 @@ hipError_t launch_vt_transpose(const uint16_t *v, const DocSpan *docs, const int
 hipError_t launch_attend_prefill(const uint16_t *q, const uint16_t *k, const uint16_t *vt,
                                  const int32_t *q2k, int topk, const DocSpan *docs,
                                  const int32_t *tile_off, const int32_t *unit_off, int ndocs, int T,
-                                 float scale, uint16_t *out, hipStream_t stream) {
+                                 float scale, uint16_t *out, float *lse, hipStream_t stream) {
     const int max_tiles = ceil_div(T, kTok) + ndocs;  // document-aligned tiles (upper bound)
     const int grid = 8 * 8 * ceil_div(max_tiles, 16);  // 8 XCDs x slots
     const size_t lds = size_t(kRing) * kUnitBytes;
     hipLaunchKernelGGL(attend_prefill_kernel, dim3(grid), dim3(kThreads), lds, stream, q, k, vt, q2k,
-                       topk, docs, tile_off, unit_off, ndocs, T, scale * kLog2e, out);
+                       topk, docs, tile_off, unit_off, ndocs, T, scale * kLog2e, out, lse);
     return hipGetLastError();
 }
 

@@ -88,6 +88,37 @@ PrefillWs prefill_layout(int T, int ndocs) {
     return w;
 }
 
+struct BwdWs {
+    size_t docs, tile_off, blk_off, dsum, cnt, list_off, chunk_off, lists, part, total;
+    BwdLayout L;
+};
+
+BwdWs backward_layout(int T, int ndocs, int topk) {
+    BwdWs w;
+    w.L = bwd_layout(T, ndocs, topk);
+    size_t o = 0;
+    w.docs = o;
+    o = align256(o + sizeof(DocSpan) * size_t(ndocs));
+    w.tile_off = o;
+    o = align256(o + sizeof(int32_t) * (size_t(ndocs) + 1));
+    w.blk_off = o;
+    o = align256(o + sizeof(int32_t) * (size_t(ndocs) + 1));
+    w.dsum = o;
+    o = align256(o + sizeof(float) * size_t(T) * kHeads);
+    w.cnt = o;
+    o = align256(o + sizeof(int32_t) * size_t(w.L.nlists));
+    w.list_off = o;
+    o = align256(o + sizeof(int32_t) * (size_t(w.L.nlists) + 1));
+    w.chunk_off = o;
+    o = align256(o + sizeof(int32_t) * (size_t(w.L.nlists) + 1));
+    w.lists = o;
+    o = align256(o + sizeof(int32_t) * w.L.list_entries);
+    w.part = o;
+    o = align256(o + sizeof(float) * size_t(w.L.max_chunks) * 2 * kBlock * kDim);
+    w.total = o;
+    return w;
+}
+
 struct DecodeWs {
     size_t scores, q2k, part, total;
 };
@@ -170,6 +201,13 @@ size_t msa_prefill_workspace_bytes(int total_tokens, int num_docs, int max_seqle
     return prefill_layout(total_tokens, num_docs).total;
 }
 
+size_t msa_prefill_backward_workspace_bytes(int total_tokens, int num_docs, int max_seqlen, int topk) {
+    if (total_tokens < 1 || num_docs < 1 || num_docs > total_tokens || max_seqlen < 1 ||
+        max_seqlen > total_tokens || topk < 1 || topk > kMaxTopk || total_tokens > kBwdMaxTokens)
+        return 0;
+    return backward_layout(total_tokens, num_docs, topk).total;
+}
+
 size_t msa_decode_workspace_bytes(int batch, int max_context_len, int topk) {
     if (batch < 1 || max_context_len < 1 || topk < 1 || topk > kMaxTopk ||
         ceil_div(max_context_len, kBlock) > kDecodeMaxBlocks)
@@ -215,11 +253,10 @@ msa_status msa_select_blocks(const void *index_q, const void *index_k, int index
     return MSA_OK;
 }
 
-msa_status msa_sparse_attend_prefill(const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                                     const int32_t *q2k, int topk, const int32_t *cu_seqlens,
-                                     int num_docs, int total_tokens, int max_seqlen,
-                                     float softmax_scale, uint16_t *out, void *workspace,
-                                     size_t workspace_bytes, void *stream) {
+static msa_status prefill_impl(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                               const int32_t *q2k, int topk, const int32_t *cu_seqlens, int num_docs,
+                               int total_tokens, int max_seqlen, float softmax_scale, uint16_t *out,
+                               float *lse, void *workspace, size_t workspace_bytes, void *stream) {
     if (!q || !k || !v || !q2k || !out) return fail(MSA_ERR_INVALID_ARG, "q, k, v, q2k and out must be non-NULL");
     if (topk < 1 || topk > kMaxTopk)
         return fail(MSA_ERR_UNSUPPORTED, "topk must be in [1, %d] (got %d)", kMaxTopk, topk);
@@ -247,8 +284,85 @@ msa_status msa_sparse_attend_prefill(const uint16_t *q, const uint16_t *k, const
     if (e != hipSuccess) return hip_fail(e, "vt_transpose");
     tm.mark(s, "attend_prefill");
     e = launch_attend_prefill(q, k, vt, q2k, topk, docs, off, uoff, num_docs, total_tokens,
-                              softmax_scale, out, s);
+                              softmax_scale, out, lse, s);
     if (e != hipSuccess) return hip_fail(e, "attend_prefill");
+    tm.mark(s, nullptr);
+    return MSA_OK;
+}
+
+msa_status msa_sparse_attend_prefill(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                     const int32_t *q2k, int topk, const int32_t *cu_seqlens,
+                                     int num_docs, int total_tokens, int max_seqlen,
+                                     float softmax_scale, uint16_t *out, void *workspace,
+                                     size_t workspace_bytes, void *stream) {
+    return prefill_impl(q, k, v, q2k, topk, cu_seqlens, num_docs, total_tokens, max_seqlen, softmax_scale,
+                        out, nullptr, workspace, workspace_bytes, stream);
+}
+
+msa_status msa_sparse_attend_prefill_lse(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                         const int32_t *q2k, int topk, const int32_t *cu_seqlens,
+                                         int num_docs, int total_tokens, int max_seqlen,
+                                         float softmax_scale, uint16_t *out, float *lse, void *workspace,
+                                         size_t workspace_bytes, void *stream) {
+    if (!lse) return fail(MSA_ERR_INVALID_ARG, "lse must be non-NULL");
+    return prefill_impl(q, k, v, q2k, topk, cu_seqlens, num_docs, total_tokens, max_seqlen, softmax_scale,
+                        out, lse, workspace, workspace_bytes, stream);
+}
+
+msa_status msa_sparse_attend_prefill_backward(
+    const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *out, const float *lse,
+    const uint16_t *dout, const int32_t *q2k, int topk, const int32_t *cu_seqlens, int num_docs,
+    int total_tokens, int max_seqlen, float softmax_scale, uint16_t *dq, uint16_t *dk, uint16_t *dv,
+    void *workspace, size_t workspace_bytes, void *stream) {
+    if (!q || !k || !v || !out || !lse || !dout || !q2k || !dq || !dk || !dv)
+        return fail(MSA_ERR_INVALID_ARG, "q, k, v, out, lse, dout, q2k, dq, dk and dv must be non-NULL");
+    if (topk < 1 || topk > kMaxTopk)
+        return fail(MSA_ERR_UNSUPPORTED, "topk must be in [1, %d] (got %d)", kMaxTopk, topk);
+    msa_status st = check_geometry(cu_seqlens, num_docs, total_tokens, max_seqlen);
+    if (st != MSA_OK) return st;
+    if (total_tokens > kBwdMaxTokens)
+        return fail(MSA_ERR_UNSUPPORTED, "total_tokens above %d is not supported by the backward (got %d)",
+                    kBwdMaxTokens, total_tokens);
+    if (!(softmax_scale > 0.f) || softmax_scale > 1e30f)
+        return fail(MSA_ERR_INVALID_ARG, "softmax_scale must be a positive finite number");
+    const BwdWs ws = backward_layout(total_tokens, num_docs, topk);
+    if (!workspace || workspace_bytes < ws.total)
+        return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", ws.total,
+                    workspace ? workspace_bytes : size_t(0));
+    hipStream_t s = (hipStream_t)stream;
+    uint8_t *base = (uint8_t *)workspace;
+    DocSpan *docs = (DocSpan *)(base + ws.docs);
+    int32_t *tile_off = (int32_t *)(base + ws.tile_off);
+    int32_t *blk_off = (int32_t *)(base + ws.blk_off);
+    float *dsum = (float *)(base + ws.dsum);
+    int32_t *cnt = (int32_t *)(base + ws.cnt);
+    int32_t *list_off = (int32_t *)(base + ws.list_off);
+    int32_t *chunk_off = (int32_t *)(base + ws.chunk_off);
+    int32_t *lists = (int32_t *)(base + ws.lists);
+    float *part = (float *)(base + ws.part);
+    TimingScope tm;
+    tm.mark(s, "doc_setup");
+    hipError_t e = launch_doc_setup(cu_seqlens, num_docs, total_tokens, max_seqlen, kAttnTile, kBlock, docs,
+                                    tile_off, blk_off, s);
+    if (e != hipSuccess) return hip_fail(e, "doc_setup");
+    tm.mark(s, "bwd_rowdot");
+    e = launch_bwd_rowdot(out, dout, total_tokens, dsum, s);
+    if (e != hipSuccess) return hip_fail(e, "bwd_rowdot");
+    tm.mark(s, "bwd_lists");
+    e = launch_bwd_lists(q2k, topk, total_tokens, docs, blk_off, num_docs, ws.L, cnt, list_off, chunk_off,
+                         lists, s);
+    if (e != hipSuccess) return hip_fail(e, "bwd_lists");
+    tm.mark(s, "bwd_dq");
+    e = launch_bwd_dq(q, k, v, dout, lse, dsum, q2k, topk, docs, tile_off, num_docs, total_tokens,
+                      softmax_scale, dq, s);
+    if (e != hipSuccess) return hip_fail(e, "bwd_dq");
+    tm.mark(s, "bwd_dkdv");
+    e = launch_bwd_dkdv(q, k, v, dout, lse, dsum, docs, blk_off, num_docs, ws.L, lists, list_off, chunk_off,
+                        softmax_scale, part, s);
+    if (e != hipSuccess) return hip_fail(e, "bwd_dkdv");
+    tm.mark(s, "bwd_reduce");
+    e = launch_bwd_reduce(part, chunk_off, docs, blk_off, num_docs, ws.L, dk, dv, s);
+    if (e != hipSuccess) return hip_fail(e, "bwd_reduce");
     tm.mark(s, nullptr);
     return MSA_OK;
 }

@@ -37,10 +37,41 @@ hipError_t launch_topk_prefill(const float *S, const DocSpan *docs, int ndocs, i
 size_t prefill_vt_bytes(int T, int ndocs);
 hipError_t launch_vt_transpose(const uint16_t *v, const DocSpan *docs, const int32_t *unit_off,
                                int ndocs, int T, uint16_t *vt, hipStream_t stream);
+// lse (optional, NULL to skip): natural-log log-sum-exp of every row [T,64].
 hipError_t launch_attend_prefill(const uint16_t *q, const uint16_t *k, const uint16_t *vt,
                                  const int32_t *q2k, int topk, const DocSpan *docs,
                                  const int32_t *tile_off, const int32_t *unit_off, int ndocs, int T,
-                                 float scale, uint16_t *out, hipStream_t stream);
+                                 float scale, uint16_t *out, float *lse, hipStream_t stream);
+
+// Backward of the prefill attention.  Block lists: for list li = g*nb_max +
+// Bg (KV head g, document block Bg numbered over all documents by blk_off)
+// the tokens selecting the block, ascending; chunks of kBwdChunk tokens.
+constexpr int kBwdChunk = 512;
+constexpr int kBwdMaxTokens = 1 << 22;  // keeps 4 * T * topk list entries within int32
+struct BwdLayout {
+    int nb_max;           // upper bound on the number of document blocks
+    int nlists;           // 4 * nb_max
+    int max_chunks;       // upper bound on the number of list chunks
+    size_t list_entries;  // upper bound on the list entries: 4 * T * topk
+};
+BwdLayout bwd_layout(int T, int ndocs, int topk);
+hipError_t launch_bwd_rowdot(const uint16_t *o, const uint16_t *dout, int T, float *Dsum,
+                             hipStream_t stream);
+hipError_t launch_bwd_lists(const int32_t *q2k, int topk, int T, const DocSpan *docs,
+                            const int32_t *blk_off, int ndocs, const BwdLayout &L, int32_t *cnt,
+                            int32_t *list_off, int32_t *chunk_off, int32_t *lists, hipStream_t stream);
+hipError_t launch_bwd_dq(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *dout,
+                         const float *lse, const float *Dsum, const int32_t *q2k, int topk,
+                         const DocSpan *docs, const int32_t *tile_off, int ndocs, int T, float scale,
+                         uint16_t *dq, hipStream_t stream);
+hipError_t launch_bwd_dkdv(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *dout,
+                           const float *lse, const float *Dsum, const DocSpan *docs,
+                           const int32_t *blk_off, int ndocs, const BwdLayout &L, const int32_t *lists,
+                           const int32_t *list_off, const int32_t *chunk_off, float scale, float *part,
+                           hipStream_t stream);
+hipError_t launch_bwd_reduce(const float *part, const int32_t *chunk_off, const DocSpan *docs,
+                             const int32_t *blk_off, int ndocs, const BwdLayout &L, uint16_t *dk,
+                             uint16_t *dv, hipStream_t stream);
 
 // Paged decode.
 hipError_t launch_decode_scores(const void *iq, const void *ikc, bool fp8, const int32_t *pt,

@@ -90,6 +90,8 @@ int msa_version(void);
 /* Workspace sizes in bytes (0 if the arguments are invalid). */
 size_t msa_select_blocks_workspace_bytes(int total_tokens, int num_docs, int max_seqlen);
 size_t msa_prefill_workspace_bytes(int total_tokens, int num_docs, int max_seqlen);
+/* also 0 above 4194304 tokens */
+size_t msa_prefill_backward_workspace_bytes(int total_tokens, int num_docs, int max_seqlen, int topk);
 size_t msa_decode_workspace_bytes(int batch, int max_context_len, int topk);
 
 /*
@@ -138,6 +140,53 @@ msa_status msa_sparse_attend_prefill(const uint16_t *q, const uint16_t *k, const
                                      int num_docs, int total_tokens, int max_seqlen,
                                      float softmax_scale, uint16_t *out, void *workspace,
                                      size_t workspace_bytes, void *stream);
+
+/*
+ * msa_sparse_attend_prefill that also returns the log-sum-exp of every
+ * attention row, the state the backward needs (NeMo msa page,
+ * _SparseAttention: the forward saves what the backward uses).
+ *
+ *  lse out fp32 [T,64]: lse[t,h] = log sum_j exp(softmax_scale * q[t,h].k_j)
+ *      over the row's key set (natural log; -inf for an empty key set).
+ *  Every other argument, the workspace and the errors are those of
+ *  msa_sparse_attend_prefill; lse == NULL is MSA_ERR_INVALID_ARG.
+ */
+msa_status msa_sparse_attend_prefill_lse(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                         const int32_t *q2k, int topk, const int32_t *cu_seqlens,
+                                         int num_docs, int total_tokens, int max_seqlen,
+                                         float softmax_scale, uint16_t *out, float *lse, void *workspace,
+                                         size_t workspace_bytes, void *stream);
+
+/*
+ * Backward of msa_sparse_attend_prefill for a fixed selection (NeMo msa
+ * page, _SparseAttention.backward: bf16 grad_out [tokens,64,128] -> dq
+ * [tokens,64,128] and dk, dv [tokens,4,128]; the block selection is a hard
+ * top-k and receives no gradient).
+ *
+ *  q, k, v, q2k, topk, cu_seqlens, num_docs, total_tokens, max_seqlen,
+ *      softmax_scale: those of the forward call.
+ *  out  [T,64,128] bf16: the forward output; lse [T,64] fp32: the forward's
+ *      log-sum-exp (msa_sparse_attend_prefill_lse).
+ *  dout [T,64,128] bf16: gradient of the loss with respect to out.
+ *  dq [T,64,128], dk [T,4,128], dv [T,4,128] out, bf16: with P the rows'
+ *      softmax weights, dS = P * (dout.v - rowsum(dout*out)):
+ *      dq = softmax_scale * sum_j dS_j k_j; dk_j and dv_j sum softmax_scale *
+ *      dS q and P * dout over the query rows (all 16 heads of the KV group)
+ *      whose key set holds j; zero for keys no row attends to.  fp32
+ *      accumulation in a fixed order (results repeat bit for bit), rounded
+ *      to nearest even once.
+ *  workspace: msa_prefill_backward_workspace_bytes(T, num_docs, max_seqlen,
+ *      topk) bytes of device memory, owned by the caller, no alignment
+ *      beyond 256 bytes, contents on entry ignored.
+ *  Errors: NULL pointers, bad geometry or scale (MSA_ERR_INVALID_ARG), topk
+ *  outside 1..16 or T above 4194304 (MSA_ERR_UNSUPPORTED), a short
+ *  workspace (MSA_ERR_WORKSPACE), all before any work is enqueued.
+ */
+msa_status msa_sparse_attend_prefill_backward(
+    const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *out, const float *lse,
+    const uint16_t *dout, const int32_t *q2k, int topk, const int32_t *cu_seqlens, int num_docs,
+    int total_tokens, int max_seqlen, float softmax_scale, uint16_t *dq, uint16_t *dk, uint16_t *dv,
+    void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * One decode step over a paged cache (TensorRT-LLM config class description:

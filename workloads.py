@@ -127,6 +127,41 @@ def grad_out(seed: int, T: int) -> np.ndarray:
     return normal_bf16(np.random.SeedSequence([seed, 0x6472]), (T, 64, 128))
 
 
+def synthetic_q2k(seed: int, cu_seqlens, topk: int, init_blocks: int = 0, local_blocks: int = 1,
+                  hot_frac: float = 0.05) -> np.ndarray:
+    """A seeded stand-in selection, token-major int32 [T,4,topk], shaped like
+    the planted long-prefill workload's: every row holds its forced blocks,
+    then the document's "hot" blocks (a fixed random hot_frac of its blocks)
+    that precede the query block, then distinct random earlier blocks, in
+    ascending order with -1 padding.  No scores are computed: it is an input
+    for the attention step only."""
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    T = int(cu[-1])
+    g = np.random.default_rng(np.random.SeedSequence([seed, 0x71]))
+    rows = np.full((T, 4, topk), -1, dtype=np.int32)
+    for d in range(len(cu) - 1):
+        L = int(cu[d + 1] - cu[d])
+        nb = (L + 127) // 128
+        hot = [np.sort(g.choice(nb, size=max(1, int(round(hot_frac * nb))), replace=False))
+               for _ in range(4)]
+        for p in range(L):
+            c = p // 128
+            for h in range(4):
+                forced = {b for b in range(c + 1) if b < init_blocks or b >= c - local_blocks + 1}
+                pick = list(forced)
+                for b in hot[h]:
+                    if len(pick) >= topk or b > c:
+                        break
+                    if b not in forced:
+                        pick.append(int(b))
+                if len(pick) < topk:
+                    rest = np.setdiff1d(np.arange(c + 1), pick)
+                    pick += g.permutation(rest)[:topk - len(pick)].tolist()
+                pick = sorted(pick)[:topk]
+                rows[cu[d] + p, h, :len(pick)] = pick
+    return rows
+
+
 def rms_normalise(z: np.ndarray, eps: float = 1e-6) -> np.ndarray:
     """z / sqrt(mean(z^2) + eps) along the last axis (index vectors arrive
     post-norm; this stands in for the model's norm)."""
