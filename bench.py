@@ -47,6 +47,7 @@ def parse():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (reference dispatch for scaling the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
+    ap.add_argument("--no-backward", action="store_true", help="skip the prefill backward leg")
     ap.add_argument("--no-graph", action="store_true",
                     help="time direct launches only (default: the decode step is also captured "
                          "into a HIP graph and the replay time is the headline value)")
@@ -309,6 +310,48 @@ def bench_prefill(args, hip, flush):
                 score_flops=score_flops, attn_flops=attn_flops, q2k=q2k, out=out)
 
 
+def bench_backward(args, hip, flush, pres):
+    """Training leg on the 32k planted prefill: the forward with log-sum-exp,
+    then the backward (dq, dk, dv) for the selection the GPU made."""
+    import torch
+    import block_sparse_gqa_score_amd as msa
+    import workloads as W
+    w, q2k = pres["w"], pres["q2k"]
+    q, k, v, cu = dev(w.q), dev(w.k), dev(w.v), dev(w.cu_seqlens)
+    dout = dev(W.grad_out(2, w.T))
+    out = torch.empty((w.T, 64, 128), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.T, 64), dtype=torch.float32, device="cuda")
+    dq = torch.empty_like(out)
+    dk = torch.empty((w.T, 4, 128), dtype=torch.bfloat16, device="cuda")
+    dv = torch.empty_like(dk)
+    ws_a = torch.empty(max(256, msa.prefill_workspace_bytes(w.T, w.num_docs, w.max_seqlen)),
+                       dtype=torch.uint8, device="cuda")
+    ws_b = torch.empty(msa.prefill_backward_workspace_bytes(w.T, w.num_docs, w.max_seqlen, w.topk),
+                       dtype=torch.uint8, device="cuda")
+    L = msa.lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    st = L.msa_sparse_attend_prefill_lse(P(q), P(k), P(v), P(q2k), w.topk, P(cu), w.num_docs, w.T,
+                                         w.max_seqlen, w.scale, P(out), P(lse), P(ws_a), ws_a.numel(),
+                                         ctypes.c_void_p(stream))
+    if st != 0:
+        raise RuntimeError(L.msa_last_error().decode())
+
+    def run(events):
+        if events is not None:
+            L.msa_set_timing_events(ctypes.c_void_p(ctypes.addressof(events)), 7)
+        st = L.msa_sparse_attend_prefill_backward(
+            P(q), P(k), P(v), P(out), P(lse), P(dout), P(q2k), w.topk, P(cu), w.num_docs, w.T,
+            w.max_seqlen, w.scale, P(dq), P(dk), P(dv), P(ws_b), ws_b.numel(), ctypes.c_void_p(stream))
+        if st != 0:
+            raise RuntimeError(L.msa_last_error().decode())
+
+    step_ms, evs, names = timed_steps(run, args.prefill_steps, args.warmup, hip, stream, flush, 7)
+    kt = kernel_times(evs, [names], hip)
+    per_kernel = {kk: stats(vv)["mean"] for kk, vv in kt.items()}
+    return dict(step=stats(step_ms), per_kernel_ms=per_kernel)
+
+
 def cpu_baseline_decode(d, seconds):
     import numpy as np
     import oracle
@@ -468,6 +511,25 @@ def main():
             "block_scores": {"achieved_tflops": round(pres["score_flops"] / (s_ms * 1e-3) / 1e12, 2),
                              "frac": round(pres["score_flops"] / (s_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
         }
+        if not args.no_backward:
+            bres = bench_backward(args, hip, flush, pres)
+            b_ms = bres["step"]["mean"]
+            pk = bres["per_kernel_ms"]
+            # algorithmic: S recomputed, dP, dV, dK, dQ = 2.5x the forward's attention flops;
+            # the dQ kernel executes S, dP, dQ (1.5x), the dK/dV kernel S, dP, dV, dK (2x)
+            alg = 2.5 * pres["attn_flops"]
+            line["backward_32k"] = {
+                "workload": "prefill_32k_planted", "what": "dq, dk, dv for the GPU's selection",
+                "ms_per_step": round(b_ms, 6), "steps": args.prefill_steps,
+                "per_kernel_us": {kk: round(vv * 1e3, 3) for kk, vv in pk.items()},
+                "roofline": {"bound": "mfma", "achieved": round(alg / (b_ms * 1e-3) / 1e12, 2),
+                             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                             "frac": round(alg / (b_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                             "alg_flops_per_step": alg},
+                "bwd_dq_tflops": round(1.5 * pres["attn_flops"] / (pk["bwd_dq"] * 1e-3) / 1e12, 2),
+                "bwd_dkdv_tflops": round(2.0 * pres["attn_flops"] / (pk["bwd_dkdv"] * 1e-3) / 1e12, 2),
+                "train_attention_ms": round(b_ms + pres["per_kernel_ms"]["attend_prefill"], 3),
+            }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_decode(d, args.cpu_seconds)
         if not args.no_prefill:

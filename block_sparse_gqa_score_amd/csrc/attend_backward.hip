@@ -23,9 +23,11 @@
 //       as MFMA operands; per step of 4 tokens (64 query rows of the KV
 //       group, staged in LDS) S = Q K^T, dP = dO V^T, dS, then
 //       dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T taken by
-//       transposing LDS reads; one fp32 partial (dK, dV) per chunk.
-//   bwd_reduce_kernel   - per block, its chunk partials summed in chunk order
-//       into bf16 dk, dv (zero for keys that no query attends to).
+//       transposing LDS reads; one fp32 partial (dK, dV) per chunk, or the
+//       final bf16 dk, dv when the block's list is a single chunk.
+//   bwd_reduce_kernel   - per block with several chunks, the partials summed
+//       in chunk order into bf16 dk, dv (a single-chunk block is written by
+//       its chunk; keys that no query attends to get zeros).
 #include "attend_common.hpp"
 
 namespace msa {
@@ -85,6 +87,21 @@ __global__ __launch_bounds__(256) void bwd_rowdot_kernel(const uint16_t *__restr
 // blk_off), KV head g; list index li = g * nb_max + Bg.  Token at document
 // position p >= 128b selects block b when its row lists b (a token before
 // the block cannot: its candidates stop at its own block).
+// Whether a q2k row of topk entries lists block b (16-byte loads when every
+// row is 16-byte aligned: vec = aligned base and topk % 4 == 0).
+__device__ __forceinline__ bool row_has(const int32_t *__restrict__ r, int topk, int b, bool vec) {
+    bool hit = false;
+    if (vec) {
+        for (int s = 0; s < topk; s += 4) {
+            const u32x4 x = *(const u32x4 *)(r + s);
+            hit |= (int(x[0]) == b) | (int(x[1]) == b) | (int(x[2]) == b) | (int(x[3]) == b);
+        }
+    } else {
+        for (int s = 0; s < topk; ++s) hit |= r[s] == b;
+    }
+    return hit;
+}
+
 template <bool kFill>
 __global__ __launch_bounds__(256) void bwd_list_kernel(const int32_t *__restrict__ q2k, int topk, int T,
                                                        const DocSpan *__restrict__ docs,
@@ -92,7 +109,8 @@ __global__ __launch_bounds__(256) void bwd_list_kernel(const int32_t *__restrict
                                                        int nb_max, int32_t *__restrict__ cnt,
                                                        const int32_t *__restrict__ list_off,
                                                        int32_t *__restrict__ lists) {
-    __shared__ int s_w[4];
+    constexpr int kSub = 4;  // rounds of 256 tokens whose rows are loaded together
+    __shared__ int s_w[kSub][4];
     const int Bg = blockIdx.x, g = blockIdx.y;
     const int li = g * nb_max + Bg;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -105,25 +123,34 @@ __global__ __launch_bounds__(256) void bwd_list_kernel(const int32_t *__restrict
     const int b = Bg - blk_off[d];
     const int32_t *rows = q2k + size_t(g) * T * topk;
     int base = kFill ? list_off[li] : 0;
-    for (int p0 = b * kBlock; p0 < doc.len; p0 += 256) {
-        const int p = p0 + tid;
-        bool hit = false;
-        if (p < doc.len) {
-            const int32_t *r = rows + size_t(doc.start + p) * topk;
-            for (int s = 0; s < topk; ++s) hit |= r[s] == b;
-        }
-        const uint64_t m = __ballot(hit);
-        if (lane == 0) s_w[wave] = __popcll(m);
-        __syncthreads();
-        int before = 0, all = 0;
+    const bool vec = (topk & 3) == 0 && (reinterpret_cast<uintptr_t>(q2k) & 15) == 0;
+    for (int p0 = b * kBlock; p0 < doc.len; p0 += 256 * kSub) {
+        bool hit[kSub];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const int x = s_w[w];
-            before += w < wave ? x : 0;
-            all += x;
+        for (int j = 0; j < kSub; ++j) {
+            const int p = p0 + 256 * j + tid;
+            hit[j] = p < doc.len && row_has(rows + size_t(doc.start + p) * topk, topk, b, vec);
         }
-        if (kFill && hit) lists[base + before + __popcll(m & ((1ull << lane) - 1ull))] = doc.start + p;
-        base += all;
+        uint64_t m[kSub];
+#pragma unroll
+        for (int j = 0; j < kSub; ++j) {
+            m[j] = __ballot(hit[j]);
+            if (lane == 0) s_w[j][wave] = __popcll(m[j]);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kSub; ++j) {
+            int before = 0, all = 0;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const int x = s_w[j][w];
+                before += w < wave ? x : 0;
+                all += x;
+            }
+            if (kFill && hit[j])
+                lists[base + before + __popcll(m[j] & ((1ull << lane) - 1ull))] = doc.start + p0 + 256 * j + tid;
+            base += all;
+        }
         __syncthreads();  // s_w is rewritten next round
     }
     if (!kFill && tid == 0) cnt[li] = base;
@@ -413,7 +440,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
     const DocSpan *__restrict__ docs, const int32_t *__restrict__ blk_off, int ndocs, int nb_max,
     const int32_t *__restrict__ lists, const int32_t *__restrict__ list_off,
     const int32_t *__restrict__ chunk_off, int nlists, float scale, float scale_log2,
-    float *__restrict__ part) {
+    float *__restrict__ part, uint16_t *__restrict__ dk, uint16_t *__restrict__ dv) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * 2 * kStageBytes];  // 2 stages x (Q, dO)
     const int ci = blockIdx.x;
     if (ci >= chunk_off[nlists]) return;
@@ -558,6 +585,27 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
         barrier_keep_prefetch();  // every wave is done with buf before it is refilled
     }
 
+    if (chunk_off[li + 1] - chunk_off[li] == 1) {
+        // the block's only chunk: its sums are final, written as bf16
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+            const int kp = kb + 16 * kt + n;
+            if (kp >= doc.len) continue;
+            const size_t row = (size_t(doc.start + kp) * kKvHeads + g) * kDim + 4 * grp;
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+                bf16x4 a, c;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    a[i] = (__bf16)(dkt[kt][dt][i] * scale);
+                    c[i] = (__bf16)dvt[kt][dt][i];
+                }
+                *(bf16x4 *)(dk + row + 16 * dt) = a;
+                *(bf16x4 *)(dv + row + 16 * dt) = c;
+            }
+        }
+        return;
+    }
     float *pk = part + size_t(ci) * 2 * kBlock * kDim;
     float *pv = pk + kBlock * kDim;
 #pragma unroll
@@ -571,44 +619,43 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
     }
 }
 
-// Workgroup (Bg, g): block Bg's chunk partials for KV head g summed in chunk
-// order -> bf16 dk, dv of the block's keys.
+// Workgroup (Bg, g, z): keys 16z..16z+15 of block Bg, KV head g.  A block
+// with several chunks gets its partials summed in chunk order into bf16
+// dk, dv; a block no row selects gets zeros; a single-chunk block was
+// written by its chunk.
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(const float *__restrict__ part,
                                                          const int32_t *__restrict__ chunk_off,
                                                          const DocSpan *__restrict__ docs,
                                                          const int32_t *__restrict__ blk_off, int ndocs,
                                                          int nb_max, uint16_t *__restrict__ dk,
                                                          uint16_t *__restrict__ dv) {
-    const int Bg = blockIdx.x, g = blockIdx.y;
+    const int Bg = blockIdx.x, g = blockIdx.y, z = blockIdx.z;
     if (Bg >= blk_off[ndocs]) return;
     const int li = g * nb_max + Bg;
+    const int c0 = chunk_off[li], c1 = chunk_off[li + 1];
+    if (c1 - c0 == 1) return;
     const int d = prefix_doc(blk_off, ndocs, Bg);
     const DocSpan doc = docs[d];
     const int b = Bg - blk_off[d];
     const int nk = min(kBlock, doc.len - b * kBlock);
-    const int c0 = chunk_off[li], c1 = chunk_off[li + 1];
     const int tid = threadIdx.x;
-    const int col = 4 * (tid & 31);
+    const int which = tid >> 7;            // 0: dk, 1: dv
+    const int key = 16 * z + ((tid >> 3) & 15);
+    const int col = 16 * (tid & 7);        // 16 consecutive d per thread
+    f32x4 acc[4] = {f32x4{}, f32x4{}, f32x4{}, f32x4{}};
+    for (int c = c0; c < c1; ++c) {
+        const float *src = part + ((size_t(c) * 2 + which) * kBlock + key) * kDim + col;
 #pragma unroll
-    for (int which = 0; which < 2; ++which) {
-        f32x4 acc[16];
+        for (int j = 0; j < 4; ++j) acc[j] += *(const f32x4 *)(src + 4 * j);
+    }
+    if (key < nk) {
+        uint16_t *dst = (which == 0 ? dk : dv) + (size_t(doc.start + b * kBlock + key) * kKvHeads + g) * kDim + col;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) acc[j] = f32x4{};
-        for (int c = c0; c < c1; ++c) {
-            const float *src = part + (size_t(c) * 2 + which) * kBlock * kDim;
+        for (int j = 0; j < 4; ++j) {
+            bf16x4 o;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) acc[j] += *(const f32x4 *)(src + (8 * j + (tid >> 5)) * kDim + col);
-        }
-        uint16_t *dst = which == 0 ? dk : dv;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int key = 8 * j + (tid >> 5);
-            if (key < nk) {
-                bf16x4 o;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) o[i] = (__bf16)acc[j][i];
-                *(bf16x4 *)(dst + (size_t(doc.start + b * kBlock + key) * kKvHeads + g) * kDim + col) = o;
-            }
+            for (int i = 0; i < 4; ++i) o[i] = (__bf16)acc[j][i];
+            *(bf16x4 *)(dst + 4 * j) = o;
         }
     }
 }
@@ -663,17 +710,17 @@ hipError_t launch_bwd_dkdv(const uint16_t *q, const uint16_t *k, const uint16_t 
                            const float *lse, const float *Dsum, const DocSpan *docs,
                            const int32_t *blk_off, int ndocs, const BwdLayout &L, const int32_t *lists,
                            const int32_t *list_off, const int32_t *chunk_off, float scale, float *part,
-                           hipStream_t stream) {
+                           uint16_t *dk, uint16_t *dv, hipStream_t stream) {
     hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(L.max_chunks), dim3(256), 0, stream, q, k, v, dout, lse, Dsum,
                        docs, blk_off, ndocs, L.nb_max, lists, list_off, chunk_off, L.nlists, scale,
-                       scale * kLog2e, part);
+                       scale * kLog2e, part, dk, dv);
     return hipGetLastError();
 }
 
 hipError_t launch_bwd_reduce(const float *part, const int32_t *chunk_off, const DocSpan *docs,
                              const int32_t *blk_off, int ndocs, const BwdLayout &L, uint16_t *dk,
                              uint16_t *dv, hipStream_t stream) {
-    hipLaunchKernelGGL(bwd_reduce_kernel, dim3(L.nb_max, kKvHeads), dim3(256), 0, stream, part, chunk_off,
+    hipLaunchKernelGGL(bwd_reduce_kernel, dim3(L.nb_max, kKvHeads, kBlock / 16), dim3(256), 0, stream, part, chunk_off,
                        docs, blk_off, ndocs, L.nb_max, dk, dv);
     return hipGetLastError();
 }

@@ -358,7 +358,7 @@ msa_status msa_sparse_attend_prefill_backward(
     if (e != hipSuccess) return hip_fail(e, "bwd_dq");
     tm.mark(s, "bwd_dkdv");
     e = launch_bwd_dkdv(q, k, v, dout, lse, dsum, docs, blk_off, num_docs, ws.L, lists, list_off, chunk_off,
-                        softmax_scale, part, s);
+                        softmax_scale, part, dk, dv, s);
     if (e != hipSuccess) return hip_fail(e, "bwd_dkdv");
     tm.mark(s, "bwd_reduce");
     e = launch_bwd_reduce(part, chunk_off, docs, blk_off, num_docs, ws.L, dk, dv, s);

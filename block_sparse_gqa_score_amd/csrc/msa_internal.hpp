@@ -68,7 +68,7 @@ hipError_t launch_bwd_dkdv(const uint16_t *q, const uint16_t *k, const uint16_t 
                            const float *lse, const float *Dsum, const DocSpan *docs,
                            const int32_t *blk_off, int ndocs, const BwdLayout &L, const int32_t *lists,
                            const int32_t *list_off, const int32_t *chunk_off, float scale, float *part,
-                           hipStream_t stream);
+                           uint16_t *dk, uint16_t *dv, hipStream_t stream);
 hipError_t launch_bwd_reduce(const float *part, const int32_t *chunk_off, const DocSpan *docs,
                              const int32_t *blk_off, int ndocs, const BwdLayout &L, uint16_t *dk,
                              uint16_t *dv, hipStream_t stream);
