@@ -323,9 +323,8 @@ def cache_insert(k, v, index_k, slot_mapping, k_cache, v_cache, index_k_cache):
     _dev_tensor("index_k", index_k, (N, 1, 128), (torch.bfloat16,), device)
     _dev_tensor("slot_mapping", slot_mapping, (N,), (torch.int32,), device)
     slots = int(k_cache.shape[0])
-    kv_types = (torch.bfloat16,) if kv_scales is None else (torch.float8_e4m3fn, torch.uint8)
-    _dev_tensor("k_cache", k_cache, (slots, 4, 128), kv_types, device)
-    _dev_tensor("v_cache", v_cache, (slots, 4, 128), kv_types, device)
+    _dev_tensor("k_cache", k_cache, (slots, 4, 128), (torch.bfloat16,), device)
+    _dev_tensor("v_cache", v_cache, (slots, 4, 128), (torch.bfloat16,), device)
     _dev_tensor("index_k_cache", index_k_cache, (slots, 1, 128), _INDEX_DTYPES, device)
     _check(lib().msa_cache_insert(_ptr(k), _ptr(v), _ptr(index_k), _ptr(slot_mapping), N,
                                   _index_code(index_k_cache), _ptr(k_cache), _ptr(v_cache),
