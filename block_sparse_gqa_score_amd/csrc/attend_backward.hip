@@ -21,7 +21,8 @@
 //   bwd_dkdv_kernel     - key-major: one workgroup per chunk of kBwdChunk
 //       tokens of one block's list; 4 waves x 32 keys hold their K and V rows
 //       as MFMA operands; per step of 4 tokens (64 query rows of the KV
-//       group, staged in LDS) S = Q K^T, dP = dO V^T, dS, then
+//       group, with their lse and D, staged in a 4-step LDS ring) S = Q K^T,
+//       dP = dO V^T, dS, then
 //       dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T taken by
 //       transposing LDS reads; one fp32 partial (dK, dV) per chunk, or the
 //       final bf16 dk, dv when the block's list is a single chunk.
@@ -333,6 +334,14 @@ __global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(
         st.lse2[t] = lse[row] * kLog2e;
         st.dsum[t] = Dsum[row];
     }
+    // use the loaded operands once here, so that the compiler's wait for them
+    // sits before the block loop (a wait inside it would drain the prefetch)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) asm volatile("" ::"v"(st.qb[t][ks]), "v"(st.dob[t][ks]));
+        asm volatile("" ::"v"(st.lse2[t]), "v"(st.dsum[t]));
+    }
 
     const int nu = tile_union(q2k, T, topk, g, doc.start + p0, ntok, c, tid, s_id, s_first, s_mask,
                               s_ublk, s_umask, &s_nu);
@@ -426,6 +435,27 @@ namespace {
 constexpr int kKvTok = 4;                      // tokens per step
 constexpr int kKvRows = kKvTok * kGroup;       // 64 query rows per step
 constexpr int kStageBytes = kKvRows * kRowB;   // 16 KiB of Q (or dO) rows
+constexpr int kStageAll = 2 * kStageBytes + 2 * kKvRows * 4;  // Q, dO, lse, D of one step
+constexpr int kStages = 4;                     // LDS ring: steps s+1..s+3 stream in during step s
+
+// HBM -> LDS copy of 4 bytes per lane (lane l writes lds_dst + 4l).
+__device__ __forceinline__ void copy_dword_to_lds(const void *src, uint8_t *lds_dst) {
+    const uint32_t m0 = (uint32_t)reinterpret_cast<uintptr_t>((lds_void *)lds_dst);
+    asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(m0) : "memory");
+}
+
+// Wait until at most n (<= 31) of this wave's copies are outstanding.
+__device__ __forceinline__ void wait_copies32(int n) {
+#define MSA_W(i) case i: asm volatile("s_waitcnt vmcnt(" #i ")" ::: "memory"); break;
+    switch (n) {
+        MSA_W(1) MSA_W(2) MSA_W(3) MSA_W(4) MSA_W(5) MSA_W(6) MSA_W(7) MSA_W(8) MSA_W(9) MSA_W(10)
+        MSA_W(11) MSA_W(12) MSA_W(13) MSA_W(14) MSA_W(15) MSA_W(16) MSA_W(17) MSA_W(18) MSA_W(19)
+        MSA_W(20) MSA_W(21) MSA_W(22) MSA_W(23) MSA_W(24) MSA_W(25) MSA_W(26) MSA_W(27) MSA_W(28)
+        MSA_W(29) MSA_W(30) MSA_W(31)
+        default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    }
+#undef MSA_W
+}
 
 // Row r (0..63) of a staged Q / dO tile, chunk c at position c ^ swz16(r):
 // the 16 rows 16rt + m of a plain operand read map to 16 distinct
@@ -441,7 +471,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
     const int32_t *__restrict__ lists, const int32_t *__restrict__ list_off,
     const int32_t *__restrict__ chunk_off, int nlists, float scale, float scale_log2,
     float *__restrict__ part, uint16_t *__restrict__ dk, uint16_t *__restrict__ dv) {
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * 2 * kStageBytes];  // 2 stages x (Q, dO)
+    extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];  // kStages x (Q, dO, lse, D)
     const int ci = blockIdx.x;
     if (ci >= chunk_off[nlists]) return;
     int lo = 0, hi = nlists - 1;  // list li: the last with chunk_off[li] <= ci
@@ -474,6 +504,12 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
             vreg[kt][ks] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(v + row + 8 * (4 * ks + grp)));
         }
     }
+    // use the operands once here, so that the compiler's wait for them sits
+    // before the step loop (a wait inside it would also drain the prefetch)
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) asm volatile("" ::"v"(kreg[kt][ks]), "v"(vreg[kt][ks]));
     f32x4 dkt[2][8], dvt[2][8];  // [key tile][d tile]: key 16kt + n, d 16dt + 4grp + i
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
@@ -482,9 +518,14 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
 
     // Stage s: tokens e0 + 4s .. +3 (past the list end: its last token,
     // masked).  32 one-KiB copies (16 of Q, 16 of dO rows), 8 per wave;
-    // copy cc fills rows 4cc..4cc+3 = heads 4(cc%4).. of token cc/4.
+    // copy cc fills rows 4cc..4cc+3 = heads 4(cc%4).. of token cc/4.  Wave 0
+    // also copies the 4 tokens' lse rows, wave 1 their D rows (64 floats,
+    // [token][head]), so that the step loop issues no vector load of its own
+    // (the compiler would wait for it, and with it for the whole prefetch).
     const int nsteps = (ne + kKvTok - 1) / kKvTok;
+    const int per_stage = 8 + (wave < 2 ? 1 : 0);
     auto issue_stage = [&](int s, int buf) {
+        uint8_t *st = smem + buf * kStageAll;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int c = 8 * wave + j;
@@ -494,7 +535,16 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
             const int ch = (lane & 15) ^ swz16(r);
             const uint16_t *src =
                 (c < 16 ? q : dout) + (size_t(tok) * kHeads + g * kGroup + (r & 15)) * kDim + 8 * ch;
-            copy_to_lds(src, smem + buf * 2 * kStageBytes + (c < 16 ? 0 : kStageBytes) + cc * 1024);
+            copy_to_lds(src, st + (c < 16 ? 0 : kStageBytes) + cc * 1024);
+        }
+        if (wave < 2) {
+            int t4[kKvTok];  // wave-uniform (scalar) loads; the lane picks its token
+#pragma unroll
+            for (int j = 0; j < kKvTok; ++j) t4[j] = lists[e0 + min(kKvTok * s + j, ne - 1)];
+            const int tj = lane >> 4;
+            const int tok = tj == 0 ? t4[0] : tj == 1 ? t4[1] : tj == 2 ? t4[2] : t4[3];
+            const float *src = (wave == 0 ? lse : Dsum) + size_t(tok) * kHeads + g * kGroup + (lane & 15);
+            copy_dword_to_lds(src, st + 2 * kStageBytes + wave * (kKvRows * 4));
         }
     };
 
@@ -511,18 +561,19 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
     }
     const int tr_lo = (n & 1) * 8;
 
-    issue_stage(0, 0);
+    // queries' operands are in registers before the first copy is issued
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+    for (int s = 0; s < min(nsteps, kStages - 1); ++s) issue_stage(s, s);
     for (int s = 0; s < nsteps; ++s) {
-        const int buf = s & 1;
-        if (s + 1 < nsteps) {
-            issue_stage(s + 1, buf ^ 1);
-            wait_copies(8);
-        } else {
-            wait_copies(0);
-        }
+        const int buf = s % kStages;
+        if (s + kStages - 1 < nsteps) issue_stage(s + kStages - 1, (s + kStages - 1) % kStages);
+        // copies complete in issue order: leave the later stages in flight
+        wait_copies32(per_stage * (min(nsteps - 1, s + kStages - 1) - s));
         barrier_keep_prefetch();
-        const uint8_t *Qs = smem + buf * 2 * kStageBytes;
+        const uint8_t *Qs = smem + buf * kStageAll;
         const uint8_t *Ds = Qs + kStageBytes;
+        const float *Ls = (const float *)(Qs + 2 * kStageBytes);
+        const float *Dl = Ls + kKvRows;
 
         // per row tile rt (token 4s + rt): heads 4grp + i
         float lse2[4][4], dsum[4][4];
@@ -532,9 +583,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
             const int e = kKvTok * s + rt;
             const int tok = lists[e0 + min(e, ne - 1)];
             pos[rt] = e < ne ? tok - doc.start : -1;  // -1: no key passes the mask
-            const size_t base = size_t(tok) * kHeads + g * kGroup + 4 * grp;
-            const f32x4 l4 = *(const f32x4 *)(lse + base);
-            const f32x4 d4 = *(const f32x4 *)(Dsum + base);
+            const f32x4 l4 = *(const f32x4 *)(Ls + 16 * rt + 4 * grp);
+            const f32x4 d4 = *(const f32x4 *)(Dl + 16 * rt + 4 * grp);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 lse2[rt][i] = l4[i] * kLog2e;
@@ -711,7 +761,8 @@ hipError_t launch_bwd_dkdv(const uint16_t *q, const uint16_t *k, const uint16_t 
                            const int32_t *blk_off, int ndocs, const BwdLayout &L, const int32_t *lists,
                            const int32_t *list_off, const int32_t *chunk_off, float scale, float *part,
                            uint16_t *dk, uint16_t *dv, hipStream_t stream) {
-    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(L.max_chunks), dim3(256), 0, stream, q, k, v, dout, lse, Dsum,
+    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(L.max_chunks), dim3(256), size_t(kStages) * kStageAll, stream,
+                       q, k, v, dout, lse, Dsum,
                        docs, blk_off, ndocs, L.nb_max, lists, list_off, chunk_off, L.nlists, scale,
                        scale * kLog2e, part, dk, dv);
     return hipGetLastError();
