@@ -13,12 +13,13 @@
 //       largest score found by bisection on order-preserving score bits with
 //       wave-wide counts, then an ascending ballot-compacted emit (ties go
 //       to the lower block id); forced init/local blocks always emitted.
-//   decode_attend_kernel - one workgroup per (selected block, KV head,
-//       request); 4 waves x 32 keys: S^T = K Q^T and O^T = V^T P^T on MFMA
-//       16x16x32 (16 query heads = N), partial softmax merged across waves in
-//       LDS, one (O, m, l) partial per selected block written to workspace.
+//   decode_attend_kernel - one workgroup per 4 selected blocks of a (KV
+//       head, request); 4 waves x 32 keys per block: S^T = K Q^T and
+//       O^T = V^T P^T on MFMA 16x16x32 (16 query heads = N); the 16 wave
+//       partials merged in LDS in fixed order, one (O, m, l) partial per
+//       workgroup written to workspace.
 //   decode_combine_kernel - per (request, KV head): log-sum-exp merge of the
-//       topk partials in fixed block order, bf16 output (or, for the MXFP8
+//       ceil(topk/4) partials in fixed order, bf16 output (or, for the MXFP8
 //       variant, that bf16 output encoded as E4M3 + E8M0 per 32 values).
 #include "msa_internal.hpp"
 #include "mxfp8.hpp"
@@ -28,6 +29,7 @@ namespace msa {
 namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kDecPagesPerWg = 4;
+constexpr int kDecBlocksPerWg = 4;  // selected blocks per attention workgroup (4 waves each)
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -240,40 +242,50 @@ __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, kHi));
 }
 
-// Workgroup (s, g, r): selected block s of KV head g for request r; 4 waves,
-// wave w owns keys 32w..32w+31 of the block.
+// Workgroup (sg, g, r): selected blocks kBpw*sg .. kBpw*sg + kBpw-1 of KV
+// head g for request r; 4 waves per block, wave w owns keys 32(w%4)..+31 of
+// block w/4.
 //   S^T[32 keys x 16 heads] = K . Q^T   (MFMA 16x16x32, K straight from HBM)
 //   per-wave softmax partial, V rows copied HBM -> LDS (global_load_lds),
-//   O^T[128 x 16] = V^T . P^T with V^T from ds_read_b64_tr_b16,
-//   the 4 waves merged in LDS into one (O, m, l) partial of the block.
+//   O^T[128 x 16] = V^T . P^T with V^T from ds_read_b64_tr_b16;
+//   a wave whose slot is unselected (-1 or past the query block) holds an
+//   empty partial; the 4*kBpw waves are merged in LDS, in wave order, into
+//   one (O, m, l) partial of the workgroup.
 // kFp8Kv: K/V caches hold E4M3FN bytes.  E4M3 values are exact in bf16, so
 // K and V are converted exactly (V into the bf16 LDS layout of the other
 // variant); the K scale is folded into scale_log2 by the caller and the V
 // scale multiplies the block's partial O.
-template <bool kFp8Kv>
-__global__ __launch_bounds__(256) void decode_attend_kernel(
+template <bool kFp8Kv, int kBpw>
+__global__ __launch_bounds__(256 * kBpw) void decode_attend_kernel(
     const uint16_t *__restrict__ q, const void *__restrict__ kc_, const void *__restrict__ vc_,
     const int32_t *__restrict__ pt, int max_pages, const int32_t *__restrict__ ctx, int max_ctx,
-    int B, const int32_t *__restrict__ q2k, int topk, float scale_log2, float v_scale,
+    int B, const int32_t *__restrict__ q2k, int topk, int nparts, float scale_log2, float v_scale,
     float *__restrict__ part_o, float *__restrict__ part_ml) {
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * kWaveVBytes];  // V, then O^T
-    __shared__ float s_m[4][16], s_l[4][16];
-    const int s = blockIdx.x, g = blockIdx.y, r = blockIdx.z;
+    extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];  // per wave: V rows, then O^T
+    __shared__ float s_m[4 * kBpw][16], s_l[4 * kBpw][16];
+    const int sg = blockIdx.x, g = blockIdx.y, r = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 15, qd = lane >> 4;
-    const size_t pidx = (size_t(r) * kKvHeads + g) * topk + s;
+    const int s = sg * kBpw + (wave >> 2);  // this wave's slot of the row
+    const int wq = wave & 3;                // its quarter (32 keys) of the block
+    const size_t pidx = (size_t(r) * kKvHeads + g) * nparts + sg;
     float *po = part_o + pidx * (kGroup * kDim);
     float *pml = part_ml + pidx * (kGroup * 2);
 
     const int L = min(max(ctx[r], 1), max_ctx);
     const int c = (L - 1) / kBlock;
-    const int b = q2k[(size_t(g) * B + r) * topk + s];
+    const int b = s < topk ? q2k[(size_t(g) * B + r) * topk + s] : -1;
+    uint8_t *vt = smem + wave * kWaveVBytes;
+    // this wave's partial over its 32 keys (empty when the slot is unselected)
+    float mloc = -INFINITY, psum = 0.f;
+    f32x4 oacc[8];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) oacc[dt] = f32x4{};
     if (b >= 0 && b <= c) {
         const size_t slot0 = size_t(pt[size_t(r) * max_pages + b]) * kBlock;
-        const int key0 = 32 * wave;
+        const int key0 = 32 * wq;
         const int kmax = L - 1 - b * kBlock;  // last valid key of the block
-        uint8_t *vt = smem + wave * kWaveVBytes;
 
         // V rows key0..key0+31 -> LDS; rows past L re-read the last valid row
         // (their probabilities are 0).
@@ -344,7 +356,6 @@ __global__ __launch_bounds__(256) void decode_attend_kernel(
         }
         // softmax over this wave's 32 keys for head column n (lane holds keys
         // 16mt + 4qd + i of its column)
-        float mloc = -INFINITY;
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -357,7 +368,6 @@ __global__ __launch_bounds__(256) void decode_attend_kernel(
         mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
         mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
         const float base = mloc == -INFINITY ? 0.f : mloc;
-        float psum = 0.f;
         bf16x8 pb;  // P^T operand: keys 4qd + e (tile 0) then 16 + 4qd + e (tile 1)
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
@@ -374,7 +384,6 @@ __global__ __launch_bounds__(256) void decode_attend_kernel(
         // O^T[d x heads] = V^T . P^T.  Transposing read: in lane group qd, lane
         // i supplies row (16h + 4qd + i/4), columns 16dt + 4(i%4)..+3, and
         // lane j receives V[row0 + e][16dt + j] for e = 0..3.
-        f32x4 oacc[8];
         const int gi = lane & 15;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
@@ -390,58 +399,56 @@ __global__ __launch_bounds__(256) void decode_attend_kernel(
             const i16x8 ab = {t[0][0], t[0][1], t[0][2], t[0][3], t[1][0], t[1][1], t[1][2], t[1][3]};
             oacc[dt] = mfma_16x16x32(__builtin_bit_cast(bf16x8, ab), pb, f32x4{});
         }
-        // wave partial O^T -> LDS (over this wave's own V rows, already consumed)
-        float *so = (float *)vt;  // [16 heads][128 d]
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+    // wave partial O^T -> LDS (over this wave's own V rows, already consumed)
+    float *so = (float *)vt;  // [16 heads][128 d]
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
+    for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) so[n * kDim + 16 * dt + 4 * qd + i] = oacc[dt][i];
-        if (qd == 0) {
-            s_m[wave][n] = mloc;
-            s_l[wave][n] = psum;
+        for (int i = 0; i < 4; ++i) so[n * kDim + 16 * dt + 4 * qd + i] = oacc[dt][i];
+    if (qd == 0) {
+        s_m[wave][n] = mloc;
+        s_l[wave][n] = psum;
+    }
+    __syncthreads();
+    if (tid >= 256) return;
+    // merge the workgroup's 4*kBpw waves (kBpw blocks) in wave order:
+    // thread -> (head hh, 8 d)
+    constexpr int kW = 4 * kBpw;
+    const int hh = tid >> 4, d0 = (tid & 15) * 8;
+    float mw[kW], M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kW; ++w) { mw[w] = s_m[w][hh]; M = fmaxf(M, mw[w]); }
+    const float baseM = M == -INFINITY ? 0.f : M;
+    float sc[kW], l = 0.f;
+#pragma unroll
+    for (int w = 0; w < kW; ++w) {
+        sc[w] = __builtin_amdgcn_exp2f(mw[w] - baseM);
+        l += sc[w] * s_l[w][hh];
+    }
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = 0.f;
+#pragma unroll
+    for (int w = 0; w < kW; ++w) {
+        const float *src = (const float *)(smem + w * kWaveVBytes) + hh * kDim + d0;
+        const f32x4 a = *(const f32x4 *)src, c4 = *(const f32x4 *)(src + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            o[e] += sc[w] * a[e];
+            o[4 + e] += sc[w] * c4[e];
         }
-        __syncthreads();
-        // merge the 4 waves: thread -> (head hh, 8 d)
-        const int hh = tid >> 4, d0 = (tid & 15) * 8;
-        float mw[4], M = -INFINITY;
+    }
+    if constexpr (kFp8Kv) {
 #pragma unroll
-        for (int w = 0; w < 4; ++w) { mw[w] = s_m[w][hh]; M = fmaxf(M, mw[w]); }
-        const float baseM = M == -INFINITY ? 0.f : M;
-        float sc[4], l = 0.f;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            sc[w] = __builtin_amdgcn_exp2f(mw[w] - baseM);
-            l += sc[w] * s_l[w][hh];
-        }
-        float o[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float acc = 0.f;
-#pragma unroll
-            for (int w = 0; w < 4; ++w)
-                acc += sc[w] * ((const float *)(smem + w * kWaveVBytes))[hh * kDim + d0 + e];
-            o[e] = acc;
-        }
-        if constexpr (kFp8Kv) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] *= v_scale;
-        }
-        *(f32x4 *)(po + hh * kDim + d0) = f32x4{o[0], o[1], o[2], o[3]};
-        *(f32x4 *)(po + hh * kDim + d0 + 4) = f32x4{o[4], o[5], o[6], o[7]};
-        if ((tid & 15) == 0) {
-            pml[2 * hh] = M;
-            pml[2 * hh + 1] = l;
-        }
-    } else {
-        // unselected slot: an empty partial (zero O, m = -inf, l = 0)
-        const int hh = tid >> 4, d0 = (tid & 15) * 8;
-        *(f32x4 *)(po + hh * kDim + d0) = f32x4{};
-        *(f32x4 *)(po + hh * kDim + d0 + 4) = f32x4{};
-        if (tid < kGroup) {
-            pml[2 * tid] = -INFINITY;
-            pml[2 * tid + 1] = 0.f;
-        }
+        for (int e = 0; e < 8; ++e) o[e] *= v_scale;
+    }
+    *(f32x4 *)(po + hh * kDim + d0) = f32x4{o[0], o[1], o[2], o[3]};
+    *(f32x4 *)(po + hh * kDim + d0 + 4) = f32x4{o[4], o[5], o[6], o[7]};
+    if ((tid & 15) == 0) {
+        pml[2 * hh] = M;
+        pml[2 * hh + 1] = l;
     }
 }
 
@@ -513,24 +520,33 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float *__restr
     }
 }
 
+// partials per (request, KV head): one per attention workgroup
+int decode_parts(int topk) { return ceil_div(topk, kDecBlocksPerWg); }
+
 hipError_t launch_decode_attend(const uint16_t *q, const void *kc, const void *vc, bool fp8kv, float k_scale,
                                 float v_scale, const int32_t *pt, int max_pages, const int32_t *ctx,
                                 int max_ctx, int B, const int32_t *q2k, int topk, float scale,
                                 float *partial, hipStream_t stream) {
+    const int nparts = decode_parts(topk);
     float *part_o = partial;
-    float *part_ml = partial + size_t(B) * kKvHeads * topk * kGroup * kDim;
-    const dim3 grid(topk, kKvHeads, B);
+    float *part_ml = partial + size_t(B) * kKvHeads * nparts * kGroup * kDim;
+    const dim3 grid(nparts, kKvHeads, B);
+    const float sl = scale * kLog2e * (fp8kv ? k_scale : 1.0f);
+    const float vs = fp8kv ? v_scale : 1.0f;
+    constexpr int N = kDecBlocksPerWg;
+    const size_t lds = size_t(4 * N) * kWaveVBytes;
     if (fp8kv)
-        hipLaunchKernelGGL(decode_attend_kernel<true>, grid, dim3(256), 0, stream, q, kc, vc, pt, max_pages,
-                           ctx, max_ctx, B, q2k, topk, scale * kLog2e * k_scale, v_scale, part_o, part_ml);
+        hipLaunchKernelGGL((decode_attend_kernel<true, N>), grid, dim3(256 * N), lds, stream, q, kc, vc, pt,
+                           max_pages, ctx, max_ctx, B, q2k, topk, nparts, sl, vs, part_o, part_ml);
     else
-        hipLaunchKernelGGL(decode_attend_kernel<false>, grid, dim3(256), 0, stream, q, kc, vc, pt, max_pages,
-                           ctx, max_ctx, B, q2k, topk, scale * kLog2e, 1.0f, part_o, part_ml);
+        hipLaunchKernelGGL((decode_attend_kernel<false, N>), grid, dim3(256 * N), lds, stream, q, kc, vc, pt,
+                           max_pages, ctx, max_ctx, B, q2k, topk, nparts, sl, vs, part_o, part_ml);
     return hipGetLastError();
 }
 
 hipError_t launch_decode_combine(const float *partial, int B, int topk, uint16_t *out, uint8_t *out_q,
                                  uint8_t *out_scale, hipStream_t stream) {
+    topk = decode_parts(topk);  // partials per (request, KV head)
     const float *part_o = partial;
     const float *part_ml = partial + size_t(B) * kKvHeads * topk * kGroup * kDim;
     if (out_q)
