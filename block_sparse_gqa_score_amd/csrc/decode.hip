@@ -28,20 +28,20 @@ namespace msa {
 
 namespace {
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kDecPagesPerWg = 4;
+constexpr int kDecPagesPerWg = 1;  // pages (one wave each) per score workgroup
 constexpr int kDecBlocksPerWg = 4;  // selected blocks per attention workgroup (4 waves each)
 }  // namespace
 
 // ---------------------------------------------------------------------------
 // G4: per-page index scores
 // ---------------------------------------------------------------------------
-template <bool kFp8>
-__global__ __launch_bounds__(256) void decode_scores_kernel(
+template <bool kFp8, int kPpw>  // kPpw pages (one wave each) per workgroup
+__global__ __launch_bounds__(64 * kPpw) void decode_scores_kernel(
     const uint8_t *__restrict__ iq, const uint8_t *__restrict__ ikc, const int32_t *__restrict__ pt,
     int max_pages, const int32_t *__restrict__ ctx, int max_ctx, int nb_max, float *__restrict__ S) {
     const int r = blockIdx.y;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int pi = blockIdx.x * kDecPagesPerWg + wave;
+    const int pi = blockIdx.x * kPpw + wave;
     // the page-table entry is fetched together with the context length (an
     // entry past the context is in bounds and simply unused)
     const int page = pt[size_t(r) * max_pages + min(pi, max_pages - 1)];
@@ -115,13 +115,17 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(
 hipError_t launch_decode_scores(const void *iq, const void *ikc, bool fp8, const int32_t *pt,
                                 int max_pages, const int32_t *ctx, int B, int max_ctx, int nb_max, float *S,
                                 hipStream_t stream) {
+    // one page per 64-thread workgroup: measured against 2, 4, 8 and 16 pages
+    // per workgroup, the finest grain spreads the uneven request lengths best
     const dim3 grid(ceil_div(nb_max, kDecPagesPerWg), B);
     if (fp8)
-        hipLaunchKernelGGL(decode_scores_kernel<true>, grid, dim3(256), 0, stream,
-                           (const uint8_t *)iq, (const uint8_t *)ikc, pt, max_pages, ctx, max_ctx, nb_max, S);
+        hipLaunchKernelGGL((decode_scores_kernel<true, kDecPagesPerWg>), grid, dim3(64 * kDecPagesPerWg), 0,
+                           stream, (const uint8_t *)iq, (const uint8_t *)ikc, pt, max_pages, ctx, max_ctx,
+                           nb_max, S);
     else
-        hipLaunchKernelGGL(decode_scores_kernel<false>, grid, dim3(256), 0, stream,
-                           (const uint8_t *)iq, (const uint8_t *)ikc, pt, max_pages, ctx, max_ctx, nb_max, S);
+        hipLaunchKernelGGL((decode_scores_kernel<false, kDecPagesPerWg>), grid, dim3(64 * kDecPagesPerWg), 0,
+                           stream, (const uint8_t *)iq, (const uint8_t *)ikc, pt, max_pages, ctx, max_ctx,
+                           nb_max, S);
     return hipGetLastError();
 }
 
