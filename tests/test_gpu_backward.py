@@ -177,3 +177,43 @@ def test_backward_full_size_32k_sampled():
         got = dv[:, g].sum(axis=0)
         assert np.all(np.abs(got - want) <= 2.0 ** -7 * np.abs(dv[:, g]).sum(axis=0) + 1e-6)
         assert np.all(np.abs(dk[:, g].sum(axis=0)) <= 2.0 ** -7 * np.abs(dk[:, g]).sum(axis=0) + 1e-6)
+
+
+def test_backward_packed_documents_sampled():
+    """The packed microbatch (2 x 16384 rows of log-uniform documents, init 1,
+    local 1, topk 16) on a synthetic selection: dq and lse on tokens spread
+    over every document, dk and dv on keys of the shortest document (the
+    oracle gets lse and D of all its tokens), and the whole-tensor sums."""
+    from parity import sample_tokens
+    print("[backward] packed documents", flush=True)
+    w = W.config(3)
+    rows = W.synthetic_q2k(3, w.cu_seqlens, 16, w.init_blocks, w.local_blocks)
+    dout = W.grad_out(3, w.T)
+    lse, dq, dk, dv = run_gpu(w, rows, dout)
+    cu = w.cu_seqlens
+    toks = sample_tokens(cu, per_doc=3, seed=4)
+    r_lse, _, r_dq = oracle.attend_backward_rows(w.q, w.k, w.v, dout, rows, cu, toks, w.scale)
+    assert np.abs(lse[toks] - r_lse).max() <= 1e-4
+    mx, mean = rel_errors(dq[toks], r_dq)
+    print(f"[backward] packed dq rows ({len(toks)}): max {mx:.3g} mean {mean:.3g}", flush=True)
+    assert mx <= MAX_REL and mean <= MEAN_REL
+    lens = np.diff(cu)
+    d = int(np.argmin(lens))
+    s, L = int(cu[d]), int(lens[d])
+    keys = (s + np.unique(np.array([0, 1, 127, 128, L // 2, L - 1]).clip(0, L - 1))).astype(np.int32)
+    users = np.arange(s, s + L, dtype=np.int32)
+    u_lse, u_D, _ = oracle.attend_backward_rows(w.q, w.k, w.v, dout, rows, cu, users, w.scale)
+    lse_full = np.full((w.T, 64), np.nan)
+    D_full = np.full((w.T, 64), np.nan)
+    lse_full[users], D_full[users] = u_lse, u_D
+    r_dk, r_dv = oracle.attend_backward_keys(w.q, w.k, w.v, dout, rows, cu, lse_full, D_full, keys, w.scale)
+    for nm, g_, r_ in (("dk", dk[keys], r_dk), ("dv", dv[keys], r_dv)):
+        mx, mean = rel_errors(g_, r_)
+        print(f"[backward] packed {nm} keys: max {mx:.3g} mean {mean:.3g}", flush=True)
+        assert mx <= MAX_REL and mean <= MEAN_REL
+    dO = torch.from_numpy(dout.view(np.int16)).view(torch.bfloat16).double().numpy()
+    for g in range(4):
+        want = dO[:, 16 * g:16 * g + 16].sum(axis=(0, 1))
+        got = dv[:, g].sum(axis=0)
+        assert np.all(np.abs(got - want) <= 2.0 ** -7 * np.abs(dv[:, g]).sum(axis=0) + 1e-6)
+        assert np.all(np.abs(dk[:, g].sum(axis=0)) <= 2.0 ** -7 * np.abs(dk[:, g]).sum(axis=0) + 1e-6)
