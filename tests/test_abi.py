@@ -223,3 +223,43 @@ def _decode_fp8kv(**kw):
 def test_decode_fp8kv_rejects(kw, status, needle):
     assert _decode_fp8kv(**kw) == status
     assert needle in msa.lib().msa_last_error().decode()
+
+
+def test_prefill_lse_rejects_null_lse():
+    st = msa.lib().msa_sparse_attend_prefill_lse(FAKE, FAKE, FAKE, FAKE, 16, FAKE, 1, 256, 256, 0.088, FAKE,
+                                                 None, FAKE, 1 << 40, None)
+    assert st == 1 and "lse" in msa.lib().msa_last_error().decode()
+
+
+def _backward(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=FAKE, dout=FAKE, q2k=FAKE, topk=16, cu=FAKE, ndocs=1,
+             T=256, max_seqlen=256, scale=0.088, dq=FAKE, dk=FAKE, dv=FAKE, ws=FAKE, ws_bytes=1 << 40)
+    a.update(kw)
+    return msa.lib().msa_sparse_attend_prefill_backward(
+        a["q"], a["k"], a["v"], a["out"], a["lse"], a["dout"], a["q2k"], a["topk"], a["cu"], a["ndocs"],
+        a["T"], a["max_seqlen"], a["scale"], a["dq"], a["dk"], a["dv"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(lse=None), 1, "non-NULL"),
+    (dict(dout=None), 1, "non-NULL"),
+    (dict(dv=None), 1, "non-NULL"),
+    (dict(topk=17), 2, "topk"),
+    (dict(ndocs=0), 1, "num_docs"),
+    (dict(T=(1 << 22) + 1, max_seqlen=1000), 2, "total_tokens"),
+    (dict(scale=-1.0), 1, "softmax_scale"),
+    (dict(ws_bytes=1000), 3, "workspace"),
+])
+def test_backward_rejects(kw, status, needle):
+    assert _backward(**kw) == status
+    assert needle in msa.lib().msa_last_error().decode()
+
+
+def test_backward_workspace_bytes():
+    T, D = 32768, 1
+    ws = msa.prefill_backward_workspace_bytes(T, D, T, 16)
+    # at least: D [T,64] fp32 and the block lists (4*T*topk int32)
+    assert ws >= T * 64 * 4 + 4 * T * 16 * 4 and ws % 256 == 0
+    assert msa.prefill_backward_workspace_bytes(T, D, T, 17) == 0
+    assert msa.prefill_backward_workspace_bytes((1 << 22) + 1, 1, 100, 16) == 0
+    assert msa.prefill_backward_workspace_bytes(0, 1, 1, 16) == 0
