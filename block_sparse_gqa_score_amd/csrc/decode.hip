@@ -457,6 +457,206 @@ __global__ __launch_bounds__(256 * kBpw) void decode_attend_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// G6, bf16 caches: streaming attention, one workgroup per 8 slots of a row
+// ---------------------------------------------------------------------------
+namespace {
+constexpr int kStreamSlots = 8;                    // selected slots per workgroup
+constexpr int kStreamStage = 2 * kWaveVBytes;      // one wave's K rows + V rows of one block (16 KiB)
+constexpr int kStreamWaveBytes = 2 * kStreamStage; // two stages per wave (32 KiB)
+
+// HBM -> LDS copy of 16 bytes per lane (lane l writes lds_dst + 16l), from
+// asm so that the compiler does not wait for it before unrelated LDS reads;
+// completion is awaited with explicit vmcnt.
+__device__ __forceinline__ void stream_copy(const void *src, uint8_t *lds_dst) {
+    const uint32_t m0 = (uint32_t)reinterpret_cast<uintptr_t>((lds_void *)lds_dst);
+    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0) : "memory");
+}
+}  // namespace
+
+// Workgroup (sg, g, r): slots 8sg .. 8sg+7 of row (KV head g, request r);
+// 4 waves, wave w owns keys 32w..32w+31 of every selected block.  Each wave
+// streams its K and V rows of the next block into its own 2-stage LDS ring
+// while it computes the current one (no workgroup barrier until the end):
+//   S^T[32 x 16] = K . Q^T   (K rows read from LDS as the MFMA A operand),
+//   an online softmax across the blocks, O^T += V^T . P^T (V^T by
+//   transposing LDS reads); the 4 waves' partials are merged at the end
+//   into one (O, m, l) partial of the workgroup.
+// Both row buffers keep 16-byte chunk c of row rr at position c ^ (rr & 15).
+__global__ __launch_bounds__(256) void decode_attend_stream_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc, const uint16_t *__restrict__ vc,
+    const int32_t *__restrict__ pt, int max_pages, const int32_t *__restrict__ ctx, int max_ctx, int B,
+    const int32_t *__restrict__ q2k, int topk, int nparts, float scale_log2, float *__restrict__ part_o,
+    float *__restrict__ part_ml) {
+    extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];  // 4 waves x 2 stages x (K, V)
+    __shared__ float s_m[4][16], s_l[4][16];
+    const int sg = blockIdx.x, g = blockIdx.y, r = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 15, qd = lane >> 4;
+    const int L = min(max(ctx[r], 1), max_ctx);
+    const int c = (L - 1) / kBlock;
+    const int key0 = 32 * wave;
+    uint8_t *ring = smem + wave * kStreamWaveBytes;
+
+    // the workgroup's slots (wave-uniform): block id, or -1 when unselected
+    int bsel[kStreamSlots];
+#pragma unroll
+    for (int j = 0; j < kStreamSlots; ++j) {
+        const int s = sg * kStreamSlots + j;
+        const int b = s < topk ? q2k[(size_t(g) * B + r) * topk + s] : -1;
+        bsel[j] = (b >= 0 && b <= c) ? b : -1;
+    }
+    // copies of slot j into stage st: K rows key0..key0+31 (8 one-KiB copies)
+    // then V rows (8); rows past L re-read the last valid row (masked)
+    auto issue = [&](int j, int st) {
+        const int b = bsel[j];
+        const size_t slot0 = size_t(pt[size_t(r) * max_pages + b]) * kBlock;
+        const int kmax = L - 1 - b * kBlock;
+        uint8_t *kb = ring + st * kStreamStage;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int rr = 4 * i + (lane >> 4);
+            const int chunk = (lane & 15) ^ vswz(rr);
+            const size_t row = ((slot0 + min(key0 + rr, kmax)) * kKvHeads + g) * kDim + 8 * chunk;
+            stream_copy(kc + row, kb + i * 1024);
+            stream_copy(vc + row, kb + kWaveVBytes + i * 1024);
+        }
+    };
+
+    // Q^T operand: lane (n = head, qd), step ks: 16-byte chunk 4ks + qd
+    const uint16_t *qrow = q + (size_t(r) * kHeads + g * kGroup + n) * kDim;
+    bf16x8 qb[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qb[ks] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qrow + 8 * (4 * ks + qd)));
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): q is in before any copy is issued
+
+    float m_run = -INFINITY, l_run = 0.f;  // per head column n (log2 domain)
+    f32x4 oacc[8];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) oacc[dt] = f32x4{};
+    const int gi = lane & 15;
+    if (bsel[0] >= 0) issue(0, 0);
+#pragma unroll
+    for (int j = 0; j < kStreamSlots; ++j) {
+        const bool next = j + 1 < kStreamSlots && bsel[j + 1] >= 0;
+        if (next) {
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // stage (j+1)&1 was last read at slot j-1
+            issue(j + 1, (j + 1) & 1);
+        }
+        if (bsel[j] < 0) continue;
+        if (next) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");  // slot j's 16 copies have landed
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        const uint8_t *kb = ring + (j & 1) * kStreamStage;
+        const uint8_t *vt = kb + kWaveVBytes;
+        const int kmax = L - 1 - bsel[j] * kBlock;
+        // S^T: M-tile mt = keys key0 + 16mt + m (row 16mt + m of the buffer)
+        f32x4 sacc[2];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            sacc[mt] = f32x4{};
+            const int rr = 16 * mt + n;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const bf16x8 ka = __builtin_bit_cast(
+                    bf16x8, *(const u32x4 *)(kb + rr * kRowB + (((4 * ks + qd) ^ vswz(rr)) << 4)));
+                sacc[mt] = mfma_16x16x32(ka, qb[ks], sacc[mt]);
+            }
+        }
+        // online softmax over this block's keys 16mt + 4qd + i for head n
+        float mloc = -INFINITY;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool ok = key0 + 16 * mt + 4 * qd + i <= kmax;
+                const float z = ok ? sacc[mt][i] * scale_log2 : -INFINITY;
+                sacc[mt][i] = z;
+                mloc = fmaxf(mloc, z);
+            }
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+        const float m_new = fmaxf(m_run, mloc);
+        const float base = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - base);  // 0 while m_run is -inf
+        float psum = 0.f;
+        bf16x8 pb;  // P^T operand: keys 4qd + e (tile 0) then 16 + 4qd + e (tile 1)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float pv = __builtin_amdgcn_exp2f(sacc[mt][i] - base);
+                psum += pv;
+                pb[4 * mt + i] = (__bf16)pv;
+            }
+        psum += __shfl_xor(psum, 16);
+        psum += __shfl_xor(psum, 32);
+        l_run = l_run * alpha + psum;
+        m_run = m_new;
+        // O^T = alpha O^T + V^T . P^T (transposing reads as in the one-block kernel)
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+            i16x4 t[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int rr = 16 * h + 4 * qd + (gi >> 2);
+                const int col = 16 * dt + 4 * (gi & 3);
+                const int pos = ((col >> 3) ^ vswz(rr)) << 4;
+                t[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_i16x4 *)(vt + rr * kRowB + pos + ((col & 7) << 1)));
+            }
+            const i16x8 ab = {t[0][0], t[0][1], t[0][2], t[0][3], t[1][0], t[1][1], t[1][2], t[1][3]};
+            oacc[dt] = mfma_16x16x32(__builtin_bit_cast(bf16x8, ab), pb, oacc[dt] * alpha);
+        }
+    }
+    // wave partial O^T -> LDS (stage 0 of the wave's own ring, no longer read)
+    float *so = (float *)ring;  // [16 heads][128 d]
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) so[n * kDim + 16 * dt + 4 * qd + i] = oacc[dt][i];
+    if (qd == 0) {
+        s_m[wave][n] = m_run;
+        s_l[wave][n] = l_run;
+    }
+    __syncthreads();
+    // merge the 4 waves: thread -> (head hh, 8 d)
+    const int hh = tid >> 4, d0 = (tid & 15) * 8;
+    float mw[4], M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) { mw[w] = s_m[w][hh]; M = fmaxf(M, mw[w]); }
+    const float baseM = M == -INFINITY ? 0.f : M;
+    float sc[4], l = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        sc[w] = __builtin_amdgcn_exp2f(mw[w] - baseM);
+        l += sc[w] * s_l[w][hh];
+    }
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const float *src = (const float *)(smem + w * kStreamWaveBytes) + hh * kDim + d0;
+        const f32x4 a = *(const f32x4 *)src, c4 = *(const f32x4 *)(src + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            o[e] += sc[w] * a[e];
+            o[4 + e] += sc[w] * c4[e];
+        }
+    }
+    const size_t pidx = (size_t(r) * kKvHeads + g) * nparts + sg;
+    float *po = part_o + pidx * (kGroup * kDim);
+    float *pml = part_ml + pidx * (kGroup * 2);
+    *(f32x4 *)(po + hh * kDim + d0) = f32x4{o[0], o[1], o[2], o[3]};
+    *(f32x4 *)(po + hh * kDim + d0 + 4) = f32x4{o[4], o[5], o[6], o[7]};
+    if ((tid & 15) == 0) {
+        pml[2 * hh] = M;
+        pml[2 * hh + 1] = l;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // G7: merge the topk partials of each (request, KV head) in fixed block order
 // ---------------------------------------------------------------------------
 // One 64-thread workgroup per (d quarter, KV head, request): thread ->
@@ -524,17 +724,24 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float *__restr
     }
 }
 
-// partials per (request, KV head): one per attention workgroup
-int decode_parts(int topk) { return ceil_div(topk, kDecBlocksPerWg); }
+// partials per (request, KV head): one per attention workgroup (8 slots per
+// workgroup for bf16 caches, 4 for E4M3 caches)
+int decode_parts(int topk, bool fp8kv) { return ceil_div(topk, fp8kv ? kDecBlocksPerWg : kStreamSlots); }
 
 hipError_t launch_decode_attend(const uint16_t *q, const void *kc, const void *vc, bool fp8kv, float k_scale,
                                 float v_scale, const int32_t *pt, int max_pages, const int32_t *ctx,
                                 int max_ctx, int B, const int32_t *q2k, int topk, float scale,
                                 float *partial, hipStream_t stream) {
-    const int nparts = decode_parts(topk);
+    const int nparts = decode_parts(topk, fp8kv);
     float *part_o = partial;
     float *part_ml = partial + size_t(B) * kKvHeads * nparts * kGroup * kDim;
     const dim3 grid(nparts, kKvHeads, B);
+    if (!fp8kv) {
+        hipLaunchKernelGGL(decode_attend_stream_kernel, grid, dim3(256), size_t(4) * kStreamWaveBytes, stream, q,
+                           (const uint16_t *)kc, (const uint16_t *)vc, pt, max_pages, ctx, max_ctx, B, q2k, topk,
+                           nparts, scale * kLog2e, part_o, part_ml);
+        return hipGetLastError();
+    }
     const float sl = scale * kLog2e * (fp8kv ? k_scale : 1.0f);
     const float vs = fp8kv ? v_scale : 1.0f;
     constexpr int N = kDecBlocksPerWg;
@@ -548,9 +755,9 @@ hipError_t launch_decode_attend(const uint16_t *q, const void *kc, const void *v
     return hipGetLastError();
 }
 
-hipError_t launch_decode_combine(const float *partial, int B, int topk, uint16_t *out, uint8_t *out_q,
-                                 uint8_t *out_scale, hipStream_t stream) {
-    topk = decode_parts(topk);  // partials per (request, KV head)
+hipError_t launch_decode_combine(const float *partial, int B, int topk, bool fp8kv, uint16_t *out,
+                                 uint8_t *out_q, uint8_t *out_scale, hipStream_t stream) {
+    topk = decode_parts(topk, fp8kv);  // partials per (request, KV head)
     const float *part_o = partial;
     const float *part_ml = partial + size_t(B) * kKvHeads * topk * kGroup * kDim;
     if (out_q)

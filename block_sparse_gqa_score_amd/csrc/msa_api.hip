@@ -418,7 +418,7 @@ static msa_status decode_paged_impl(
                              context_lens, max_context_len, batch, q2k, topk, softmax_scale, part, s);
     if (e != hipSuccess) return hip_fail(e, "decode_attend");
     tm.mark(s, "decode_combine");
-    e = launch_decode_combine(part, batch, topk, out, out_q, out_scale, s);
+    e = launch_decode_combine(part, batch, topk, kv_fp8, out, out_q, out_scale, s);
     if (e != hipSuccess) return hip_fail(e, "decode_combine");
     tm.mark(s, nullptr);
     return MSA_OK;

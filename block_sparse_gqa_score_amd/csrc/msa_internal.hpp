@@ -86,8 +86,8 @@ hipError_t launch_decode_attend(const uint16_t *q, const void *kc, const void *v
                                 float *partial, hipStream_t stream);
 // bf16 output, or (out_q != NULL) its MXFP8 encoding: E4M3 [B, 64*128] and
 // E8M0 scales [B, 64*128/32].
-hipError_t launch_decode_combine(const float *partial, int B, int topk, uint16_t *out, uint8_t *out_q,
-                                 uint8_t *out_scale, hipStream_t stream);
+hipError_t launch_decode_combine(const float *partial, int B, int topk, bool fp8kv, uint16_t *out,
+                                 uint8_t *out_q, uint8_t *out_scale, hipStream_t stream);
 
 // Paged-cache insertion of n tokens' K, V and index-K rows (index-K stored
 // as bf16, or as unscaled E4M3 when fp8).
