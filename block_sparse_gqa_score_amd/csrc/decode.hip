@@ -112,6 +112,124 @@ __global__ __launch_bounds__(64 * kPpw) void decode_scores_kernel(
     if (qd == 0 && n < kIdxHeads) S[(size_t(r) * kIdxHeads + n) * nb_max + pi] = mx;
 }
 
+// Streaming variant for bf16 index keys: kScoreWaves persistent one-wave
+// workgroups share the flattened list of pages of all requests, each taking
+// an equal contiguous range of whole pages.  A page is contracted as two
+// half pages (64 keys); the wave double-buffers half pages in registers (the
+// next one loads while the current one is contracted) and stores the page's
+// scores after its second half.
+namespace {
+constexpr int kScoreWaves = 2048;
+
+struct HalfPage {
+    u32x4 k[4][4];  // [M-tile][k-step]: keys 16mt + n of the half page, chunk 4ks + qd
+};
+
+__device__ __forceinline__ int pages_of(const int32_t *ctx, int r, int max_ctx) {
+    return (min(max(ctx[r], 1), max_ctx) + kBlock - 1) / kBlock;
+}
+}  // namespace
+
+__global__ __launch_bounds__(64) void decode_scores_stream_kernel(
+    const uint16_t *__restrict__ iq, const uint16_t *__restrict__ ikc, const int32_t *__restrict__ pt,
+    int max_pages, const int32_t *__restrict__ ctx, int max_ctx, int B, int nb_max, float *__restrict__ S) {
+    const int lane = threadIdx.x;
+    const int n = lane & 15, qd = lane >> 4;
+    // total pages (a wave scan per 64 requests) and this wave's page range [p0, p1)
+    int total = 0;
+    for (int base = 0; base < B; base += 64) {
+        int x = base + lane < B ? pages_of(ctx, base + lane, max_ctx) : 0;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+        total += x;
+    }
+    const int wid = blockIdx.x;
+    const int p0 = int((int64_t(total) * wid) / kScoreWaves);
+    const int p1 = int((int64_t(total) * (wid + 1)) / kScoreWaves);
+    if (p0 >= p1) return;
+    // request r holding global page p0, and p0's page index within it
+    int r = 0, before = 0;
+    for (int base = 0; base < B; base += 64) {
+        const int rr = base + lane;
+        const int cnt = rr < B ? pages_of(ctx, rr, max_ctx) : 0;
+        int x = cnt;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(x, o);
+            if (lane >= o) x += y;
+        }
+        const int excl = before + x - cnt;  // pages before request rr
+        const uint64_t m = __ballot(rr < B && excl <= p0 && p0 < excl + cnt);
+        if (m) {
+            const int src = __ffsll((long long)m) - 1;
+            r = base + src;
+            before = __shfl(excl, src);
+            break;
+        }
+        before += __shfl(x, 63);
+    }
+    int Lr = min(max(ctx[r], 1), max_ctx);
+    int npr = (Lr + kBlock - 1) / kBlock;
+
+    auto load_q = [&](int rr, bf16x8 (&qb)[4]) {
+        const uint16_t *qrow = iq + (size_t(rr) * kIdxHeads + (n & 3)) * kDim;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            qb[ks] = n < kIdxHeads ? __builtin_bit_cast(bf16x8, *(const u32x4 *)(qrow + 8 * (4 * ks + qd)))
+                                   : bf16x8{};
+    };
+    auto load_half = [&](int rr, int pg, int half, HalfPage &h) {
+        const int page = pt[size_t(rr) * max_pages + pg];
+        const uint16_t *kbase = ikc + (size_t(page) * kBlock + 64 * half) * kDim;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                h.k[mt][ks] = *(const u32x4 *)(kbase + (16 * mt + n) * kDim + 8 * (4 * ks + qd));
+    };
+    // max over the half page's keys < L for index head column n
+    auto half_max = [&](const HalfPage &h, const bf16x8 (&qb)[4], int pg, int half, int L) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            f32x4 acc = f32x4{};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) acc = mfma_16x16x32(__builtin_bit_cast(bf16x8, h.k[mt][ks]), qb[ks], acc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int j = pg * kBlock + 64 * half + 16 * mt + 4 * qd + i;
+                mx = fmaxf(mx, j < L ? acc[i] : -INFINITY);
+            }
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        return fmaxf(mx, __shfl_xor(mx, 32));
+    };
+
+    bf16x8 qb[4];
+    load_q(r, qb);
+    int pg = p0 - before;  // page of request r
+    HalfPage h0, h1;
+    load_half(r, pg, 0, h0);
+    for (int p = p0; p < p1; ++p) {
+        // first half (in h0); the second half loads meanwhile
+        load_half(r, pg, 1, h1);
+        float pmax = half_max(h0, qb, pg, 0, Lr);
+        // next page's first half loads while the second half is contracted
+        int rn = r, pgn = pg + 1;
+        if (pgn == npr) { rn = r + 1; pgn = 0; }
+        if (p + 1 < p1) load_half(rn, pgn, 0, h0);
+        pmax = fmaxf(pmax, half_max(h1, qb, pg, 1, Lr));
+        if (qd == 0 && n < kIdxHeads) S[(size_t(r) * kIdxHeads + n) * nb_max + pg] = pmax;
+        if (rn != r && p + 1 < p1) {
+            r = rn;
+            Lr = min(max(ctx[r], 1), max_ctx);
+            npr = (Lr + kBlock - 1) / kBlock;
+            load_q(r, qb);
+        }
+        pg = pgn;
+    }
+}
+
 hipError_t launch_decode_scores(const void *iq, const void *ikc, bool fp8, const int32_t *pt,
                                 int max_pages, const int32_t *ctx, int B, int max_ctx, int nb_max, float *S,
                                 hipStream_t stream) {
@@ -123,9 +241,9 @@ hipError_t launch_decode_scores(const void *iq, const void *ikc, bool fp8, const
                            stream, (const uint8_t *)iq, (const uint8_t *)ikc, pt, max_pages, ctx, max_ctx,
                            nb_max, S);
     else
-        hipLaunchKernelGGL((decode_scores_kernel<false, kDecPagesPerWg>), grid, dim3(64 * kDecPagesPerWg), 0,
-                           stream, (const uint8_t *)iq, (const uint8_t *)ikc, pt, max_pages, ctx, max_ctx,
-                           nb_max, S);
+        hipLaunchKernelGGL(decode_scores_stream_kernel, dim3(kScoreWaves), dim3(64), 0, stream,
+                           (const uint16_t *)iq, (const uint16_t *)ikc, pt, max_pages, ctx, max_ctx, B, nb_max,
+                           S);
     return hipGetLastError();
 }
 
