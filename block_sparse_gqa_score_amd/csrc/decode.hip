@@ -6,20 +6,24 @@
 // position L-1; logical key j lives in slot pt[r, j/128]*128 + j%128.
 //
 // Kernels (one pass over the caches, HBM-bound):
-//   decode_scores_kernel - one wave per (request, page): the page's 128
-//       index keys against the 4 index heads on MFMA (bf16 16x16x32, or E4M3
-//       16x16x128 with unit scales), slots >= L masked, per-page max.
+//   decode_scores_stream_kernel - bf16 index keys: persistent one-wave
+//       workgroups over equal ranges of the flattened page list, half pages
+//       double-buffered in registers, MFMA 16x16x32 against the 4 index
+//       heads, slots >= L masked, per-page max.
+//   decode_scores_kernel - E4M3 index keys: one wave per (request, page),
+//       MFMA 16x16x128 with unit scales.
 //   decode_topk_kernel   - one wave per (request, index head): the R-th
 //       largest score found by bisection on order-preserving score bits with
 //       wave-wide counts, then an ascending ballot-compacted emit (ties go
 //       to the lower block id); forced init/local blocks always emitted.
-//   decode_attend_kernel - one workgroup per 4 selected blocks of a (KV
-//       head, request); 4 waves x 32 keys per block: S^T = K Q^T and
-//       O^T = V^T P^T on MFMA 16x16x32 (16 query heads = N); the 16 wave
-//       partials merged in LDS in fixed order, one (O, m, l) partial per
-//       workgroup written to workspace.
+//   decode_attend_stream_kernel - one workgroup per 8 selected slots of a
+//       (KV head, request); each wave streams its 32 keys of the next block
+//       through its own LDS ring while computing the current one: S^T = K Q^T
+//       and O^T = V^T P^T on MFMA 16x16x32 (16 query heads = N), an online
+//       softmax across the blocks, the 4 waves merged in LDS into one
+//       (O, m, l) partial per workgroup.
 //   decode_combine_kernel - per (request, KV head): log-sum-exp merge of the
-//       ceil(topk/4) partials in fixed order, bf16 output (or, for the MXFP8
+//       ceil(topk/8) partials in fixed order, bf16 output (or, for the MXFP8
 //       variant, that bf16 output encoded as E4M3 + E8M0 per 32 values).
 #include "msa_internal.hpp"
 #include "mxfp8.hpp"
@@ -29,7 +33,6 @@ namespace msa {
 namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kDecPagesPerWg = 1;  // pages (one wave each) per score workgroup
-constexpr int kDecBlocksPerWg = 4;  // selected blocks per attention workgroup (4 waves each)
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -364,223 +367,22 @@ __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, kHi));
 }
 
-// Workgroup (sg, g, r): selected blocks kBpw*sg .. kBpw*sg + kBpw-1 of KV
-// head g for request r; 4 waves per block, wave w owns keys 32(w%4)..+31 of
-// block w/4.
-//   S^T[32 keys x 16 heads] = K . Q^T   (MFMA 16x16x32, K straight from HBM)
-//   per-wave softmax partial, V rows copied HBM -> LDS (global_load_lds),
-//   O^T[128 x 16] = V^T . P^T with V^T from ds_read_b64_tr_b16;
-//   a wave whose slot is unselected (-1 or past the query block) holds an
-//   empty partial; the 4*kBpw waves are merged in LDS, in wave order, into
-//   one (O, m, l) partial of the workgroup.
-// kFp8Kv: K/V caches hold E4M3FN bytes.  E4M3 values are exact in bf16, so
-// K and V are converted exactly (V into the bf16 LDS layout of the other
-// variant); the K scale is folded into scale_log2 by the caller and the V
-// scale multiplies the block's partial O.
-template <bool kFp8Kv, int kBpw>
-__global__ __launch_bounds__(256 * kBpw) void decode_attend_kernel(
-    const uint16_t *__restrict__ q, const void *__restrict__ kc_, const void *__restrict__ vc_,
-    const int32_t *__restrict__ pt, int max_pages, const int32_t *__restrict__ ctx, int max_ctx,
-    int B, const int32_t *__restrict__ q2k, int topk, int nparts, float scale_log2, float v_scale,
-    float *__restrict__ part_o, float *__restrict__ part_ml) {
-    extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];  // per wave: V rows, then O^T
-    __shared__ float s_m[4 * kBpw][16], s_l[4 * kBpw][16];
-    const int sg = blockIdx.x, g = blockIdx.y, r = blockIdx.z;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int n = lane & 15, qd = lane >> 4;
-    const int s = sg * kBpw + (wave >> 2);  // this wave's slot of the row
-    const int wq = wave & 3;                // its quarter (32 keys) of the block
-    const size_t pidx = (size_t(r) * kKvHeads + g) * nparts + sg;
-    float *po = part_o + pidx * (kGroup * kDim);
-    float *pml = part_ml + pidx * (kGroup * 2);
-
-    const int L = min(max(ctx[r], 1), max_ctx);
-    const int c = (L - 1) / kBlock;
-    const int b = s < topk ? q2k[(size_t(g) * B + r) * topk + s] : -1;
-    uint8_t *vt = smem + wave * kWaveVBytes;
-    // this wave's partial over its 32 keys (empty when the slot is unselected)
-    float mloc = -INFINITY, psum = 0.f;
-    f32x4 oacc[8];
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) oacc[dt] = f32x4{};
-    if (b >= 0 && b <= c) {
-        const size_t slot0 = size_t(pt[size_t(r) * max_pages + b]) * kBlock;
-        const int key0 = 32 * wq;
-        const int kmax = L - 1 - b * kBlock;  // last valid key of the block
-
-        // V rows key0..key0+31 -> LDS; rows past L re-read the last valid row
-        // (their probabilities are 0).
-        if constexpr (!kFp8Kv) {
-            // 8 one-KiB copies straight into the swizzled bf16 layout
-            const uint16_t *vc = (const uint16_t *)vc_;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int rr = 4 * j + (lane >> 4);  // row within the wave's 32
-                const int chunk = (lane & 15) ^ vswz(rr);
-                const int key = min(key0 + rr, kmax);
-                const uint16_t *src = vc + ((slot0 + key) * kKvHeads + g) * kDim + 8 * chunk;
-                __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(vt + j * 1024), 16, 0, 0);
-            }
-        } else {
-            // lane: 16 E4M3 values (d 16c..16c+15) of row 8j + lane/8, written
-            // as the two bf16 chunks 2c, 2c+1 of that row
-            const uint8_t *vc = (const uint8_t *)vc_;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int rr = 8 * j + (lane >> 3), c = lane & 7;
-                const int key = min(key0 + rr, kmax);
-                const u32x4 x = *(const u32x4 *)(vc + ((slot0 + key) * kKvHeads + g) * kDim + 16 * c);
-                u32x4 lo, hi;
-#pragma unroll
-                for (int w = 0; w < 2; ++w) {
-                    lo[2 * w] = e4m3x2_to_bf16x2<false>(x[w]);
-                    lo[2 * w + 1] = e4m3x2_to_bf16x2<true>(x[w]);
-                    hi[2 * w] = e4m3x2_to_bf16x2<false>(x[2 + w]);
-                    hi[2 * w + 1] = e4m3x2_to_bf16x2<true>(x[2 + w]);
-                }
-                *(u32x4 *)(vt + rr * kRowB + (((2 * c) ^ vswz(rr)) << 4)) = lo;
-                *(u32x4 *)(vt + rr * kRowB + (((2 * c + 1) ^ vswz(rr)) << 4)) = hi;
-            }
-        }
-        // Q^T operand: lane (n = head, qd), step ks: 16-byte chunk 4ks + qd
-        const uint16_t *qrow = q + (size_t(r) * kHeads + g * kGroup + n) * kDim;
-        bf16x8 qb[4];
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-            qb[ks] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qrow + 8 * (4 * ks + qd)));
-        // K operand: M-tile mt = keys key0 + 16mt + m, same chunk order
-        u32x4 ka[2][4];
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-            const int key = min(key0 + 16 * mt + n, kmax);
-            if constexpr (!kFp8Kv) {
-                const uint16_t *src = (const uint16_t *)kc_ + ((slot0 + key) * kKvHeads + g) * kDim;
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks) ka[mt][ks] = *(const u32x4 *)(src + 8 * (4 * ks + qd));
-            } else {
-                const uint8_t *src = (const uint8_t *)kc_ + ((slot0 + key) * kKvHeads + g) * kDim;
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    const u32x2 x = *(const u32x2 *)(src + 8 * (4 * ks + qd));
-                    ka[mt][ks] = u32x4{e4m3x2_to_bf16x2<false>(x[0]), e4m3x2_to_bf16x2<true>(x[0]),
-                                       e4m3x2_to_bf16x2<false>(x[1]), e4m3x2_to_bf16x2<true>(x[1])};
-                }
-            }
-        }
-        f32x4 sacc[2];
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-            sacc[mt] = f32x4{};
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-                sacc[mt] = mfma_16x16x32(__builtin_bit_cast(bf16x8, ka[mt][ks]), qb[ks], sacc[mt]);
-        }
-        // softmax over this wave's 32 keys for head column n (lane holds keys
-        // 16mt + 4qd + i of its column)
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const bool ok = key0 + 16 * mt + 4 * qd + i <= kmax;
-                const float z = ok ? sacc[mt][i] * scale_log2 : -INFINITY;
-                sacc[mt][i] = z;
-                mloc = fmaxf(mloc, z);
-            }
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-        const float base = mloc == -INFINITY ? 0.f : mloc;
-        bf16x8 pb;  // P^T operand: keys 4qd + e (tile 0) then 16 + 4qd + e (tile 1)
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float p = __builtin_amdgcn_exp2f(sacc[mt][i] - base);
-                psum += p;
-                pb[4 * mt + i] = (__bf16)p;
-            }
-        psum += __shfl_xor(psum, 16);
-        psum += __shfl_xor(psum, 32);
-
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's V rows are in LDS
-        // O^T[d x heads] = V^T . P^T.  Transposing read: in lane group qd, lane
-        // i supplies row (16h + 4qd + i/4), columns 16dt + 4(i%4)..+3, and
-        // lane j receives V[row0 + e][16dt + j] for e = 0..3.
-        const int gi = lane & 15;
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-            i16x4 t[2];
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int rr = 16 * h + 4 * qd + (gi >> 2);
-                const int col = 16 * dt + 4 * (gi & 3);
-                const int pos = ((col >> 3) ^ vswz(rr)) << 4;
-                t[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_i16x4 *)(vt + rr * kRowB + pos + ((col & 7) << 1)));
-            }
-            const i16x8 ab = {t[0][0], t[0][1], t[0][2], t[0][3], t[1][0], t[1][1], t[1][2], t[1][3]};
-            oacc[dt] = mfma_16x16x32(__builtin_bit_cast(bf16x8, ab), pb, f32x4{});
-        }
-    }
-    // wave partial O^T -> LDS (over this wave's own V rows, already consumed)
-    float *so = (float *)vt;  // [16 heads][128 d]
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) so[n * kDim + 16 * dt + 4 * qd + i] = oacc[dt][i];
-    if (qd == 0) {
-        s_m[wave][n] = mloc;
-        s_l[wave][n] = psum;
-    }
-    __syncthreads();
-    if (tid >= 256) return;
-    // merge the workgroup's 4*kBpw waves (kBpw blocks) in wave order:
-    // thread -> (head hh, 8 d)
-    constexpr int kW = 4 * kBpw;
-    const int hh = tid >> 4, d0 = (tid & 15) * 8;
-    float mw[kW], M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kW; ++w) { mw[w] = s_m[w][hh]; M = fmaxf(M, mw[w]); }
-    const float baseM = M == -INFINITY ? 0.f : M;
-    float sc[kW], l = 0.f;
-#pragma unroll
-    for (int w = 0; w < kW; ++w) {
-        sc[w] = __builtin_amdgcn_exp2f(mw[w] - baseM);
-        l += sc[w] * s_l[w][hh];
-    }
-    float o[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = 0.f;
-#pragma unroll
-    for (int w = 0; w < kW; ++w) {
-        const float *src = (const float *)(smem + w * kWaveVBytes) + hh * kDim + d0;
-        const f32x4 a = *(const f32x4 *)src, c4 = *(const f32x4 *)(src + 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            o[e] += sc[w] * a[e];
-            o[4 + e] += sc[w] * c4[e];
-        }
-    }
-    if constexpr (kFp8Kv) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] *= v_scale;
-    }
-    *(f32x4 *)(po + hh * kDim + d0) = f32x4{o[0], o[1], o[2], o[3]};
-    *(f32x4 *)(po + hh * kDim + d0 + 4) = f32x4{o[4], o[5], o[6], o[7]};
-    if ((tid & 15) == 0) {
-        pml[2 * hh] = M;
-        pml[2 * hh + 1] = l;
-    }
-}
-
 // ---------------------------------------------------------------------------
-// G6, bf16 caches: streaming attention, one workgroup per 8 slots of a row
+// G6: streaming attention, one workgroup per 8 slots of a row
 // ---------------------------------------------------------------------------
 namespace {
-constexpr int kStreamSlots = 8;                    // selected slots per workgroup
-constexpr int kStreamStage = 2 * kWaveVBytes;      // one wave's K rows + V rows of one block (16 KiB)
-constexpr int kStreamWaveBytes = 2 * kStreamStage; // two stages per wave (32 KiB)
+constexpr int kStreamSlots = 8;  // selected slots per workgroup
+// Per wave: two stages of one block's K rows + V rows (bf16: 2 x 16 KiB;
+// E4M3: 2 x 8 KiB of bytes plus an 8 KiB bf16 V buffer for the transposing
+// reads).
+template <bool kFp8Kv> struct StreamLayout {
+    static constexpr int kRowBytes = kFp8Kv ? kDim : 2 * kDim;    // one K or V row
+    static constexpr int kHalf = 32 * kRowBytes;                   // 32 rows
+    static constexpr int kStage = 2 * kHalf;                       // K rows, V rows
+    static constexpr int kVbf = kFp8Kv ? 2 * kStage : 0;           // offset of the bf16 V buffer
+    static constexpr int kWave = 2 * kStage + (kFp8Kv ? kWaveVBytes : 0);
+    static constexpr int kCopies = kStage / 1024;                  // one-KiB copies per block
+};
 
 // HBM -> LDS copy of 16 bytes per lane (lane l writes lds_dst + 16l), from
 // asm so that the compiler does not wait for it before unrelated LDS reads;
@@ -600,11 +402,18 @@ __device__ __forceinline__ void stream_copy(const void *src, uint8_t *lds_dst) {
 //   transposing LDS reads); the 4 waves' partials are merged at the end
 //   into one (O, m, l) partial of the workgroup.
 // Both row buffers keep 16-byte chunk c of row rr at position c ^ (rr & 15).
+// kFp8Kv: E4M3 caches; K is widened to bf16 as it is read, and each wave's
+// V rows are widened once into a bf16 buffer in the layout above (E4M3
+// values are exact in bf16; k_scale is folded into scale_log2 and v_scale
+// multiplies the partial O).  Byte rows keep 16-byte chunk c of row rr at
+// position c ^ (rr & 7).
+template <bool kFp8Kv>
 __global__ __launch_bounds__(256) void decode_attend_stream_kernel(
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc, const uint16_t *__restrict__ vc,
+    const uint16_t *__restrict__ q, const void *__restrict__ kc_, const void *__restrict__ vc_,
     const int32_t *__restrict__ pt, int max_pages, const int32_t *__restrict__ ctx, int max_ctx, int B,
-    const int32_t *__restrict__ q2k, int topk, int nparts, float scale_log2, float *__restrict__ part_o,
-    float *__restrict__ part_ml) {
+    const int32_t *__restrict__ q2k, int topk, int nparts, float scale_log2, float v_scale,
+    float *__restrict__ part_o, float *__restrict__ part_ml) {
+    using SL = StreamLayout<kFp8Kv>;
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];  // 4 waves x 2 stages x (K, V)
     __shared__ float s_m[4][16], s_l[4][16];
     const int sg = blockIdx.x, g = blockIdx.y, r = blockIdx.z;
@@ -614,7 +423,7 @@ __global__ __launch_bounds__(256) void decode_attend_stream_kernel(
     const int L = min(max(ctx[r], 1), max_ctx);
     const int c = (L - 1) / kBlock;
     const int key0 = 32 * wave;
-    uint8_t *ring = smem + wave * kStreamWaveBytes;
+    uint8_t *ring = smem + wave * SL::kWave;
 
     // the workgroup's slots (wave-uniform): block id, or -1 when unselected
     int bsel[kStreamSlots];
@@ -630,14 +439,16 @@ __global__ __launch_bounds__(256) void decode_attend_stream_kernel(
         const int b = bsel[j];
         const size_t slot0 = size_t(pt[size_t(r) * max_pages + b]) * kBlock;
         const int kmax = L - 1 - b * kBlock;
-        uint8_t *kb = ring + st * kStreamStage;
+        uint8_t *kb = ring + st * SL::kStage;
+        constexpr int kRowsPerCopy = 1024 / SL::kRowBytes;  // 4 (bf16) or 8 (E4M3)
+        constexpr int kChunksPerRow = SL::kRowBytes / 16;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int rr = 4 * i + (lane >> 4);
-            const int chunk = (lane & 15) ^ vswz(rr);
-            const size_t row = ((slot0 + min(key0 + rr, kmax)) * kKvHeads + g) * kDim + 8 * chunk;
-            stream_copy(kc + row, kb + i * 1024);
-            stream_copy(vc + row, kb + kWaveVBytes + i * 1024);
+        for (int i = 0; i < SL::kCopies / 2; ++i) {
+            const int rr = kRowsPerCopy * i + lane / kChunksPerRow;
+            const int chunk = (lane % kChunksPerRow) ^ (kFp8Kv ? (rr & 7) : vswz(rr));
+            const size_t off = ((slot0 + min(key0 + rr, kmax)) * kKvHeads + g) * SL::kRowBytes + 16 * chunk;
+            stream_copy((const uint8_t *)kc_ + off, kb + i * 1024);
+            stream_copy((const uint8_t *)vc_ + off, kb + SL::kHalf + i * 1024);
         }
     };
 
@@ -662,11 +473,38 @@ __global__ __launch_bounds__(256) void decode_attend_stream_kernel(
             issue(j + 1, (j + 1) & 1);
         }
         if (bsel[j] < 0) continue;
-        if (next) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");  // slot j's 16 copies have landed
-        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        const uint8_t *kb = ring + (j & 1) * kStreamStage;
-        const uint8_t *vt = kb + kWaveVBytes;
+        // slot j's copies have landed (the next slot's may still be in flight)
+        if (next) {
+            if constexpr (kFp8Kv) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+            else asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+        } else {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+        const uint8_t *kb = ring + (j & 1) * SL::kStage;
+        const uint8_t *vt = kFp8Kv ? ring + SL::kVbf : kb + SL::kHalf;
         const int kmax = L - 1 - bsel[j] * kBlock;
+        if constexpr (kFp8Kv) {
+            // widen this wave's 32 V rows into the bf16 buffer: lane -> row
+            // lane/2, byte chunks 4(lane%2)..+3 (16 E4M3 values each)
+            const uint8_t *vr = kb + SL::kHalf;
+            uint8_t *vb = ring + SL::kVbf;
+            const int rr = lane >> 1;
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) {
+                const int c = 4 * (lane & 1) + cc;
+                const u32x4 x = *(const u32x4 *)(vr + rr * SL::kRowBytes + ((c ^ (rr & 7)) << 4));
+                u32x4 lo, hi;
+#pragma unroll
+                for (int w = 0; w < 2; ++w) {
+                    lo[2 * w] = e4m3x2_to_bf16x2<false>(x[w]);
+                    lo[2 * w + 1] = e4m3x2_to_bf16x2<true>(x[w]);
+                    hi[2 * w] = e4m3x2_to_bf16x2<false>(x[2 + w]);
+                    hi[2 * w + 1] = e4m3x2_to_bf16x2<true>(x[2 + w]);
+                }
+                *(u32x4 *)(vb + rr * kRowB + (((2 * c) ^ vswz(rr)) << 4)) = lo;
+                *(u32x4 *)(vb + rr * kRowB + (((2 * c + 1) ^ vswz(rr)) << 4)) = hi;
+            }
+        }
         // S^T: M-tile mt = keys key0 + 16mt + m (row 16mt + m of the buffer)
         f32x4 sacc[2];
 #pragma unroll
@@ -675,8 +513,16 @@ __global__ __launch_bounds__(256) void decode_attend_stream_kernel(
             const int rr = 16 * mt + n;
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                const bf16x8 ka = __builtin_bit_cast(
-                    bf16x8, *(const u32x4 *)(kb + rr * kRowB + (((4 * ks + qd) ^ vswz(rr)) << 4)));
+                bf16x8 ka;
+                if constexpr (kFp8Kv) {
+                    // 8 E4M3 values: the half (4ks + qd) % 2 of byte chunk (4ks + qd) / 2
+                    const int e = 4 * ks + qd;
+                    const u32x2 x = *(const u32x2 *)(kb + rr * SL::kRowBytes + ((((e >> 1) ^ (rr & 7)) << 4) | ((e & 1) << 3)));
+                    ka = __builtin_bit_cast(bf16x8, u32x4{e4m3x2_to_bf16x2<false>(x[0]), e4m3x2_to_bf16x2<true>(x[0]),
+                                                          e4m3x2_to_bf16x2<false>(x[1]), e4m3x2_to_bf16x2<true>(x[1])});
+                } else {
+                    ka = __builtin_bit_cast(bf16x8, *(const u32x4 *)(kb + rr * kRowB + (((4 * ks + qd) ^ vswz(rr)) << 4)));
+                }
                 sacc[mt] = mfma_16x16x32(ka, qb[ks], sacc[mt]);
             }
         }
@@ -726,8 +572,8 @@ __global__ __launch_bounds__(256) void decode_attend_stream_kernel(
             oacc[dt] = mfma_16x16x32(__builtin_bit_cast(bf16x8, ab), pb, oacc[dt] * alpha);
         }
     }
-    // wave partial O^T -> LDS (stage 0 of the wave's own ring, no longer read)
-    float *so = (float *)ring;  // [16 heads][128 d]
+    // wave partial O^T -> LDS (the start of the wave's own ring, no longer read)
+    float *so = (float *)ring;  // [16 heads][128 d] (8 KiB)
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
@@ -755,13 +601,17 @@ __global__ __launch_bounds__(256) void decode_attend_stream_kernel(
     for (int e = 0; e < 8; ++e) o[e] = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-        const float *src = (const float *)(smem + w * kStreamWaveBytes) + hh * kDim + d0;
+        const float *src = (const float *)(smem + w * SL::kWave) + hh * kDim + d0;
         const f32x4 a = *(const f32x4 *)src, c4 = *(const f32x4 *)(src + 4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             o[e] += sc[w] * a[e];
             o[4 + e] += sc[w] * c4[e];
         }
+    }
+    if constexpr (kFp8Kv) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] *= v_scale;
     }
     const size_t pidx = (size_t(r) * kKvHeads + g) * nparts + sg;
     float *po = part_o + pidx * (kGroup * kDim);
@@ -842,40 +692,31 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float *__restr
     }
 }
 
-// partials per (request, KV head): one per attention workgroup (8 slots per
-// workgroup for bf16 caches, 4 for E4M3 caches)
-int decode_parts(int topk, bool fp8kv) { return ceil_div(topk, fp8kv ? kDecBlocksPerWg : kStreamSlots); }
+// partials per (request, KV head): one per attention workgroup (8 slots)
+int decode_parts(int topk) { return ceil_div(topk, kStreamSlots); }
 
 hipError_t launch_decode_attend(const uint16_t *q, const void *kc, const void *vc, bool fp8kv, float k_scale,
                                 float v_scale, const int32_t *pt, int max_pages, const int32_t *ctx,
                                 int max_ctx, int B, const int32_t *q2k, int topk, float scale,
                                 float *partial, hipStream_t stream) {
-    const int nparts = decode_parts(topk, fp8kv);
+    const int nparts = decode_parts(topk);
     float *part_o = partial;
     float *part_ml = partial + size_t(B) * kKvHeads * nparts * kGroup * kDim;
     const dim3 grid(nparts, kKvHeads, B);
-    if (!fp8kv) {
-        hipLaunchKernelGGL(decode_attend_stream_kernel, grid, dim3(256), size_t(4) * kStreamWaveBytes, stream, q,
-                           (const uint16_t *)kc, (const uint16_t *)vc, pt, max_pages, ctx, max_ctx, B, q2k, topk,
-                           nparts, scale * kLog2e, part_o, part_ml);
-        return hipGetLastError();
-    }
-    const float sl = scale * kLog2e * (fp8kv ? k_scale : 1.0f);
-    const float vs = fp8kv ? v_scale : 1.0f;
-    constexpr int N = kDecBlocksPerWg;
-    const size_t lds = size_t(4 * N) * kWaveVBytes;
     if (fp8kv)
-        hipLaunchKernelGGL((decode_attend_kernel<true, N>), grid, dim3(256 * N), lds, stream, q, kc, vc, pt,
-                           max_pages, ctx, max_ctx, B, q2k, topk, nparts, sl, vs, part_o, part_ml);
+        hipLaunchKernelGGL(decode_attend_stream_kernel<true>, grid, dim3(256), size_t(4) * StreamLayout<true>::kWave,
+                           stream, q, kc, vc, pt, max_pages, ctx, max_ctx, B, q2k, topk, nparts,
+                           scale * kLog2e * k_scale, v_scale, part_o, part_ml);
     else
-        hipLaunchKernelGGL((decode_attend_kernel<false, N>), grid, dim3(256 * N), lds, stream, q, kc, vc, pt,
-                           max_pages, ctx, max_ctx, B, q2k, topk, nparts, sl, vs, part_o, part_ml);
+        hipLaunchKernelGGL(decode_attend_stream_kernel<false>, grid, dim3(256), size_t(4) * StreamLayout<false>::kWave,
+                           stream, q, kc, vc, pt, max_pages, ctx, max_ctx, B, q2k, topk, nparts, scale * kLog2e,
+                           1.0f, part_o, part_ml);
     return hipGetLastError();
 }
 
 hipError_t launch_decode_combine(const float *partial, int B, int topk, bool fp8kv, uint16_t *out,
                                  uint8_t *out_q, uint8_t *out_scale, hipStream_t stream) {
-    topk = decode_parts(topk, fp8kv);  // partials per (request, KV head)
+    topk = decode_parts(topk);  // partials per (request, KV head)
     const float *part_o = partial;
     const float *part_ml = partial + size_t(B) * kKvHeads * topk * kGroup * kDim;
     if (out_q)
