@@ -46,6 +46,7 @@ constexpr int kRing = 9;  // LDS ring slots of one unit each (144 KiB)
 constexpr int kLoadsPerWave = kUnitBytes / 1024 / kWaves;  // 2 one-KiB copies
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazyLog2 = 8.f;  // rescale only when the max grows by > 2^8
+constexpr int kSharedMin = 2;     // union blocks this many tokens selected go through the ring
 
 static_assert(kLoadsPerWave == 2, "unit copy split assumes 2 copies per wave");
 static_assert(kRing == 2 * kUnitsPerBlock + 1, "one unit of the block after next streams ahead");
@@ -176,6 +177,63 @@ __device__ __forceinline__ void attend_block(WaveState &st, const uint8_t *smem,
 
 }  // namespace
 
+namespace {
+// One block b < c for token t of a wave, read straight from memory (K rows
+// and V^T unit rows are contiguous in the MFMA operand layouts), unit by
+// unit with the lazy online softmax.  Used for blocks a single token of the
+// tile selected, which would otherwise hold the whole workgroup at a
+// barrier for one wave's work.
+__device__ __forceinline__ void attend_block_global(WaveState &st, int t, const uint16_t *__restrict__ k,
+                                                    const uint16_t *__restrict__ vt, int doc_start, int g,
+                                                    int uoff, int b, int n, int grp, float scale_log2) {
+#pragma unroll 1
+    for (int q = 0; q < kUnitsPerBlock; ++q) {
+        const int key_base = doc_start + b * kBlock + kAttnUnit * q;
+        f32x4 sacc[2] = {f32x4{}, f32x4{}};
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            const uint16_t *src = k + (size_t(key_base + 8 * (n >> 2) + 4 * mt + (n & 3)) * kKvHeads + g) * kDim;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                sacc[mt] = mfma_16x16x32(__builtin_bit_cast(bf16x8, *(const u32x4 *)(src + 8 * (4 * ks + grp))),
+                                         st.qb[t][ks], sacc[mt]);
+        }
+        const uint16_t *vsrc = vt + ((size_t(uoff + kUnitsPerBlock * b + q) * kKvHeads + g) * kDim + n) * kAttnUnit + 8 * grp;
+        bf16x8 va[8];
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) va[dt] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(vsrc + 16 * dt * kAttnUnit));
+        float mloc = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mloc = fmaxf(mloc, sacc[e >> 2][e & 3]);
+        mloc = row_max4(mloc);
+        const bool grow = mloc > st.m_ref[t] &&
+                          (st.m_ref[t] == -INFINITY || (mloc - st.m_ref[t]) * scale_log2 > kLazyLog2);
+        if (__ballot(grow)) {
+            const float m_new = grow ? mloc : st.m_ref[t];
+            const float alpha = st.m_ref[t] == -INFINITY
+                                    ? 0.f
+                                    : __builtin_amdgcn_exp2f((st.m_ref[t] - m_new) * scale_log2);
+            st.l_run[t] *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) st.acc_o[t][dt] *= alpha;
+            st.m_ref[t] = m_new;
+        }
+        const float mb = st.m_ref[t] == -INFINITY ? 0.f : st.m_ref[t] * scale_log2;
+        float psum = 0.f;
+        bf16x8 pb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float pv = __builtin_amdgcn_exp2f(sacc[e >> 2][e & 3] * scale_log2 - mb);
+            psum += pv;
+            pb[e] = (__bf16)pv;
+        }
+        st.l_run[t] += psum;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) st.acc_o[t][dt] = mfma_16x16x32(va[dt], pb, st.acc_o[t][dt]);
+    }
+}
+}  // namespace
+
 // ---------------------------------------------------------------------------
 // V -> per-unit V^T
 // ---------------------------------------------------------------------------
@@ -233,7 +291,9 @@ __global__ __launch_bounds__(kThreads) void attend_prefill_kernel(
     __shared__ int s_mask[kEntries];
     __shared__ int s_ublk[kEntries];
     __shared__ int s_umask[kEntries];
-    __shared__ int s_nu;
+    __shared__ int s_sblk[kEntries];   // the ring's blocks: shared ones and the query's own
+    __shared__ int s_smask[kEntries];
+    __shared__ int s_nu, s_ns;
 
     // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs; XCD x
     // serves KV head x/2 and alternate groups of 8 tiles (one 128-token query
@@ -281,11 +341,46 @@ __global__ __launch_bounds__(kThreads) void attend_prefill_kernel(
     // ---- union of the tile's selected blocks (ascending, with token masks)
     const int nu = tile_union(q2k, T, topk, g, doc.start + p0, ntok, c, tid, s_id, s_first, s_mask,
                               s_ublk, s_umask, &s_nu);
-    // 32-key units: 4 per union block, except that the query's own block c
+    // Split the union: blocks at least kSharedMin tokens selected, and the
+    // query's own block, go through the LDS ring (ascending); a block one
+    // token selected is read by that token's wave straight from memory.
+    if (wave == 0) {
+        int base = 0;
+        for (int u0 = 0; u0 < nu; u0 += 64) {
+            const int u = u0 + lane;
+            const bool sh = u < nu && (__popc(s_umask[u]) >= kSharedMin || s_ublk[u] == c);
+            const uint64_t m = __ballot(sh);
+            if (sh) {
+                const int pos = base + __popcll(m & ((1ull << lane) - 1ull));
+                s_sblk[pos] = s_ublk[u];
+                s_smask[pos] = s_umask[u];
+            }
+            base += __popcll(m);
+        }
+        if (lane == 0) s_ns = base;
+    }
+    __syncthreads();
+    const int ns = s_ns;
+    // ---- blocks a single token of the tile selected: that token's wave
+    // alone, straight from memory (never the query's own block), before the
+    // ring starts (the online softmax takes the blocks in any order)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        if (!tok_ok[t]) continue;
+        const int bit = 1 << (2 * wave + t);
+        for (int u = 0; u < nu; ++u) {
+            const int um = __builtin_amdgcn_readfirstlane(s_umask[u]);
+            const int b = __builtin_amdgcn_readfirstlane(s_ublk[u]);
+            if (!(um & bit) || b == c || __popc(um) >= kSharedMin) continue;
+            attend_block_global(st, t, k, vt, doc.start, g, uoff, b, n, grp, scale_log2);
+        }
+    }
+
+    // 32-key units: 4 per ring block, except that the query's own block c
     // (always last when present) stops at the unit holding p_last.
     const int last_units =
-        (nu > 0 && s_ublk[nu - 1] == c) ? (p_last - c * kBlock) / kAttnUnit + 1 : kUnitsPerBlock;
-    const int nunits = nu > 0 ? kUnitsPerBlock * (nu - 1) + last_units : 0;
+        (ns > 0 && s_sblk[ns - 1] == c) ? (p_last - c * kBlock) / kAttnUnit + 1 : kUnitsPerBlock;
+    const int nunits = ns > 0 ? kUnitsPerBlock * (ns - 1) + last_units : 0;
 
     // ---- HBM -> LDS unit copies: 16 one-KiB copies per unit.  Copy i < 8
     // fills K rows 4i..4i+3 (lane l: row 4i + l/16, slot position l%16, i.e.
@@ -313,7 +408,7 @@ __global__ __launch_bounds__(kThreads) void attend_prefill_kernel(
     };
     // Wave w issues copies 2w and 2w+1 of every unit.
     auto issue_unit = [&](int vu) {
-        const int ub = __builtin_amdgcn_readfirstlane(s_ublk[vu >> 2]);
+        const int ub = __builtin_amdgcn_readfirstlane(s_sblk[vu >> 2]);
         issue_copy(vu, ub, 2 * wave);
         issue_copy(vu, ub, 2 * wave + 1);
     };
@@ -334,14 +429,14 @@ __global__ __launch_bounds__(kThreads) void attend_prefill_kernel(
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): query operands are in (no copy issued yet)
     int issued = min(nunits, kRing);
     for (int vu = 0; vu < issued; ++vu) issue_unit(vu);
-    for (int u = 0; u < nu; ++u) {
+    for (int u = 0; u < ns; ++u) {
         const int ustart = kUnitsPerBlock * u;
-        const int nq = u == nu - 1 ? nunits - ustart : kUnitsPerBlock;
+        const int nq = u == ns - 1 ? nunits - ustart : kUnitsPerBlock;
         wait_copies(2 * (issued - (ustart + nq)));  // copies complete in issue order
         barrier_keep_prefetch();
 
-        const int b = __builtin_amdgcn_readfirstlane(s_ublk[u]);
-        const int umask = __builtin_amdgcn_readfirstlane(s_umask[u]);
+        const int b = __builtin_amdgcn_readfirstlane(s_sblk[u]);
+        const int umask = __builtin_amdgcn_readfirstlane(s_smask[u]);
         const bool act[2] = {tok_ok[0] && ((umask >> (2 * wave)) & 1),
                              tok_ok[1] && ((umask >> (2 * wave + 1)) & 1)};
         // refill the slots of block u-1 (every wave is past it)
