@@ -68,11 +68,6 @@ __device__ __forceinline__ uint32_t float_order_bits(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Selection key: score first, then the lower block id wins a tie.
-__device__ __forceinline__ uint64_t select_key(float s, int b) {
-    return (uint64_t(float_order_bits(s)) << 32) | uint64_t(0xFFFFFFFFu - uint32_t(b));
-}
-
 // Document containing compact token t (binary search over sanitised spans);
 // -1 when t lies in no span.
 __device__ __forceinline__ int find_doc(const DocSpan *docs, int ndocs, int t) {

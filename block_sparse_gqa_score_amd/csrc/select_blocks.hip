@@ -260,22 +260,31 @@ hipError_t launch_block_scores(const void *iq, const void *ik, bool fp8, const D
 // ---------------------------------------------------------------------------
 // G2: forced blocks + top-k
 // ---------------------------------------------------------------------------
-// Insert `key` into the descending list top[0..15] (smallest falls off).
-__device__ __forceinline__ void topk_insert(uint64_t (&top)[kMaxTopk], uint64_t key) {
+// Insert `key` into the descending multiset top[0..15] (the smallest falls
+// off): a min/max exchange per slot, two ALU ops each.
+__device__ __forceinline__ void topk_insert(uint32_t (&top)[kMaxTopk], uint32_t key) {
 #pragma unroll
-    for (int i = kMaxTopk - 1; i >= 0; --i) {
-        const uint64_t prev = i > 0 ? top[i - 1] : ~0ull;
-        if (key > top[i]) top[i] = key > prev ? prev : key;
+    for (int i = 0; i < kMaxTopk; ++i) {
+        const uint32_t hi = max(top[i], key);
+        key = min(top[i], key);
+        top[i] = hi;
     }
 }
 
-__device__ __forceinline__ uint64_t topk_at(const uint64_t (&top)[kMaxTopk], int i) {
-    uint64_t v = 0;
+__device__ __forceinline__ uint32_t topk_at(const uint32_t (&top)[kMaxTopk], int i) {
+    uint32_t v = 0;
 #pragma unroll
     for (int j = 0; j < kMaxTopk; ++j) v = (j == i) ? top[j] : v;
     return v;
 }
 
+// The R largest (score, lower block id first) keys are: every candidate whose
+// score key exceeds the R-th largest score key `thr`, plus the first
+// R - #(> thr) candidates in ascending block order whose key equals `thr`.
+// So the scan keeps only the 32-bit score keys (ties need no id), and the
+// emit pass hands out the tie quota in block order.  Empty slots hold 0; if a
+// row has fewer than R candidates, thr = 0 and the quota covers every
+// candidate whose key is 0, so all candidates are taken.
 __global__ __launch_bounds__(256) void topk_prefill_kernel(const float *__restrict__ S,
                                                            const DocSpan *__restrict__ docs,
                                                            int ndocs, int T, int nb_max, int topk,
@@ -294,22 +303,52 @@ __global__ __launch_bounds__(256) void topk_prefill_kernel(const float *__restri
     const int R = topk - forced_count(c, init, local);
     const float *row = S + size_t(h) * nb_max * T + t;  // row[b*T]
 
-    uint64_t top[kMaxTopk];
+    uint32_t top[kMaxTopk];
 #pragma unroll
     for (int i = 0; i < kMaxTopk; ++i) top[i] = 0;
+    // candidates are read 16 at a time, all loads issued before they are
+    // used (one load per candidate in a dependent loop waits a full memory
+    // latency each)
+    constexpr int kChunk = 16;
     if (R > 0) {
-        for (int b = 0; b <= c; ++b) {
-            if (is_forced(b, c, init, local)) continue;
-            const uint64_t key = select_key(row[size_t(b) * T], b);
-            topk_insert(top, key);
+        for (int b0 = 0; b0 <= c; b0 += kChunk) {
+            float sv[kChunk];
+#pragma unroll
+            for (int j = 0; j < kChunk; ++j) sv[j] = b0 + j <= c ? row[size_t(b0 + j) * T] : 0.f;
+#pragma unroll
+            for (int j = 0; j < kChunk; ++j) {
+                const int b = b0 + j;
+                if (b <= c && !is_forced(b, c, init, local)) topk_insert(top, float_order_bits(sv[j]));
+            }
         }
     }
-    const uint64_t thresh = R > 0 ? topk_at(top, R - 1) : ~0ull;
+    // R <= 0: the forced blocks fill the row and no candidate is taken
+    const uint32_t thr = R > 0 ? topk_at(top, R - 1) : ~0u;
+    int n_gt = 0;
+#pragma unroll
+    for (int i = 0; i < kMaxTopk; ++i) n_gt += (i < R && top[i] > thr) ? 1 : 0;
+    int quota = R > 0 ? R - n_gt : 0;
     int k = 0;
-    for (int b = 0; b <= c && k < topk; ++b) {
-        bool take = is_forced(b, c, init, local);
-        if (!take && R > 0) take = select_key(row[size_t(b) * T], b) >= thresh;
-        if (take) out[k++] = b;
+    for (int b0 = 0; b0 <= c && k < topk; b0 += kChunk) {
+        float sv[kChunk];
+#pragma unroll
+        for (int j = 0; j < kChunk; ++j) sv[j] = (R > 0 && b0 + j <= c) ? row[size_t(b0 + j) * T] : 0.f;
+#pragma unroll
+        for (int j = 0; j < kChunk; ++j) {
+            const int b = b0 + j;
+            bool take = false;
+            if (b <= c) {
+                if (is_forced(b, c, init, local)) {
+                    take = true;
+                } else if (R > 0) {
+                    const uint32_t key = float_order_bits(sv[j]);
+                    const bool tie = key == thr && quota > 0;
+                    quota -= tie ? 1 : 0;
+                    take = key > thr || tie;
+                }
+            }
+            if (take && k < topk) out[k++] = b;
+        }
     }
     for (; k < topk; ++k) out[k] = -1;
 }
