@@ -12,16 +12,16 @@
 //       heads, slots >= L masked, per-page max.
 //   decode_scores_kernel - E4M3 index keys: one wave per (request, page),
 //       MFMA 16x16x128 with unit scales.
-//   decode_topk_kernel   - one wave per (request, index head): the R-th
-//       largest score found by bisection on order-preserving score bits with
-//       wave-wide counts, then an ascending ballot-compacted emit (ties go
-//       to the lower block id); forced init/local blocks always emitted.
 //   decode_attend_stream_kernel - one workgroup per 8 selected slots of a
-//       (KV head, request); each wave streams its 32 keys of the next block
-//       through its own LDS ring while computing the current one: S^T = K Q^T
-//       and O^T = V^T P^T on MFMA 16x16x32 (16 query heads = N), an online
-//       softmax across the blocks, the 4 waves merged in LDS into one
-//       (O, m, l) partial per workgroup.
+//       (KV head, request).  Each wave first selects the row's blocks from
+//       the scores (the R-th largest score found by bisection on
+//       order-preserving score bits with wave-wide counts, then an ascending
+//       ballot-compacted emit; ties go to the lower block id; forced
+//       init/local blocks always kept).  Then it streams its 32 keys of the
+//       next block through its own LDS ring while computing the current one:
+//       S^T = K Q^T and O^T = V^T P^T on MFMA 16x16x32 (16 query heads = N),
+//       with an online softmax across the blocks; the 4 waves are merged in
+//       LDS into one (O, m, l) partial per workgroup.
 //   decode_combine_kernel - per (request, KV head): log-sum-exp merge of the
 //       ceil(topk/8) partials in fixed order, bf16 output (or, for the MXFP8
 //       variant, that bf16 output encoded as E4M3 + E8M0 per 32 values).
@@ -307,42 +307,6 @@ __device__ __forceinline__ void select_row(const float *__restrict__ srow, int c
     for (int i = emitted + lane; i < topk; i += 64) out[i] = -1;
 }
 
-template <int kCpl>
-__global__ __launch_bounds__(256) void decode_topk_kernel(const float *__restrict__ S,
-                                                          const int32_t *__restrict__ ctx, int B,
-                                                          int max_ctx, int nb_max, int topk, int init, int local,
-                                                          int32_t *__restrict__ q2k) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int row = blockIdx.x * 4 + wave;  // (r, h) with h fastest
-    if (row >= B * kIdxHeads) return;
-    const int r = row / kIdxHeads, h = row % kIdxHeads;
-    const int c = (min(max(ctx[r], 1), max_ctx) - 1) / kBlock;
-    select_row<kCpl>(S + (size_t(r) * kIdxHeads + h) * nb_max, c, topk, init, local, lane,
-                     q2k + (size_t(h) * B + r) * topk);
-}
-
-hipError_t launch_decode_topk(const float *S, const int32_t *ctx, int B, int max_ctx, int nb_max, int topk,
-                              int init, int local, int32_t *q2k, hipStream_t stream) {
-    const int cpl = ceil_div(nb_max, 64);
-    const dim3 grid(ceil_div(B * kIdxHeads, 4));
-#define MSA_TOPK_CASE(N)                                                                         \
-    if (cpl <= N) {                                                                              \
-        hipLaunchKernelGGL(decode_topk_kernel<N>, grid, dim3(256), 0, stream, S, ctx, B, max_ctx, nb_max, \
-                           topk, init, local, q2k);                                              \
-        return hipGetLastError();                                                                \
-    }
-    MSA_TOPK_CASE(1)
-    MSA_TOPK_CASE(2)
-    MSA_TOPK_CASE(4)
-    MSA_TOPK_CASE(8)
-    MSA_TOPK_CASE(16)
-    MSA_TOPK_CASE(32)
-    MSA_TOPK_CASE(64)
-    MSA_TOPK_CASE(128)
-#undef MSA_TOPK_CASE
-    return hipErrorInvalidValue;
-}
-
 // ---------------------------------------------------------------------------
 // G6: attention over one selected block per workgroup
 // ---------------------------------------------------------------------------
@@ -407,15 +371,16 @@ __device__ __forceinline__ void stream_copy(const void *src, uint8_t *lds_dst) {
 // values are exact in bf16; k_scale is folded into scale_log2 and v_scale
 // multiplies the partial O).  Byte rows keep 16-byte chunk c of row rr at
 // position c ^ (rr & 7).
-template <bool kFp8Kv>
+template <bool kFp8Kv, int kCpl>
 __global__ __launch_bounds__(256) void decode_attend_stream_kernel(
     const uint16_t *__restrict__ q, const void *__restrict__ kc_, const void *__restrict__ vc_,
     const int32_t *__restrict__ pt, int max_pages, const int32_t *__restrict__ ctx, int max_ctx, int B,
-    const int32_t *__restrict__ q2k, int topk, int nparts, float scale_log2, float v_scale,
-    float *__restrict__ part_o, float *__restrict__ part_ml) {
+    const float *__restrict__ S, int nb_max, int topk, int init, int local, int nparts, float scale_log2,
+    float v_scale, float *__restrict__ part_o, float *__restrict__ part_ml, int32_t *__restrict__ q2k_out) {
     using SL = StreamLayout<kFp8Kv>;
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];  // 4 waves x 2 stages x (K, V)
     __shared__ float s_m[4][16], s_l[4][16];
+    __shared__ int32_t s_sel[4][kMaxTopk];
     const int sg = blockIdx.x, g = blockIdx.y, r = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -425,14 +390,27 @@ __global__ __launch_bounds__(256) void decode_attend_stream_kernel(
     const int key0 = 32 * wave;
     uint8_t *ring = smem + wave * SL::kWave;
 
+    // Q^T operand: lane (n = head, qd), step ks: 16-byte chunk 4ks + qd
+    // (loaded first, so that its latency overlaps the selection)
+    const uint16_t *qrow = q + (size_t(r) * kHeads + g * kGroup + n) * kDim;
+    bf16x8 qb[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qb[ks] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qrow + 8 * (4 * ks + qd)));
+
+    // The row's selection from the scores of index head g: every wave computes
+    // the same row into its own LDS slots, so no barrier is needed.
+    select_row<kCpl>(S + (size_t(r) * kIdxHeads + g) * nb_max, c, topk, init, local, lane, s_sel[wave]);
+    __builtin_amdgcn_wave_barrier();
+    if (q2k_out && sg == 0 && wave == 0 && lane < topk) q2k_out[(size_t(g) * B + r) * topk + lane] = s_sel[0][lane];
     // the workgroup's slots (wave-uniform): block id, or -1 when unselected
     int bsel[kStreamSlots];
 #pragma unroll
     for (int j = 0; j < kStreamSlots; ++j) {
         const int s = sg * kStreamSlots + j;
-        const int b = s < topk ? q2k[(size_t(g) * B + r) * topk + s] : -1;
+        const int b = s < topk ? __builtin_amdgcn_readfirstlane(s_sel[wave][s]) : -1;
         bsel[j] = (b >= 0 && b <= c) ? b : -1;
     }
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): q is in before any copy is issued
     // copies of slot j into stage st: K rows key0..key0+31 (8 one-KiB copies)
     // then V rows (8); rows past L re-read the last valid row (masked)
     auto issue = [&](int j, int st) {
@@ -452,12 +430,6 @@ __global__ __launch_bounds__(256) void decode_attend_stream_kernel(
         }
     };
 
-    // Q^T operand: lane (n = head, qd), step ks: 16-byte chunk 4ks + qd
-    const uint16_t *qrow = q + (size_t(r) * kHeads + g * kGroup + n) * kDim;
-    bf16x8 qb[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qb[ks] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qrow + 8 * (4 * ks + qd)));
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): q is in before any copy is issued
 
     float m_run = -INFINITY, l_run = 0.f;  // per head column n (log2 domain)
     f32x4 oacc[8];
@@ -613,14 +585,14 @@ __global__ __launch_bounds__(256) void decode_attend_stream_kernel(
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[e] *= v_scale;
     }
-    const size_t pidx = (size_t(r) * kKvHeads + g) * nparts + sg;
-    float *po = part_o + pidx * (kGroup * kDim);
-    float *pml = part_ml + pidx * (kGroup * 2);
-    *(f32x4 *)(po + hh * kDim + d0) = f32x4{o[0], o[1], o[2], o[3]};
-    *(f32x4 *)(po + hh * kDim + d0 + 4) = f32x4{o[4], o[5], o[6], o[7]};
+    // this workgroup's (O, m, l) partial; the combine kernel merges the row's partials
+    float *po = part_o + (size_t(r) * kKvHeads + g) * nparts * (kGroup * kDim);
+    float *pml = part_ml + (size_t(r) * kKvHeads + g) * nparts * (kGroup * 2);
+    *(f32x4 *)(po + sg * (kGroup * kDim) + hh * kDim + d0) = f32x4{o[0], o[1], o[2], o[3]};
+    *(f32x4 *)(po + sg * (kGroup * kDim) + hh * kDim + d0 + 4) = f32x4{o[4], o[5], o[6], o[7]};
     if ((tid & 15) == 0) {
-        pml[2 * hh] = M;
-        pml[2 * hh + 1] = l;
+        pml[sg * (kGroup * 2) + 2 * hh] = M;
+        pml[sg * (kGroup * 2) + 2 * hh + 1] = l;
     }
 }
 
@@ -697,21 +669,37 @@ int decode_parts(int topk) { return ceil_div(topk, kStreamSlots); }
 
 hipError_t launch_decode_attend(const uint16_t *q, const void *kc, const void *vc, bool fp8kv, float k_scale,
                                 float v_scale, const int32_t *pt, int max_pages, const int32_t *ctx,
-                                int max_ctx, int B, const int32_t *q2k, int topk, float scale,
-                                float *partial, hipStream_t stream) {
+                                int max_ctx, int B, const float *S, int nb_max, int topk, int init, int local,
+                                float scale, float *partial, int32_t *q2k_out, hipStream_t stream) {
     const int nparts = decode_parts(topk);
     float *part_o = partial;
     float *part_ml = partial + size_t(B) * kKvHeads * nparts * kGroup * kDim;
     const dim3 grid(nparts, kKvHeads, B);
-    if (fp8kv)
-        hipLaunchKernelGGL(decode_attend_stream_kernel<true>, grid, dim3(256), size_t(4) * StreamLayout<true>::kWave,
-                           stream, q, kc, vc, pt, max_pages, ctx, max_ctx, B, q2k, topk, nparts,
-                           scale * kLog2e * k_scale, v_scale, part_o, part_ml);
-    else
-        hipLaunchKernelGGL(decode_attend_stream_kernel<false>, grid, dim3(256), size_t(4) * StreamLayout<false>::kWave,
-                           stream, q, kc, vc, pt, max_pages, ctx, max_ctx, B, q2k, topk, nparts, scale * kLog2e,
-                           1.0f, part_o, part_ml);
-    return hipGetLastError();
+    const int cpl = ceil_div(nb_max, 64);
+#define MSA_ATTEND_CASE(N)                                                                                   \
+    if (cpl <= N) {                                                                                          \
+        if (fp8kv)                                                                                           \
+            hipLaunchKernelGGL((decode_attend_stream_kernel<true, N>), grid, dim3(256),                      \
+                               size_t(4) * StreamLayout<true>::kWave, stream, q, kc, vc, pt, max_pages, ctx, \
+                               max_ctx, B, S, nb_max, topk, init, local, nparts, scale * kLog2e * k_scale,   \
+                               v_scale, part_o, part_ml, q2k_out);                                          \
+        else                                                                                                 \
+            hipLaunchKernelGGL((decode_attend_stream_kernel<false, N>), grid, dim3(256),                     \
+                               size_t(4) * StreamLayout<false>::kWave, stream, q, kc, vc, pt, max_pages, ctx, \
+                               max_ctx, B, S, nb_max, topk, init, local, nparts, scale * kLog2e, 1.0f,       \
+                               part_o, part_ml, q2k_out);                                                   \
+        return hipGetLastError();                                                                            \
+    }
+    MSA_ATTEND_CASE(1)
+    MSA_ATTEND_CASE(2)
+    MSA_ATTEND_CASE(4)
+    MSA_ATTEND_CASE(8)
+    MSA_ATTEND_CASE(16)
+    MSA_ATTEND_CASE(32)
+    MSA_ATTEND_CASE(64)
+    MSA_ATTEND_CASE(128)
+#undef MSA_ATTEND_CASE
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_decode_combine(const float *partial, int B, int topk, bool fp8kv, uint16_t *out,

@@ -120,16 +120,17 @@ BwdWs backward_layout(int T, int ndocs, int topk) {
 }
 
 struct DecodeWs {
-    size_t scores, q2k, part, total;
+    size_t scores, part, total;
 };
 
+// scores fp32 [B][4][nb_max]; partials: O fp32 [B][4][parts][16][128], then
+// (m, l) fp32 [B][4][parts][16][2]
 DecodeWs decode_layout(int B, int max_ctx, int topk) {
     DecodeWs w;
     const int nb_max = ceil_div(max_ctx, kBlock);
     w.scores = 0;
-    w.q2k = align256(sizeof(float) * size_t(B) * kIdxHeads * nb_max);
-    w.part = align256(w.q2k + sizeof(int32_t) * size_t(kIdxHeads) * B * topk);
-    const size_t part_floats = size_t(B) * kKvHeads * topk * kGroup * (kDim + 2);
+    w.part = align256(sizeof(float) * size_t(B) * kIdxHeads * nb_max);
+    const size_t part_floats = size_t(B) * kKvHeads * decode_parts(topk) * kGroup * (kDim + 2);
     w.total = align256(w.part + sizeof(float) * part_floats);
     return w;
 }
@@ -401,7 +402,6 @@ static msa_status decode_paged_impl(
     hipStream_t s = (hipStream_t)stream;
     uint8_t *base = (uint8_t *)workspace;
     float *S = (float *)(base + ws.scores);
-    int32_t *q2k = q2k_out ? q2k_out : (int32_t *)(base + ws.q2k);
     float *part = (float *)(base + ws.part);
     TimingScope tm;
     tm.mark(s, "decode_scores");
@@ -409,13 +409,10 @@ static msa_status decode_paged_impl(
                                         page_table, max_pages_per_seq, context_lens, batch,
                                         max_context_len, nb_max, S, s);
     if (e != hipSuccess) return hip_fail(e, "decode_scores");
-    tm.mark(s, "decode_topk");
-    e = launch_decode_topk(S, context_lens, batch, max_context_len, nb_max, topk, init_blocks,
-                           local_blocks, q2k, s);
-    if (e != hipSuccess) return hip_fail(e, "decode_topk");
     tm.mark(s, "decode_attend");
     e = launch_decode_attend(q, k_cache, v_cache, kv_fp8, k_scale, v_scale, page_table, max_pages_per_seq,
-                             context_lens, max_context_len, batch, q2k, topk, softmax_scale, part, s);
+                             context_lens, max_context_len, batch, S, nb_max, topk, init_blocks, local_blocks,
+                             softmax_scale, part, q2k_out, s);
     if (e != hipSuccess) return hip_fail(e, "decode_attend");
     tm.mark(s, "decode_combine");
     e = launch_decode_combine(part, batch, topk, kv_fp8, out, out_q, out_scale, s);

@@ -77,17 +77,19 @@ hipError_t launch_bwd_reduce(const float *part, const int32_t *chunk_off, const 
 hipError_t launch_decode_scores(const void *iq, const void *ikc, bool fp8, const int32_t *pt,
                                 int max_pages, const int32_t *ctx, int B, int max_ctx, int nb_max,
                                 float *S, hipStream_t stream);
-hipError_t launch_decode_topk(const float *S, const int32_t *ctx, int B, int max_ctx, int nb_max, int topk,
-                              int init, int local, int32_t *q2k, hipStream_t stream);
-// kc/vc: bf16 caches, or (fp8kv) E4M3FN caches dequantised as byte * k_scale / v_scale.
+// Selection of each (request, KV head) row from S, then the attention over
+// the selected blocks into ceil(topk/8) partials per row; q2k_out [4, B, topk]
+// is optional.  kc/vc: bf16 caches, or (fp8kv) E4M3FN caches dequantised as
+// byte * k_scale / v_scale.
 hipError_t launch_decode_attend(const uint16_t *q, const void *kc, const void *vc, bool fp8kv, float k_scale,
                                 float v_scale, const int32_t *pt, int max_pages, const int32_t *ctx,
-                                int max_ctx, int B, const int32_t *q2k, int topk, float scale,
-                                float *partial, hipStream_t stream);
+                                int max_ctx, int B, const float *S, int nb_max, int topk, int init, int local,
+                                float scale, float *partial, int32_t *q2k_out, hipStream_t stream);
 // bf16 output, or (out_q != NULL) its MXFP8 encoding: E4M3 [B, 64*128] and
 // E8M0 scales [B, 64*128/32].
 hipError_t launch_decode_combine(const float *partial, int B, int topk, bool fp8kv, uint16_t *out,
                                  uint8_t *out_q, uint8_t *out_scale, hipStream_t stream);
+int decode_parts(int topk);
 
 // Paged-cache insertion of n tokens' K, V and index-K rows (index-K stored
 // as bf16, or as unscaled E4M3 when fp8).
