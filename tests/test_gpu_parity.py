@@ -141,6 +141,30 @@ def test_decode_matches_oracle(case):
     assert np.all(np.isfinite(out.float().cpu().numpy())), "NaN from poisoned tail slots"
 
 
+@pytest.mark.parametrize("max_ctx,idt", [(1048576, "bf16"), (1048576, "fp8"), (262145, "bf16"),
+                                         (131073, "fp8")])
+def test_decode_context_bound_far_above_lengths(max_ctx, idt):
+    """max_context_len only bounds the grid and the per-lane candidate count
+    of the in-kernel top-k (up to 128 per lane at the largest supported
+    bound, 1048576): with the same short requests the outputs must equal,
+    bit for bit, those of the call with the tight bound, and the oracle."""
+    print(f"[decode bound] max_ctx={max_ctx} {idt}", flush=True)
+    lens = [1, 300, 4097, 9000]
+    d = W.make_decode(lens, 77, topk=16, init_blocks=1, local_blocks=1, index_dtype=idt)
+    wide = np.full((d.B, -(-max_ctx // 128)), -1, dtype=np.int32)
+    wide[:, :d.page_table.shape[1]] = d.page_table
+    args = (dev(d.q), dev(d.iq), dev(d.k_cache), dev(d.v_cache), dev(d.ik_cache))
+    out_w, q2k_w = msa.sparse_attend_decode_paged(*args, dev(wide), dev(d.context_lens), max_ctx, 16, 1,
+                                                  1, d.scale, return_q2k=True)
+    out_t, q2k_t = msa.sparse_attend_decode_paged(*args, dev(d.page_table), dev(d.context_lens),
+                                                  d.max_context_len, 16, 1, 1, d.scale, return_q2k=True)
+    assert torch.equal(q2k_w, q2k_t) and torch.equal(out_w, out_t)
+    ref = oracle.decode(d)
+    rows = check_selection(_tok_major(q2k_w), ref, 16, 1, 1).all(axis=1)
+    check_attention(out_w.float().cpu().numpy()[rows], ref["out"][rows],
+                    max_tol=2e-2 if idt == "bf16" else 5e-2, what=f"bound {max_ctx}")
+
+
 def test_decode_page_permutation_invariance():
     lens = [700, 1281, 256, 3000]
     a = W.make_decode(lens, 81, topk=5, identity_pages=True)
