@@ -296,7 +296,7 @@ def bench_prefill(args, hip, flush):
     kt = {}
     for arr in evs:
         for nm, (a, b) in {"doc_setup(select)": (0, 1), "block_scores": (1, 2), "topk_prefill": (2, 3),
-                           "doc_setup(attend)": (4, 5), "vt_transpose": (5, 6),
+                           "doc_setup(attend)": (4, 5), "kv_units": (5, 6),
                            "attend_prefill": (6, 7)}.items():
             kt.setdefault(nm, []).append(hip.elapsed_ms(arr[a], arr[b]))
     # algorithmic flops (causal index dots + selected-key attention)

@@ -7,9 +7,12 @@
 // q2k row (h/16, t).
 //
 // Two kernels:
-//   vt_transpose_kernel - V of every document re-laid per 32-key unit as
-//       V^T [unit][KV head][d][32 keys] (keys past the document end are 0),
-//       so that the PV operand is read from LDS with plain 16-byte reads.
+//   kv_units_kernel - K and V of every document re-laid per 32-key unit:
+//       V^T [unit][KV head][d][32 keys], so that the PV operand is read from
+//       LDS with plain 16-byte reads, and K [unit][KV head][32 keys][d], so
+//       that a unit's K rows of one head are 8 KiB contiguous (in the input
+//       they are 256 B apart from each other by the other heads' rows).  Keys
+//       past the document end are 0 in both.
 //   attend_prefill_kernel - workgroup = (KV head g, 16 consecutive tokens of
 //       one document inside one 128-token block, so all share the query
 //       block c); 8 waves, each owning 2 tokens x 16 heads.  The workgroup
@@ -178,21 +181,21 @@ __device__ __forceinline__ void attend_block(WaveState &st, const uint8_t *smem,
 }  // namespace
 
 namespace {
-// One block b < c for token t of a wave, read straight from memory (K rows
-// and V^T unit rows are contiguous in the MFMA operand layouts), unit by
+// One block b < c for token t of a wave, read straight from memory (the
+// per-unit K rows and V^T rows are contiguous in the MFMA operand layouts), unit by
 // unit with the lazy online softmax.  Used for blocks a single token of the
 // tile selected, which would otherwise hold the whole workgroup at a
 // barrier for one wave's work.
-__device__ __forceinline__ void attend_block_global(WaveState &st, int t, const uint16_t *__restrict__ k,
-                                                    const uint16_t *__restrict__ vt, int doc_start, int g,
+__device__ __forceinline__ void attend_block_global(WaveState &st, int t, const uint16_t *__restrict__ ku,
+                                                    const uint16_t *__restrict__ vt, int g,
                                                     int uoff, int b, int n, int grp, float scale_log2) {
 #pragma unroll 1
     for (int q = 0; q < kUnitsPerBlock; ++q) {
-        const int key_base = doc_start + b * kBlock + kAttnUnit * q;
         f32x4 sacc[2] = {f32x4{}, f32x4{}};
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
-            const uint16_t *src = k + (size_t(key_base + 8 * (n >> 2) + 4 * mt + (n & 3)) * kKvHeads + g) * kDim;
+            const uint16_t *src = ku + ((size_t(uoff + kUnitsPerBlock * b + q) * kKvHeads + g) * kAttnUnit +
+                                        8 * (n >> 2) + 4 * mt + (n & 3)) * kDim;
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks)
                 sacc[mt] = mfma_16x16x32(__builtin_bit_cast(bf16x8, *(const u32x4 *)(src + 8 * (4 * ks + grp))),
@@ -235,12 +238,13 @@ __device__ __forceinline__ void attend_block_global(WaveState &st, int t, const 
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// V -> per-unit V^T
+// K, V -> per-unit K and V^T
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void vt_transpose_kernel(const uint16_t *__restrict__ v,
-                                                           const DocSpan *__restrict__ docs,
-                                                           const int32_t *__restrict__ unit_off,
-                                                           int ndocs, uint16_t *__restrict__ vt) {
+__global__ __launch_bounds__(256) void kv_units_kernel(const uint16_t *__restrict__ k,
+                                                       const uint16_t *__restrict__ v,
+                                                       const DocSpan *__restrict__ docs,
+                                                       const int32_t *__restrict__ unit_off, int ndocs,
+                                                       uint16_t *__restrict__ ku, uint16_t *__restrict__ vt) {
     __shared__ uint16_t tile[kAttnUnit][kDim + 2];
     const int U = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
     if (U >= unit_off[ndocs]) return;
@@ -254,6 +258,10 @@ __global__ __launch_bounds__(256) void vt_transpose_kernel(const uint16_t *__res
         u32x4 x = {0u, 0u, 0u, 0u};
         if (key0 + r < doc.len)
             x = *(const u32x4 *)(v + (size_t(doc.start + key0 + r) * kKvHeads + g) * kDim + 8 * ch);
+        u32x4 kx = {0u, 0u, 0u, 0u};
+        if (key0 + r < doc.len)
+            kx = *(const u32x4 *)(k + (size_t(doc.start + key0 + r) * kKvHeads + g) * kDim + 8 * ch);
+        *(u32x4 *)(ku + ((size_t(U) * kKvHeads + g) * kAttnUnit + r) * kDim + 8 * ch) = kx;
         uint32_t *dst = (uint32_t *)&tile[r][8 * ch];  // 4-byte aligned (row pitch 260 B)
         dst[0] = x[0];
         dst[1] = x[1];
@@ -279,7 +287,7 @@ __global__ __launch_bounds__(256) void vt_transpose_kernel(const uint16_t *__res
 // attention
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void attend_prefill_kernel(
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ vt,
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ ku, const uint16_t *__restrict__ vt,
     const int32_t *__restrict__ q2k, int topk, const DocSpan *__restrict__ docs,
     const int32_t *__restrict__ tile_off, const int32_t *__restrict__ unit_off, int ndocs, int T,
     float scale_log2, uint16_t *__restrict__ out, float *__restrict__ lse) {
@@ -372,7 +380,7 @@ __global__ __launch_bounds__(kThreads) void attend_prefill_kernel(
             const int um = __builtin_amdgcn_readfirstlane(s_umask[u]);
             const int b = __builtin_amdgcn_readfirstlane(s_ublk[u]);
             if (!(um & bit) || b == c || __popc(um) >= kSharedMin) continue;
-            attend_block_global(st, t, k, vt, doc.start, g, uoff, b, n, grp, scale_log2);
+            attend_block_global(st, t, ku, vt, g, uoff, b, n, grp, scale_log2);
         }
     }
 
@@ -385,17 +393,16 @@ __global__ __launch_bounds__(kThreads) void attend_prefill_kernel(
     // ---- HBM -> LDS unit copies: 16 one-KiB copies per unit.  Copy i < 8
     // fills K rows 4i..4i+3 (lane l: row 4i + l/16, slot position l%16, i.e.
     // chunk (l%16) ^ kswz(row)); copy i >= 8 fills V^T rows 16(i-8)..+15
-    // (lane l: row 16(i-8) + l/4, chunk (l%4) ^ vswz(row)).  K rows past the
-    // last query of the tile are never attended: they re-read row p_last so
-    // that no load leaves the document.
+    // (lane l: row 16(i-8) + l/4, chunk (l%4) ^ vswz(row)).  Both come from
+    // the per-unit copies, whose rows past the document end are zero.
     auto issue_copy = [&](int vu, int ub, int i) {
         const int qq = vu & 3;
         uint8_t *slot = smem + (vu % kRing) * kUnitBytes;
         if (i < 8) {
             const int r = 4 * i + (lane >> 4);
             const int ch = (lane & 15) ^ kswz(r);
-            const int kp = min(ub * kBlock + qq * kAttnUnit + r, p_last);
-            const uint16_t *src = k + (size_t(doc.start + kp) * kKvHeads + g) * kDim + 8 * ch;
+            const size_t unit = size_t(uoff + ub * kUnitsPerBlock + qq);
+            const uint16_t *src = ku + ((unit * kKvHeads + g) * kAttnUnit + r) * kDim + 8 * ch;
             copy_to_lds(src, slot + i * 1024);
         } else {
             const int jv = i - 8;
@@ -481,27 +488,31 @@ __global__ __launch_bounds__(kThreads) void attend_prefill_kernel(
     }
 }
 
-size_t prefill_vt_bytes(int T, int ndocs) {
-    return (size_t(ceil_div(T, kAttnUnit)) + size_t(ndocs)) * kKvHeads * kDim * kAttnUnit * 2;
+// V^T per unit, then K per unit [unit][KV head][32 keys][d] (same size)
+static size_t unit_elems(int T, int ndocs) {
+    return (size_t(ceil_div(T, kAttnUnit)) + size_t(ndocs)) * kKvHeads * kDim * kAttnUnit;
 }
 
-hipError_t launch_vt_transpose(const uint16_t *v, const DocSpan *docs, const int32_t *unit_off,
-                               int ndocs, int T, uint16_t *vt, hipStream_t stream) {
+size_t prefill_units_bytes(int T, int ndocs) { return 2 * unit_elems(T, ndocs) * 2; }
+
+hipError_t launch_kv_units(const uint16_t *k, const uint16_t *v, const DocSpan *docs,
+                           const int32_t *unit_off, int ndocs, int T, uint16_t *vt, hipStream_t stream) {
     const int max_units = ceil_div(T, kAttnUnit) + ndocs;  // document-aligned units (upper bound)
-    hipLaunchKernelGGL(vt_transpose_kernel, dim3(max_units, kKvHeads), dim3(256), 0, stream, v, docs,
-                       unit_off, ndocs, vt);
+    hipLaunchKernelGGL(kv_units_kernel, dim3(max_units, kKvHeads), dim3(256), 0, stream, k, v, docs,
+                       unit_off, ndocs, vt + unit_elems(T, ndocs), vt);
     return hipGetLastError();
 }
 
-hipError_t launch_attend_prefill(const uint16_t *q, const uint16_t *k, const uint16_t *vt,
+hipError_t launch_attend_prefill(const uint16_t *q, const uint16_t *vt,
                                  const int32_t *q2k, int topk, const DocSpan *docs,
                                  const int32_t *tile_off, const int32_t *unit_off, int ndocs, int T,
                                  float scale, uint16_t *out, float *lse, hipStream_t stream) {
     const int max_tiles = ceil_div(T, kTok) + ndocs;  // document-aligned tiles (upper bound)
     const int grid = 8 * 8 * ceil_div(max_tiles, 16);  // 8 XCDs x slots
     const size_t lds = size_t(kRing) * kUnitBytes;
-    hipLaunchKernelGGL(attend_prefill_kernel, dim3(grid), dim3(kThreads), lds, stream, q, k, vt, q2k,
-                       topk, docs, tile_off, unit_off, ndocs, T, scale * kLog2e, out, lse);
+    hipLaunchKernelGGL(attend_prefill_kernel, dim3(grid), dim3(kThreads), lds, stream, q,
+                       vt + unit_elems(T, ndocs), vt, q2k, topk, docs, tile_off, unit_off, ndocs, T,
+                       scale * kLog2e, out, lse);
     return hipGetLastError();
 }
 

@@ -84,7 +84,7 @@ PrefillWs prefill_layout(int T, int ndocs) {
     w.off = align256(sizeof(DocSpan) * size_t(ndocs));
     w.uoff = align256(w.off + sizeof(int32_t) * (size_t(ndocs) + 1));
     w.vt = align256(w.uoff + sizeof(int32_t) * (size_t(ndocs) + 1));
-    w.total = align256(w.vt + prefill_vt_bytes(T, ndocs));
+    w.total = align256(w.vt + prefill_units_bytes(T, ndocs));
     return w;
 }
 
@@ -280,11 +280,11 @@ static msa_status prefill_impl(const uint16_t *q, const uint16_t *k, const uint1
     hipError_t e = launch_doc_setup(cu_seqlens, num_docs, total_tokens, max_seqlen, kAttnTile,
                                     kAttnUnit, docs, off, uoff, s);
     if (e != hipSuccess) return hip_fail(e, "doc_setup");
-    tm.mark(s, "vt_transpose");
-    e = launch_vt_transpose(v, docs, uoff, num_docs, total_tokens, vt, s);
-    if (e != hipSuccess) return hip_fail(e, "vt_transpose");
+    tm.mark(s, "kv_units");
+    e = launch_kv_units(k, v, docs, uoff, num_docs, total_tokens, vt, s);
+    if (e != hipSuccess) return hip_fail(e, "kv_units");
     tm.mark(s, "attend_prefill");
-    e = launch_attend_prefill(q, k, vt, q2k, topk, docs, off, uoff, num_docs, total_tokens,
+    e = launch_attend_prefill(q, vt, q2k, topk, docs, off, uoff, num_docs, total_tokens,
                               softmax_scale, out, lse, s);
     if (e != hipSuccess) return hip_fail(e, "attend_prefill");
     tm.mark(s, nullptr);

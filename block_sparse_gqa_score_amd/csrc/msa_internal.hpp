@@ -32,13 +32,13 @@ hipError_t launch_topk_prefill(const float *S, const DocSpan *docs, int ndocs, i
                                int topk, int init, int local, int32_t *q2k, hipStream_t stream);
 
 // Sparse GQA prefill attention: V re-laid as per-unit V^T (unit_off = prefix
-// count of kAttnUnit-key units per document; vt holds prefill_vt_bytes),
+// count of kAttnUnit-key units per document; vt holds prefill_units_bytes),
 // then the attention kernel over K and V^T.
-size_t prefill_vt_bytes(int T, int ndocs);
-hipError_t launch_vt_transpose(const uint16_t *v, const DocSpan *docs, const int32_t *unit_off,
-                               int ndocs, int T, uint16_t *vt, hipStream_t stream);
+size_t prefill_units_bytes(int T, int ndocs);
+hipError_t launch_kv_units(const uint16_t *k, const uint16_t *v, const DocSpan *docs,
+                               const int32_t *unit_off, int ndocs, int T, uint16_t *vt, hipStream_t stream);
 // lse (optional, NULL to skip): natural-log log-sum-exp of every row [T,64].
-hipError_t launch_attend_prefill(const uint16_t *q, const uint16_t *k, const uint16_t *vt,
+hipError_t launch_attend_prefill(const uint16_t *q, const uint16_t *vt,
                                  const int32_t *q2k, int topk, const DocSpan *docs,
                                  const int32_t *tile_off, const int32_t *unit_off, int ndocs, int T,
                                  float scale, uint16_t *out, float *lse, hipStream_t stream);
