@@ -407,6 +407,19 @@ def measured_traffic(kernel):
         return None
 
 
+def measured_counter(kernel, field):
+    """A per-dispatch counter figure of `kernel` (e.g. mfma_busy_frac) from the
+    committed counter summary, or None when absent or stale."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            e = json.load(f)["kernels"][kernel]
+        if source_digest(e["source"]) != e["source_sha"]:
+            return None
+        return e[field]
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def calibrate_copy():
     import torch
     n = 1 << 30
@@ -507,9 +520,11 @@ def main():
                          "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(pres["attn_flops"] / (a_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                          "traffic": measured_traffic("attend_prefill"), "alg_flops_per_launch": pres["attn_flops"],
-                         "avg_launch_us": round(a_ms * 1e3, 3)},
+                         "avg_launch_us": round(a_ms * 1e3, 3),
+                         "mfma_busy_counter": measured_counter("attend_prefill", "mfma_busy_frac")},
             "block_scores": {"achieved_tflops": round(pres["score_flops"] / (s_ms * 1e-3) / 1e12, 2),
-                             "frac": round(pres["score_flops"] / (s_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+                             "frac": round(pres["score_flops"] / (s_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                             "mfma_busy_counter": measured_counter("block_scores", "mfma_busy_frac")},
         }
         if not args.no_backward:
             bres = bench_backward(args, hip, flush, pres)
