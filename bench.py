@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E, GB/s
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, TFLOP/s
+PEAK_FP8_TFLOPS = 5000.0        # MI355X dense fp8 MFMA, TFLOP/s
 
 
 def parse():
@@ -48,6 +49,8 @@ def parse():
                     help="only run a plain 1 GiB device copy (reference dispatch for scaling the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
     ap.add_argument("--no-backward", action="store_true", help="skip the prefill backward leg")
+    ap.add_argument("--no-fp8-decode", action="store_true",
+                    help="skip the E4M3-indexer decode leg (8 requests of 131072 tokens)")
     ap.add_argument("--no-graph", action="store_true",
                     help="time direct launches only (default: the decode step is also captured "
                          "into a HIP graph and the replay time is the headline value)")
@@ -310,6 +313,117 @@ def bench_prefill(args, hip, flush):
                 score_flops=score_flops, attn_flops=attn_flops, q2k=q2k, out=out)
 
 
+def bench_select_fp8(args, hip, flush, pres):
+    """The 32k planted prefill's selection with the index q/k as E4M3FN bytes
+    (unscaled; the RMS-normalised values lie far inside E4M3's range): the
+    block scorer's E4M3 MFMA variant, timed like the bf16 one."""
+    import torch
+    import block_sparse_gqa_score_amd as msa
+    w = pres["w"]
+    fiq = dev(w.iq).float().to(torch.float8_e4m3fn).view(torch.uint8)
+    fik = dev(w.ik).float().to(torch.float8_e4m3fn).view(torch.uint8)
+    cu = dev(w.cu_seqlens)
+    ws_s = torch.empty(msa.select_blocks_workspace_bytes(w.T, w.num_docs, w.max_seqlen),
+                       dtype=torch.uint8, device="cuda")
+    q2k = torch.empty((4, w.T, w.topk), dtype=torch.int32, device="cuda")
+    L = msa.lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+
+    def run(events):
+        if events is not None:
+            L.msa_set_timing_events(ctypes.c_void_p(ctypes.addressof(events)), 4)
+        st = L.msa_select_blocks(P(fiq), P(fik), 1, P(cu), w.num_docs, w.T, w.max_seqlen, w.topk,
+                                 w.init_blocks, w.local_blocks, P(q2k), None, P(ws_s), ws_s.numel(),
+                                 ctypes.c_void_p(stream))
+        if st != 0:
+            raise RuntimeError(L.msa_last_error().decode())
+
+    step_ms, evs, names = timed_steps(run, args.prefill_steps, args.warmup, hip, stream, flush, 4)
+    kt = {k: stats(v)["mean"] for k, v in kernel_times(evs, [names], hip).items()}
+    s_ms = kt["block_scores"]
+    return {"index_dtype": "e4m3 (unscaled)", "select_ms": round(stats(step_ms)["mean"], 4),
+            "per_kernel_us": {k: round(v * 1e3, 3) for k, v in kt.items()},
+            "achieved_tflops": round(pres["score_flops"] / (s_ms * 1e-3) / 1e12, 2),
+            "peak": PEAK_FP8_TFLOPS,
+            "frac": round(pres["score_flops"] / (s_ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
+            "mfma_busy_counter": measured_counter("block_scores_fp8", "mfma_busy_frac")}
+
+
+def bench_decode_fp8_indexer(args, hip, flush):
+    """Decode with the E4M3 indexer at long context: 8 requests of 131072
+    tokens (1024 pages each, physical pages a random permutation), bf16 K/V,
+    topk 16.  A timing leg: the inputs are drawn on the GPU from a seeded
+    torch generator with the distributions of the parity workload (K/V and
+    q ~N(0,1) bf16, index q/k RMS-normalised Gaussians as E4M3FN bytes);
+    parity at this size is covered by the GPU tests on the numpy inputs."""
+    import torch
+    import block_sparse_gqa_score_amd as msa
+    B, Lc, topk = 8, 131072, 16
+    npg = Lc // 128
+    P_ = B * npg
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1004)
+
+    def rms_fp8(shape):
+        z = torch.randn(shape, generator=g, device="cuda", dtype=torch.float32)
+        z = z / torch.sqrt((z * z).mean(dim=-1, keepdim=True) + 1e-6)
+        return z.to(torch.float8_e4m3fn).view(torch.uint8)
+
+    kc = torch.randn((P_ * 128, 4, 128), generator=g, device="cuda", dtype=torch.bfloat16)
+    vc = torch.randn((P_ * 128, 4, 128), generator=g, device="cuda", dtype=torch.bfloat16)
+    ikc = rms_fp8((P_ * 128, 1, 128))
+    q = torch.randn((B, 64, 128), generator=g, device="cuda", dtype=torch.bfloat16)
+    iq = rms_fp8((B, 4, 128))
+    pt = torch.randperm(P_, generator=g, device="cuda").to(torch.int32).reshape(B, npg).contiguous()
+    ctx = torch.full((B,), Lc, dtype=torch.int32, device="cuda")
+    out = torch.empty((B, 64, 128), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(msa.decode_workspace_bytes(B, Lc, topk), dtype=torch.uint8, device="cuda")
+    L = msa.lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    scale = 1.0 / 128 ** 0.5
+
+    def call(strm):
+        return L.msa_sparse_attend_decode_paged(P(q), P(iq), P(kc), P(vc), P(ikc), 1, P(pt), npg, P(ctx), B,
+                                                Lc, topk, 0, 1, scale, P(out), None, P(ws), ws.numel(), strm)
+
+    def run(events):
+        if events is not None:
+            L.msa_set_timing_events(ctypes.c_void_p(ctypes.addressof(events)), len(events))
+        if call(ctypes.c_void_p(stream)) != 0:
+            raise RuntimeError(L.msa_last_error().decode())
+
+    step_ms, evs, names = timed_steps(run, args.steps, args.warmup, hip, stream, flush, 4)
+    kt = {k: stats(v)["mean"] for k, v in kernel_times(evs, [names], hip).items()}
+    graph = None
+    if not args.no_graph:
+        graph = graph_replay_ms(lambda: call(ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)),
+                                torch.cuda.Stream(), args.steps, hip, stream, flush)
+    idx_bytes = B * Lc * 128 + B * 4 * 128 + B * npg * 4
+    kv_bytes = B * 4 * 512 * keys_of(Lc, topk)
+    s_ms = kt["decode_scores"]
+    a_ms = kt["decode_attend"]
+    step = (graph or stats(step_ms))["median"]
+    return {"workload": "decode_fp8idx_b8_ctx128k", "batch": B, "context": Lc, "topk": topk,
+            "index_dtype": "e4m3 (unscaled)", "step_us": round(step * 1e3, 3),
+            "launch": "hip_graph_replay" if graph is not None else "direct",
+            "direct_step_us": round(stats(step_ms)["median"] * 1e3, 3),
+            "per_kernel_us": {k: round(v * 1e3, 3) for k, v in kt.items()},
+            "path_bytes_per_step": idx_bytes + kv_bytes + 2 * B * 64 * 128 * 2,
+            "scores_roofline": {"bound": "hbm", "achieved": round(idx_bytes / (s_ms * 1e-3) / 1e9, 1),
+                                "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                "frac": round(idx_bytes / (s_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                                "alg_bytes_per_launch": idx_bytes,
+                                "traffic": measured_traffic("decode_scores_fp8"),
+                                "avg_launch_us": round(s_ms * 1e3, 3)},
+            "attend_roofline": {"bound": "hbm", "achieved": round(kv_bytes / (a_ms * 1e-3) / 1e9, 1),
+                                "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                "frac": round(kv_bytes / (a_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                                "alg_bytes_per_launch": kv_bytes, "avg_launch_us": round(a_ms * 1e3, 3)},
+            "data": "seeded torch generator on the GPU (timing leg)"}
+
+
 def bench_backward(args, hip, flush, pres):
     """Training leg on the 32k planted prefill: the forward with log-sum-exp,
     then the backward (dq, dk, dv) for the selection the GPU made."""
@@ -526,6 +640,7 @@ def main():
                              "frac": round(pres["score_flops"] / (s_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                              "mfma_busy_counter": measured_counter("block_scores", "mfma_busy_frac")},
         }
+        line["prefill_32k"]["block_scores_fp8"] = bench_select_fp8(args, hip, flush, pres)
         if not args.no_backward:
             bres = bench_backward(args, hip, flush, pres)
             b_ms = bres["step"]["mean"]
@@ -545,6 +660,8 @@ def main():
                 "bwd_dkdv_tflops": round(2.0 * pres["attn_flops"] / (pk["bwd_dkdv"] * 1e-3) / 1e12, 2),
                 "train_attention_ms": round(b_ms + pres["per_kernel_ms"]["attend_prefill"], 3),
             }
+    if not args.no_fp8_decode:
+        line["decode_fp8_indexer"] = bench_decode_fp8_indexer(args, hip, flush)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_decode(d, args.cpu_seconds)
         if not args.no_prefill:

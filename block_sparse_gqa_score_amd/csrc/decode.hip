@@ -13,7 +13,8 @@
 //   decode_scores_kernel - E4M3 index keys: one wave per (request, page),
 //       MFMA 16x16x128 with unit scales.
 //   decode_attend_stream_kernel - one workgroup per 8 selected slots of a
-//       (KV head, request).  Each wave first selects the row's blocks from
+//       (KV head, request) (fewer for small batches, so the grid still
+//       covers the CUs).  Each wave first selects the row's blocks from
 //       the scores (the R-th largest score found by bisection on
 //       order-preserving score bits with wave-wide counts, then an ascending
 //       ballot-compacted emit; ties go to the lower block id; forced
@@ -271,15 +272,37 @@ __device__ __forceinline__ void select_row(const float *__restrict__ srow, int c
         const int b = lane + 64 * i;
         u[i] = (b <= c && !is_forced(b, c, init, local)) ? max(float_order_bits(srow[b]), 1u) : 0u;
     }
-    // largest x with #{u >= x} >= R (the R-th largest order value)
+    // largest x with #{u >= x} >= R (the R-th largest order value), bisected
+    // on the high 16 bits first.  When exactly R candidates reach that
+    // prefix, the R-th largest is their minimum; otherwise (ties in the
+    // prefix) the bisection continues over the low 16 bits.
     uint32_t thr = 0;
     if (R > 0) {
-        for (int bit = 31; bit >= 0; --bit) {
+        for (int bit = 31; bit >= 16; --bit) {
             const uint32_t trial = thr | (1u << bit);
             int cnt = 0;
 #pragma unroll
             for (int i = 0; i < kCpl; ++i) cnt += wave_count(u[i] >= trial);
             if (cnt >= R) thr = trial;
+        }
+        int ge = 0;
+#pragma unroll
+        for (int i = 0; i < kCpl; ++i) ge += wave_count(u[i] >= thr);
+        if (ge == R) {
+            uint32_t mn = 0xFFFFFFFFu;
+#pragma unroll
+            for (int i = 0; i < kCpl; ++i) mn = u[i] >= thr ? min(mn, u[i]) : mn;
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) mn = min(mn, uint32_t(__shfl_xor(int(mn), o)));
+            thr = mn;
+        } else {
+            for (int bit = 15; bit >= 0; --bit) {
+                const uint32_t trial = thr | (1u << bit);
+                int cnt = 0;
+#pragma unroll
+                for (int i = 0; i < kCpl; ++i) cnt += wave_count(u[i] >= trial);
+                if (cnt >= R) thr = trial;
+            }
         }
     }
     int n_gt = 0;
@@ -335,7 +358,7 @@ __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
 // G6: streaming attention, one workgroup per 8 slots of a row
 // ---------------------------------------------------------------------------
 namespace {
-constexpr int kStreamSlots = 8;  // selected slots per workgroup
+constexpr int kStreamSlots = 8;  // selected slots per workgroup (at most)
 // Per wave: two stages of one block's K rows + V rows (bf16: 2 x 16 KiB;
 // E4M3: 2 x 8 KiB of bytes plus an 8 KiB bf16 V buffer for the transposing
 // reads).
@@ -357,7 +380,8 @@ __device__ __forceinline__ void stream_copy(const void *src, uint8_t *lds_dst) {
 }
 }  // namespace
 
-// Workgroup (sg, g, r): slots 8sg .. 8sg+7 of row (KV head g, request r);
+// Workgroup (sg, g, r): slots spw*sg .. spw*sg+spw-1 of row (KV head g,
+// request r), spw <= 8 slots per workgroup;
 // 4 waves, wave w owns keys 32w..32w+31 of every selected block.  Each wave
 // streams its K and V rows of the next block into its own 2-stage LDS ring
 // while it computes the current one (no workgroup barrier until the end):
@@ -375,7 +399,7 @@ template <bool kFp8Kv, int kCpl>
 __global__ __launch_bounds__(256) void decode_attend_stream_kernel(
     const uint16_t *__restrict__ q, const void *__restrict__ kc_, const void *__restrict__ vc_,
     const int32_t *__restrict__ pt, int max_pages, const int32_t *__restrict__ ctx, int max_ctx, int B,
-    const float *__restrict__ S, int nb_max, int topk, int init, int local, int nparts, float scale_log2,
+    const float *__restrict__ S, int nb_max, int topk, int init, int local, int spw, int nparts, float scale_log2,
     float v_scale, float *__restrict__ part_o, float *__restrict__ part_ml, int32_t *__restrict__ q2k_out) {
     using SL = StreamLayout<kFp8Kv>;
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];  // 4 waves x 2 stages x (K, V)
@@ -406,8 +430,8 @@ __global__ __launch_bounds__(256) void decode_attend_stream_kernel(
     int bsel[kStreamSlots];
 #pragma unroll
     for (int j = 0; j < kStreamSlots; ++j) {
-        const int s = sg * kStreamSlots + j;
-        const int b = s < topk ? __builtin_amdgcn_readfirstlane(s_sel[wave][s]) : -1;
+        const int s = sg * spw + j;
+        const int b = (j < spw && s < topk) ? __builtin_amdgcn_readfirstlane(s_sel[wave][s]) : -1;
         bsel[j] = (b >= 0 && b <= c) ? b : -1;
     }
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): q is in before any copy is issued
@@ -665,13 +689,23 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float *__restr
 }
 
 // partials per (request, KV head): one per attention workgroup (8 slots)
-int decode_parts(int topk) { return ceil_div(topk, kStreamSlots); }
+// Selected slots per attention workgroup: 8, or fewer when the batch is too
+// small for (requests x KV heads x ceil(topk/8)) workgroups to cover the 256
+// CUs (at batch 8, topk 16: 2 slots, 256 workgroups instead of 64).
+int decode_slots_per_wg(int topk, int B) {
+    int spw = kStreamSlots;
+    while (spw > 1 && B * kKvHeads * ceil_div(topk, spw) < 256) spw >>= 1;
+    return spw;
+}
+
+int decode_parts(int topk, int B) { return ceil_div(topk, decode_slots_per_wg(topk, B)); }
 
 hipError_t launch_decode_attend(const uint16_t *q, const void *kc, const void *vc, bool fp8kv, float k_scale,
                                 float v_scale, const int32_t *pt, int max_pages, const int32_t *ctx,
                                 int max_ctx, int B, const float *S, int nb_max, int topk, int init, int local,
                                 float scale, float *partial, int32_t *q2k_out, hipStream_t stream) {
-    const int nparts = decode_parts(topk);
+    const int spw = decode_slots_per_wg(topk, B);
+    const int nparts = ceil_div(topk, spw);
     float *part_o = partial;
     float *part_ml = partial + size_t(B) * kKvHeads * nparts * kGroup * kDim;
     const dim3 grid(nparts, kKvHeads, B);
@@ -681,12 +715,12 @@ hipError_t launch_decode_attend(const uint16_t *q, const void *kc, const void *v
         if (fp8kv)                                                                                           \
             hipLaunchKernelGGL((decode_attend_stream_kernel<true, N>), grid, dim3(256),                      \
                                size_t(4) * StreamLayout<true>::kWave, stream, q, kc, vc, pt, max_pages, ctx, \
-                               max_ctx, B, S, nb_max, topk, init, local, nparts, scale * kLog2e * k_scale,   \
+                               max_ctx, B, S, nb_max, topk, init, local, spw, nparts, scale * kLog2e * k_scale, \
                                v_scale, part_o, part_ml, q2k_out);                                          \
         else                                                                                                 \
             hipLaunchKernelGGL((decode_attend_stream_kernel<false, N>), grid, dim3(256),                     \
                                size_t(4) * StreamLayout<false>::kWave, stream, q, kc, vc, pt, max_pages, ctx, \
-                               max_ctx, B, S, nb_max, topk, init, local, nparts, scale * kLog2e, 1.0f,       \
+                               max_ctx, B, S, nb_max, topk, init, local, spw, nparts, scale * kLog2e, 1.0f,  \
                                part_o, part_ml, q2k_out);                                                   \
         return hipGetLastError();                                                                            \
     }
@@ -704,7 +738,7 @@ hipError_t launch_decode_attend(const uint16_t *q, const void *kc, const void *v
 
 hipError_t launch_decode_combine(const float *partial, int B, int topk, bool fp8kv, uint16_t *out,
                                  uint8_t *out_q, uint8_t *out_scale, hipStream_t stream) {
-    topk = decode_parts(topk);  // partials per (request, KV head)
+    topk = decode_parts(topk, B);  // partials per (request, KV head)
     const float *part_o = partial;
     const float *part_ml = partial + size_t(B) * kKvHeads * topk * kGroup * kDim;
     if (out_q)

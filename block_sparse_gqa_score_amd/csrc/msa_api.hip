@@ -130,7 +130,7 @@ DecodeWs decode_layout(int B, int max_ctx, int topk) {
     const int nb_max = ceil_div(max_ctx, kBlock);
     w.scores = 0;
     w.part = align256(sizeof(float) * size_t(B) * kIdxHeads * nb_max);
-    const size_t part_floats = size_t(B) * kKvHeads * decode_parts(topk) * kGroup * (kDim + 2);
+    const size_t part_floats = size_t(B) * kKvHeads * decode_parts(topk, B) * kGroup * (kDim + 2);
     w.total = align256(w.part + sizeof(float) * part_floats);
     return w;
 }

@@ -89,7 +89,7 @@ hipError_t launch_decode_attend(const uint16_t *q, const void *kc, const void *v
 // E8M0 scales [B, 64*128/32].
 hipError_t launch_decode_combine(const float *partial, int B, int topk, bool fp8kv, uint16_t *out,
                                  uint8_t *out_q, uint8_t *out_scale, hipStream_t stream);
-int decode_parts(int topk);
+int decode_parts(int topk, int B);  // attention partials per (request, KV head)
 
 // Paged-cache insertion of n tokens' K, V and index-K rows (index-K stored
 // as bf16, or as unscaled E4M3 when fp8).

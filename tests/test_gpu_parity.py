@@ -165,6 +165,29 @@ def test_decode_context_bound_far_above_lengths(max_ctx, idt):
                     max_tol=2e-2 if idt == "bf16" else 5e-2, what=f"bound {max_ctx}")
 
 
+@pytest.mark.parametrize("pattern", ["constant", "two_level"])
+def test_decode_tied_scores_take_lowest_ids(pattern):
+    """Index keys built so that many blocks share the same maximum score:
+    every block ("constant") or two groups of blocks ("two_level").  The
+    selection must equal the oracle's exactly: ties go to the lower block id,
+    which exercises the top-k's bisection past a shared score prefix."""
+    print(f"[decode ties] {pattern}", flush=True)
+    lens = [130, 2000, 5000, 9000, 4097]
+    d = W.make_decode(lens, 303, topk=8, init_blocks=1, local_blocks=1)
+    row_a, row_b = d.ik_cache[0].copy(), d.ik_cache[1].copy()  # first slots: never poisoned
+    for r, L in enumerate(lens):
+        for pg in range(-(-L // 128)):
+            slot0 = int(d.page_table[r, pg]) * 128
+            row = row_b if (pattern == "two_level" and pg % 3 == 0) else row_a
+            d.ik_cache[slot0:slot0 + 128] = row
+    out, q2k = msa.sparse_attend_decode_paged(
+        dev(d.q), dev(d.iq), dev(d.k_cache), dev(d.v_cache), dev(d.ik_cache), dev(d.page_table),
+        dev(d.context_lens), d.max_context_len, d.topk, 1, 1, d.scale, return_q2k=True)
+    ref = oracle.decode(d)
+    assert np.array_equal(_tok_major(q2k), ref["q2k"])
+    check_attention(out.float().cpu().numpy(), ref["out"], what=f"ties {pattern}")
+
+
 def test_decode_page_permutation_invariance():
     lens = [700, 1281, 256, 3000]
     a = W.make_decode(lens, 81, topk=5, identity_pages=True)
