@@ -260,18 +260,38 @@ __device__ __forceinline__ int wave_count(bool pred) { return __popcll(__ballot(
 // Selection for one (request, index head) row by one wave: forced blocks
 // plus the R = topk - forced highest-scoring candidates (ties to the lower
 // block id), ascending, then -1.  The R-th largest order value is found by
-// bisection on its bits with wave-wide counts; out may be global or LDS.
+// bisection on its bits with wave-wide counts.  out holds kMaxTopk + 64
+// entries: the row, then a dump slot per lane.
 template <int kCpl>  // candidates per lane: blocks lane + 64*i
-__device__ __forceinline__ void select_row(const float *__restrict__ srow, int c, int topk, int init,
-                                           int local, int lane, int32_t *out) {
+__device__ __forceinline__ void select_row(const float *__restrict__ srow, int nb_max, int c, int topk,
+                                           int init, int local, int lane, int32_t *out) {
     const int R = topk - forced_count(c, init, local);
+    // Every lane loads all its entries of the row at once (the index clamped
+    // into the row; entries past c are never candidates): a conditional load
+    // per candidate would wait for each in turn.
+    float sv[kCpl];
+#pragma unroll
+    for (int i = 0; i < kCpl; ++i) sv[i] = srow[min(lane + 64 * i, nb_max - 1)];
     // order bits of each non-forced candidate; 0 marks "not a candidate"
     uint32_t u[kCpl];
 #pragma unroll
     for (int i = 0; i < kCpl; ++i) {
         const int b = lane + 64 * i;
-        u[i] = (b <= c && !is_forced(b, c, init, local)) ? max(float_order_bits(srow[b]), 1u) : 0u;
+        u[i] = (b <= c && !is_forced(b, c, init, local)) ? max(float_order_bits(sv[i]), 1u) : 0u;
     }
+    // Number of candidates >= x over the wave: each lane counts its own, and
+    // the lane counts (< 2^kBits) are summed one bit at a time with ballots.
+    constexpr int kBits = kCpl < 2 ? 1 : kCpl < 4 ? 2 : kCpl < 8 ? 3 : kCpl < 16 ? 4 : kCpl < 32 ? 5
+                        : kCpl < 64 ? 6 : kCpl < 128 ? 7 : 8;
+    auto count_ge = [&](uint32_t x) {
+        int cl = 0;
+#pragma unroll
+        for (int i = 0; i < kCpl; ++i) cl += u[i] >= x ? 1 : 0;
+        int tot = 0;
+#pragma unroll
+        for (int k = 0; k < kBits; ++k) tot += wave_count((cl >> k) & 1) << k;
+        return tot;
+    };
     // largest x with #{u >= x} >= R (the R-th largest order value), bisected
     // on the high 16 bits first.  When exactly R candidates reach that
     // prefix, the R-th largest is their minimum; otherwise (ties in the
@@ -280,15 +300,9 @@ __device__ __forceinline__ void select_row(const float *__restrict__ srow, int c
     if (R > 0) {
         for (int bit = 31; bit >= 16; --bit) {
             const uint32_t trial = thr | (1u << bit);
-            int cnt = 0;
-#pragma unroll
-            for (int i = 0; i < kCpl; ++i) cnt += wave_count(u[i] >= trial);
-            if (cnt >= R) thr = trial;
+            if (count_ge(trial) >= R) thr = trial;
         }
-        int ge = 0;
-#pragma unroll
-        for (int i = 0; i < kCpl; ++i) ge += wave_count(u[i] >= thr);
-        if (ge == R) {
+        if (count_ge(thr) == R) {
             uint32_t mn = 0xFFFFFFFFu;
 #pragma unroll
             for (int i = 0; i < kCpl; ++i) mn = u[i] >= thr ? min(mn, u[i]) : mn;
@@ -298,21 +312,16 @@ __device__ __forceinline__ void select_row(const float *__restrict__ srow, int c
         } else {
             for (int bit = 15; bit >= 0; --bit) {
                 const uint32_t trial = thr | (1u << bit);
-                int cnt = 0;
-#pragma unroll
-                for (int i = 0; i < kCpl; ++i) cnt += wave_count(u[i] >= trial);
-                if (cnt >= R) thr = trial;
+                if (count_ge(trial) >= R) thr = trial;
             }
         }
     }
-    int n_gt = 0;
-    if (R > 0) {
-#pragma unroll
-        for (int i = 0; i < kCpl; ++i) n_gt += wave_count(u[i] > thr);
-    }
+    const int n_gt = (R > 0 && thr != 0xFFFFFFFFu) ? count_ge(thr + 1u) : 0;  // #{u > thr}
     const int ties_wanted = R > 0 ? R - n_gt : 0;  // equal-to-threshold picks, lowest ids first
     int ties_seen = 0, emitted = 0;
     const uint64_t below = (1ull << lane) - 1ull;
+    // ascending emit; a lane that takes nothing writes its own dump slot
+    // out[kMaxTopk + lane], so the stores need no branch
 #pragma unroll
     for (int i = 0; i < kCpl; ++i) {
         const int b = lane + 64 * i;
@@ -324,7 +333,7 @@ __device__ __forceinline__ void select_row(const float *__restrict__ srow, int c
         const bool take = forced || (R > 0 && u[i] != 0 && (u[i] > thr || (tie && tie_rank < ties_wanted)));
         const uint64_t take_mask = __ballot(take);
         const int pos = emitted + __popcll(take_mask & below);
-        if (take && pos < topk) out[pos] = b;
+        out[(take && pos < topk) ? pos : kMaxTopk + lane] = b;
         emitted += __popcll(take_mask);
     }
     for (int i = emitted + lane; i < topk; i += 64) out[i] = -1;
@@ -404,7 +413,7 @@ __global__ __launch_bounds__(256) void decode_attend_stream_kernel(
     using SL = StreamLayout<kFp8Kv>;
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];  // 4 waves x 2 stages x (K, V)
     __shared__ float s_m[4][16], s_l[4][16];
-    __shared__ int32_t s_sel[4][kMaxTopk];
+    __shared__ int32_t s_sel[4][kMaxTopk + 64];  // per wave: the row, then one dump slot per lane
     const int sg = blockIdx.x, g = blockIdx.y, r = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -423,7 +432,7 @@ __global__ __launch_bounds__(256) void decode_attend_stream_kernel(
 
     // The row's selection from the scores of index head g: every wave computes
     // the same row into its own LDS slots, so no barrier is needed.
-    select_row<kCpl>(S + (size_t(r) * kIdxHeads + g) * nb_max, c, topk, init, local, lane, s_sel[wave]);
+    select_row<kCpl>(S + (size_t(r) * kIdxHeads + g) * nb_max, nb_max, c, topk, init, local, lane, s_sel[wave]);
     __builtin_amdgcn_wave_barrier();
     if (q2k_out && sg == 0 && wave == 0 && lane < topk) q2k_out[(size_t(g) * B + r) * topk + lane] = s_sel[0][lane];
     // the workgroup's slots (wave-uniform): block id, or -1 when unselected
