@@ -214,21 +214,41 @@ __global__ __launch_bounds__(256) void block_scores_kernel(
         }
 
         // Per query column: max over the block's 128 keys (rows), causal in
-        // the query's own block.
-        const bool diag = (b == c);
+        // the query's own block only (one branch per block, so the other
+        // blocks take a plain max).
+        float mxv[2];
+        if (b == c) {
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                const int p = p0 + 16 * wave + 8 * nt + n / 4;
+                float mx = -INFINITY;
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int kp = b * kBlock + 32 * mt + 8 * (r >> 2) + 4 * hb + (r & 3);
+                        mx = fmaxf(mx, kp > p ? -INFINITY : acc[mt][nt][r]);
+                    }
+                mxv[nt] = mx;
+            }
+        } else {
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                float m4[4];
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) {
+                    float m = acc[mt][nt][0];
+#pragma unroll
+                    for (int r = 1; r < 16; ++r) m = fmaxf(m, acc[mt][nt][r]);
+                    m4[mt] = m;
+                }
+                mxv[nt] = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+            }
+        }
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
             const int p = p0 + 16 * wave + 8 * nt + n / 4;
-            float mx = -INFINITY;
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int kp = b * kBlock + 32 * mt + 8 * (r >> 2) + 4 * hb + (r & 3);
-                    const float v = (diag && kp > p) ? -INFINITY : acc[mt][nt][r];
-                    mx = fmaxf(mx, v);
-                }
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float mx = fmaxf(mxv[nt], __shfl_xor(mxv[nt], 32));
             if (hb == 0 && p < doc.len)
                 S[(size_t(n & 3) * nb_max + b) * T + doc.start + p] = mx;
         }
