@@ -150,16 +150,17 @@ __global__ __launch_bounds__(256) void block_scores_kernel(
     }
 
     // Stage key block b (rows doc.start + 128b + r, r < 128) into registers.
+    // Rows at or past key_end occur only in the query's own block, where the
+    // causal mask drops them: they re-read row key_end - 1, so every load is
+    // unconditional and stays in the document.
     u32x4 stage[L::kChunksPerThread];
     auto load_block = [&](int b) {
 #pragma unroll
         for (int i = 0; i < L::kChunksPerThread; ++i) {
             const int chunk = tid + 256 * i;
             const int r = chunk / L::kChunksPerRow, col = chunk % L::kChunksPerRow;
-            const int kp = b * kBlock + r;
-            stage[i] = kp < key_end
-                           ? *(const u32x4 *)(ik + size_t(doc.start + kp) * L::kRowBytes + 16 * col)
-                           : u32x4{0, 0, 0, 0};
+            const int kp = min(b * kBlock + r, key_end - 1);
+            stage[i] = *(const u32x4 *)(ik + size_t(doc.start + kp) * L::kRowBytes + 16 * col);
         }
     };
     auto store_block = [&](int buf) {
