@@ -327,15 +327,16 @@ __global__ __launch_bounds__(256) void topk_prefill_kernel(const float *__restri
     uint32_t top[kMaxTopk];
 #pragma unroll
     for (int i = 0; i < kMaxTopk; ++i) top[i] = 0;
-    // candidates are read 16 at a time, all loads issued before they are
+    // candidates are read 32 at a time, all loads issued before they are
     // used (one load per candidate in a dependent loop waits a full memory
-    // latency each)
-    constexpr int kChunk = 16;
+    // latency each); the loads are unconditional, with the block index
+    // clamped into the scores' nb_max rows (entries past c are never used)
+    constexpr int kChunk = 32;
     if (R > 0) {
         for (int b0 = 0; b0 <= c; b0 += kChunk) {
             float sv[kChunk];
 #pragma unroll
-            for (int j = 0; j < kChunk; ++j) sv[j] = b0 + j <= c ? row[size_t(b0 + j) * T] : 0.f;
+            for (int j = 0; j < kChunk; ++j) sv[j] = row[size_t(min(b0 + j, nb_max - 1)) * T];
 #pragma unroll
             for (int j = 0; j < kChunk; ++j) {
                 const int b = b0 + j;
@@ -353,7 +354,7 @@ __global__ __launch_bounds__(256) void topk_prefill_kernel(const float *__restri
     for (int b0 = 0; b0 <= c && k < topk; b0 += kChunk) {
         float sv[kChunk];
 #pragma unroll
-        for (int j = 0; j < kChunk; ++j) sv[j] = (R > 0 && b0 + j <= c) ? row[size_t(b0 + j) * T] : 0.f;
+        for (int j = 0; j < kChunk; ++j) sv[j] = R > 0 ? row[size_t(min(b0 + j, nb_max - 1)) * T] : 0.f;
 #pragma unroll
         for (int j = 0; j < kChunk; ++j) {
             const int b = b0 + j;
