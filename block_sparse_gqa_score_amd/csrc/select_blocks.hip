@@ -153,8 +153,11 @@ __global__ __launch_bounds__(256) void block_scores_kernel(
     // Rows at or past key_end occur only in the query's own block, where the
     // causal mask drops them: they re-read row key_end - 1, so every load is
     // unconditional and stays in the document.
-    u32x4 stage[L::kChunksPerThread];
-    auto load_block = [&](int b) {
+    // Two register stages: block b+1 waits in one while block b+2 loads into
+    // the other (two blocks of compute cover a load's latency).
+    typedef u32x4 Stage[L::kChunksPerThread];
+    Stage stA, stB;
+    auto load_block = [&](int b, Stage &stage) {
 #pragma unroll
         for (int i = 0; i < L::kChunksPerThread; ++i) {
             const int chunk = tid + 256 * i;
@@ -163,7 +166,7 @@ __global__ __launch_bounds__(256) void block_scores_kernel(
             stage[i] = *(const u32x4 *)(ik + size_t(doc.start + kp) * L::kRowBytes + 16 * col);
         }
     };
-    auto store_block = [&](int buf) {
+    auto store_block = [&](int buf, const Stage &stage) {
         uint8_t *dst = smem + buf * L::kBufBytes;
 #pragma unroll
         for (int i = 0; i < L::kChunksPerThread; ++i) {
@@ -173,13 +176,17 @@ __global__ __launch_bounds__(256) void block_scores_kernel(
         }
     };
 
-    load_block(0);
-    store_block(0);
+    load_block(0, stA);
+    store_block(0, stA);
+    load_block(min(1, c), stB);
     __syncthreads();
 
-    for (int b = 0; b <= c; ++b) {
+    // block b from LDS buffer b&1; nxt holds block b+1, far receives block
+    // b+2 (clamped to c: past the end it re-reads the last block, so the
+    // load is unconditional and the compiler's waits stay exact)
+    auto step = [&](int b, Stage &nxt, Stage &far) {
         const int buf = b & 1;
-        if (b < c) load_block(b + 1);
+        load_block(min(b + 2, c), far);
 
         f32x16 acc[4][2];
 #pragma unroll
@@ -254,8 +261,13 @@ __global__ __launch_bounds__(256) void block_scores_kernel(
                 S[(size_t(n & 3) * nb_max + b) * T + doc.start + p] = mx;
         }
 
-        if (b < c) store_block(buf ^ 1);
+        if (b < c) store_block(buf ^ 1, nxt);
         __syncthreads();
+    };
+    for (int b = 0; b <= c; b += 2) {
+        step(b, stB, stA);
+        if (b + 1 > c) break;
+        step(b + 1, stA, stB);
     }
 }
 
