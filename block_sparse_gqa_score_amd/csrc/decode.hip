@@ -637,7 +637,10 @@ __global__ __launch_bounds__(256) void decode_attend_stream_kernel(
 // The thread's 8 d of one head, with the 3 neighbouring lanes (tid/4 equal),
 // are exactly one 32-value MXFP8 block of the output row [64 * 128]: block
 // (head, d quarter).
-template <bool kMx>
+// kP: the partial count rounded up to a power of two; partials t >= topk
+// re-read the last one and weigh nothing, so every load is unconditional and
+// all of them are in flight together.
+template <bool kMx, int kP>
 __global__ __launch_bounds__(64) void decode_combine_kernel(const float *__restrict__ part_o,
                                                             const float *__restrict__ part_ml,
                                                             int topk, uint16_t *__restrict__ out,
@@ -646,27 +649,27 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float *__restr
     const int dq = blockIdx.x, g = blockIdx.y, r = blockIdx.z, tid = threadIdx.x;
     const size_t base = (size_t(r) * kKvHeads + g) * topk;
     const int hh = tid >> 2, d0 = 32 * dq + (tid & 3) * 8;  // head, 8 d
-    // every load independent of the others (no data-dependent branches)
-    float mt[kMaxTopk], lt[kMaxTopk];
-    f32x4 oa[kMaxTopk], ob[kMaxTopk];
+    float mt[kP], lt[kP];
+    f32x4 oa[kP], ob[kP];
 #pragma unroll
-    for (int t = 0; t < kMaxTopk; ++t) {
-        const bool ok = t < topk;
-        const float *ml = part_ml + (base + t) * (kGroup * 2) + 2 * hh;
-        const float *src = part_o + (base + t) * (kGroup * kDim) + hh * kDim + d0;
-        mt[t] = ok ? ml[0] : -INFINITY;
-        lt[t] = ok ? ml[1] : 0.f;
-        oa[t] = ok ? *(const f32x4 *)src : f32x4{};
-        ob[t] = ok ? *(const f32x4 *)(src + 4) : f32x4{};
+    for (int t = 0; t < kP; ++t) {
+        const int tt = min(t, topk - 1);
+        const float *ml = part_ml + (base + tt) * (kGroup * 2) + 2 * hh;
+        const float *src = part_o + (base + tt) * (kGroup * kDim) + hh * kDim + d0;
+        const float m = ml[0], l = ml[1];
+        mt[t] = t < topk ? m : -INFINITY;
+        lt[t] = t < topk ? l : 0.f;
+        oa[t] = *(const f32x4 *)src;
+        ob[t] = *(const f32x4 *)(src + 4);
     }
     float M = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < kMaxTopk; ++t) M = fmaxf(M, mt[t]);
+    for (int t = 0; t < kP; ++t) M = fmaxf(M, mt[t]);
     const float baseM = M == -INFINITY ? 0.f : M;
     f32x4 na = {}, nb = {};
     float den = 0.f;
 #pragma unroll
-    for (int t = 0; t < kMaxTopk; ++t) {
+    for (int t = 0; t < kP; ++t) {
         const float w = mt[t] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mt[t] - baseM);
         den += w * lt[t];
         na += w * oa[t];
@@ -750,13 +753,23 @@ hipError_t launch_decode_combine(const float *partial, int B, int topk, bool fp8
     topk = decode_parts(topk, B);  // partials per (request, KV head)
     const float *part_o = partial;
     const float *part_ml = partial + size_t(B) * kKvHeads * topk * kGroup * kDim;
-    if (out_q)
-        hipLaunchKernelGGL(decode_combine_kernel<true>, dim3(4, kKvHeads, B), dim3(64), 0, stream, part_o,
-                           part_ml, topk, out, out_q, out_scale);
-    else
-        hipLaunchKernelGGL(decode_combine_kernel<false>, dim3(4, kKvHeads, B), dim3(64), 0, stream, part_o,
-                           part_ml, topk, out, out_q, out_scale);
-    return hipGetLastError();
+#define MSA_COMBINE_CASE(P)                                                                          \
+    if (topk <= P) {                                                                                 \
+        if (out_q)                                                                                   \
+            hipLaunchKernelGGL((decode_combine_kernel<true, P>), dim3(4, kKvHeads, B), dim3(64), 0, stream, \
+                               part_o, part_ml, topk, out, out_q, out_scale);                        \
+        else                                                                                         \
+            hipLaunchKernelGGL((decode_combine_kernel<false, P>), dim3(4, kKvHeads, B), dim3(64), 0, stream, \
+                               part_o, part_ml, topk, out, out_q, out_scale);                        \
+        return hipGetLastError();                                                                    \
+    }
+    MSA_COMBINE_CASE(1)
+    MSA_COMBINE_CASE(2)
+    MSA_COMBINE_CASE(4)
+    MSA_COMBINE_CASE(8)
+    MSA_COMBINE_CASE(16)
+#undef MSA_COMBINE_CASE
+    return hipErrorInvalidValue;
 }
 
 }  // namespace msa
