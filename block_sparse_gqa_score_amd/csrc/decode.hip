@@ -24,8 +24,9 @@
 //       with an online softmax across the blocks; the 4 waves are merged in
 //       LDS into one (O, m, l) partial per workgroup.
 //   decode_combine_kernel - per (request, KV head): log-sum-exp merge of the
-//       ceil(topk/8) partials in fixed order, bf16 output (or, for the MXFP8
-//       variant, that bf16 output encoded as E4M3 + E8M0 per 32 values).
+//       row's partials (one per attention workgroup) in fixed order, bf16
+//       output (or, for the MXFP8 variant, that bf16 output encoded as E4M3
+//       + E8M0 per 32 values).
 #include "msa_internal.hpp"
 #include "mxfp8.hpp"
 

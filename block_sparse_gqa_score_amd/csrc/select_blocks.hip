@@ -16,10 +16,13 @@
 //                         32x32x64 with unit scales), fused causal mask and
 //                         per-block row max; one workgroup = 64 query tokens
 //                         x 4 index heads of one document, looping over key
-//                         blocks 0..c staged through double-buffered LDS.
+//                         blocks 0..c, each prefetched two blocks ahead into
+//                         registers and staged through double-buffered LDS.
 //   topk_prefill_kernel - one lane per (head, token) row: top-R insertion
-//                         over 64-bit (score, ~id) keys, then an ascending
-//                         emit pass against the R-th key.
+//                         over 32-bit order keys of the scores, then an
+//                         ascending emit pass that takes every candidate
+//                         above the R-th key and the first (lowest-id)
+//                         candidates equal to it, up to the quota.
 #include "msa_internal.hpp"
 
 namespace msa {
