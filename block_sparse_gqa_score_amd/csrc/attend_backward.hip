@@ -207,10 +207,14 @@ constexpr int kQRing = 2 * kUnitsPerBlock + 1;        // 9 slots (144 KiB)
 static_assert(kQRing * kQUnitBytes <= 144 * 1024, "ring must leave LDS for the union tables");
 
 // Row r of a 32-row half, 16-byte chunk c (d 8c..8c+7), sits at chunk
-// position c ^ swz32(r).  The 16 rows one plain operand read touches,
-// 8a + 4mt + e (a, e < 4), map to 16 distinct positions, and the 4 rows
-// 8a + 4h + e (e < 4) of one transposing read to 4 distinct position pairs.
-__device__ __forceinline__ int swz32(int r) { return ((r & 3) << 2) | ((r >> 3) & 3); }
+// position c ^ swz32(r), whose bits are bits 4, 0, 1 and 3 of r.  The 16
+// rows one plain operand read touches, 8a + 4mt + e (a, e < 4), map to 16
+// distinct positions; a transposing read's 32-lane half (rows 8grp + 4h + e
+// for two grp) touches 8 rows x 2 chunks at 16 distinct positions, so
+// neither read conflicts in the LDS banks.
+__device__ __forceinline__ int swz32(int r) {
+    return ((r >> 4) & 1) | ((r & 1) << 1) | (((r >> 1) & 1) << 2) | (((r >> 3) & 1) << 3);
+}
 
 struct DqState {
     bf16x8 qb[2][4];   // Q^T operand of each token (column n = head n)
@@ -457,11 +461,12 @@ __device__ __forceinline__ void wait_copies32(int n) {
 #undef MSA_W
 }
 
-// Row r (0..63) of a staged Q / dO tile, chunk c at position c ^ swz16(r):
-// the 16 rows 16rt + m of a plain operand read map to 16 distinct
-// positions, and the 4 rows 4grp + e of a transposing read to 4 distinct
-// position pairs.
-__device__ __forceinline__ int swz16(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+// Row r (0..63) of a staged Q / dO tile, chunk c at position c ^ swz16(r),
+// swz16(r) = 2 (r mod 8) + (r / 8 mod 2): the 16 rows 16rt + m of a plain
+// operand read map to 16 distinct positions, and a transposing read's
+// 32-lane half (rows 16h + 4grp + e for two grp) touches 8 rows x 2 chunks
+// at 16 distinct positions, so neither read conflicts in the LDS banks.
+__device__ __forceinline__ int swz16(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
 }  // namespace
 
 __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
