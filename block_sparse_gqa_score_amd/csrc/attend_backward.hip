@@ -207,14 +207,13 @@ constexpr int kQRing = 2 * kUnitsPerBlock + 1;        // 9 slots (144 KiB)
 static_assert(kQRing * kQUnitBytes <= 144 * 1024, "ring must leave LDS for the union tables");
 
 // Row r of a 32-row half, 16-byte chunk c (d 8c..8c+7), sits at chunk
-// position c ^ swz32(r), whose bits are bits 4, 0, 1 and 3 of r.  The 16
-// rows one plain operand read touches, 8a + 4mt + e (a, e < 4), map to 16
-// distinct positions; a transposing read's 32-lane half (rows 8grp + 4h + e
-// for two grp) touches 8 rows x 2 chunks at 16 distinct positions, so
-// neither read conflicts in the LDS banks.
-__device__ __forceinline__ int swz32(int r) {
-    return ((r >> 4) & 1) | ((r & 1) << 1) | (((r >> 1) & 1) << 2) | (((r >> 3) & 1) << 3);
-}
+// position c ^ swz32(r).  The 16 rows one plain operand read touches,
+// 8a + 4mt + e (a, e < 4), map to 16 distinct positions, and the 4 rows
+// 8a + 4h + e (e < 4) of one transposing read to 4 distinct position pairs.
+// (A swizzle without conflicts between a transposing read's two 16-lane
+// groups exists, but its extra arithmetic spilled registers in this kernel
+// and measured no faster.)
+__device__ __forceinline__ int swz32(int r) { return ((r & 3) << 2) | ((r >> 3) & 3); }
 
 struct DqState {
     bf16x8 qb[2][4];   // Q^T operand of each token (column n = head n)
