@@ -15,10 +15,12 @@
 //   decode_attend_stream_kernel - one workgroup per 8 selected slots of a
 //       (KV head, request) (fewer for small batches, so the grid still
 //       covers the CUs).  Each wave first selects the row's blocks from
-//       the scores (the R-th largest score found by bisection on
-//       order-preserving score bits with wave-wide counts, then an ascending
-//       ballot-compacted emit; ties go to the lower block id; forced
-//       init/local blocks always kept).  Then it streams its 32 keys of the
+//       the scores: the R-th largest score is bisected on order-preserving
+//       score bits with wave-wide counts, over the few candidates at or
+//       above the R-th largest lane maximum (compacted one per lane), or
+//       over all candidates when ties leave too many; then an ascending
+//       ballot-compacted emit.  Ties go to the lower block id, and forced
+//       init/local blocks are always kept.  Then it streams its 32 keys of the
 //       next block through its own LDS ring while computing the current one:
 //       S^T = K Q^T and O^T = V^T P^T on MFMA 16x16x32 (16 query heads = N),
 //       with an online softmax across the blocks; the 4 waves are merged in
@@ -261,8 +263,9 @@ __device__ __forceinline__ int wave_count(bool pred) { return __popcll(__ballot(
 // Selection for one (request, index head) row by one wave: forced blocks
 // plus the R = topk - forced highest-scoring candidates (ties to the lower
 // block id), ascending, then -1.  The R-th largest order value is found by
-// bisection on its bits with wave-wide counts.  out holds kMaxTopk + 64
-// entries: the row, then a dump slot per lane.
+// bisection on its bits with wave-wide counts.  out holds kMaxTopk + 128
+// entries: the row, a dump slot per lane, then 64 entries of working space
+// (out[0..63] also serves as working space before the row is written).
 template <int kCpl>  // candidates per lane: blocks lane + 64*i
 __device__ __forceinline__ void select_row(const float *__restrict__ srow, int nb_max, int c, int topk,
                                            int init, int local, int lane, int32_t *out) {
@@ -293,11 +296,72 @@ __device__ __forceinline__ void select_row(const float *__restrict__ srow, int n
         for (int k = 0; k < kBits; ++k) tot += wave_count((cl >> k) & 1) << k;
         return tot;
     };
-    // largest x with #{u >= x} >= R (the R-th largest order value), bisected
-    // on the high 16 bits first.  When exactly R candidates reach that
-    // prefix, the R-th largest is their minimum; otherwise (ties in the
-    // prefix) the bisection continues over the low 16 bits.
+    // thr = largest x with #{u >= x} >= R, the R-th largest order value.
+    //
+    // Fast path: the R lanes whose own maxima are the R largest each hold a
+    // distinct candidate >= lb, the R-th largest lane maximum, so thr >= lb
+    // and every candidate that decides thr is >= lb.  Those (typically about
+    // R of them) are compacted one per lane into out[0..63], and thr is
+    // bisected over them with one compare per step.  The counts #{>= x} it
+    // sees equal the full row's for every x >= lb and are >= R below lb, so
+    // it yields the same thr.  More than 64 of them (ties), or fewer than R
+    // lanes with a candidate, take the general path over all candidates.
+    const uint64_t below = (1ull << lane) - 1ull;
+    auto select1 = [&](uint32_t v) {  // R-th largest of one value per lane
+        uint32_t t = 0;
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t trial = t | (1u << bit);
+            if (wave_count(v >= trial) >= R) t = trial;
+        }
+        return t;
+    };
     uint32_t thr = 0;
+    if (R > 0) {
+        uint32_t lm = 0;
+#pragma unroll
+        for (int i = 0; i < kCpl; ++i) lm = max(lm, u[i]);
+        const uint32_t lb = select1(lm);
+        if (lb > 0) {
+            int kept = 0;
+#pragma unroll
+            for (int i = 0; i < kCpl; ++i) {
+                const bool keep = u[i] >= lb;
+                const uint64_t m = __ballot(keep);
+                const int pos = kept + __popcll(m & below);
+                if (keep && pos < 64) {
+                    out[pos] = int32_t(u[i]);
+                    out[kMaxTopk + 64 + pos] = lane + 64 * i;
+                }
+                kept += __popcll(m);
+            }
+            if (kept <= 64) {
+                const uint32_t v0 = uint32_t(out[lane]);
+                const int b0 = out[kMaxTopk + 64 + lane];
+                const uint32_t v = lane < kept ? v0 : 0u;
+                thr = select1(v);
+                // The survivors are in ascending block order, and every
+                // non-forced block lies between the forced head (< init) and
+                // tail (> c - local).  So the row is the head, the taken
+                // survivors in order, then the tail.
+                const int n_gt_fast = wave_count(v > thr);
+                const bool tie = v != 0u && v == thr;
+                const int tie_rank = __popcll(__ballot(tie) & below);
+                const bool take = v > thr || (tie && tie_rank < R - n_gt_fast);
+                const int n_head = min(init, c + 1);
+                const int tail_lo = local > 0 ? max(c - local + 1, n_head) : c + 1;
+                const int pos = n_head + __popcll(__ballot(take) & below);
+                if (take) out[pos] = b0;
+                for (int j = lane; j < n_head; j += 64) out[j] = j;
+                for (int j = lane; tail_lo + j <= c; j += 64) out[n_head + R + j] = tail_lo + j;
+                return;
+            }
+        }
+    }
+    // General path: bisected on the high 16 bits first.  When exactly R
+    // candidates reach that prefix, the R-th largest is their minimum;
+    // otherwise (ties in the prefix) the bisection continues over the low
+    // 16 bits.
+    int n_gt = 0;  // #{u > thr}
     if (R > 0) {
         for (int bit = 31; bit >= 16; --bit) {
             const uint32_t trial = thr | (1u << bit);
@@ -316,11 +380,10 @@ __device__ __forceinline__ void select_row(const float *__restrict__ srow, int n
                 if (count_ge(trial) >= R) thr = trial;
             }
         }
+        n_gt = thr != 0xFFFFFFFFu ? count_ge(thr + 1u) : 0;
     }
-    const int n_gt = (R > 0 && thr != 0xFFFFFFFFu) ? count_ge(thr + 1u) : 0;  // #{u > thr}
     const int ties_wanted = R > 0 ? R - n_gt : 0;  // equal-to-threshold picks, lowest ids first
     int ties_seen = 0, emitted = 0;
-    const uint64_t below = (1ull << lane) - 1ull;
     // ascending emit; a lane that takes nothing writes its own dump slot
     // out[kMaxTopk + lane], so the stores need no branch
 #pragma unroll
@@ -414,7 +477,7 @@ __global__ __launch_bounds__(256) void decode_attend_stream_kernel(
     using SL = StreamLayout<kFp8Kv>;
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];  // 4 waves x 2 stages x (K, V)
     __shared__ float s_m[4][16], s_l[4][16];
-    __shared__ int32_t s_sel[4][kMaxTopk + 64];  // per wave: the row, then one dump slot per lane
+    __shared__ int32_t s_sel[4][kMaxTopk + 128];  // per wave: the row, dump slots, working space
     const int sg = blockIdx.x, g = blockIdx.y, r = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);

@@ -120,6 +120,9 @@ DECODE_CASES = [
                             12000, 20000], 16, 0, 1, "bf16"),
     ("batch20_topk5_init1_fp8", [64 + 997 * i for i in range(20)], 5, 1, 1, "fp8"),
     ("batch24_short_local2_topk3_bf16", [1 + 37 * i for i in range(24)], 3, 0, 2, "bf16"),
+    # no local blocks, several init blocks
+    ("init3_local0_topk7_bf16", [1, 300, 5000, 20000], 7, 3, 0, "bf16"),
+    ("init2_local0_topk16_fp8", [129, 9000, 30000], 16, 2, 0, "fp8"),
 ]
 
 
