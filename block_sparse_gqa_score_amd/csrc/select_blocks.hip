@@ -326,8 +326,13 @@ __global__ __launch_bounds__(256) void topk_prefill_kernel(const float *__restri
                                                            int ndocs, int T, int nb_max, int topk,
                                                            int init, int local,
                                                            int32_t *__restrict__ q2k) {
-    const int t = blockIdx.x * 256 + threadIdx.x;
+    // A row's work grows with its query block.  Workgroups x of heads h and
+    // h + 2 are dispatched 2 * gridDim.x apart and tend to share a CU, so
+    // heads 2 and 3 take the tiles in reverse order: a CU then pairs a late
+    // (heavy) tile with an early (light) one.
     const int h = blockIdx.y;
+    const int tile = h >= 2 ? int(gridDim.x) - 1 - int(blockIdx.x) : int(blockIdx.x);
+    const int t = tile * 256 + threadIdx.x;
     if (t >= T) return;
     int32_t *out = q2k + (size_t(h) * T + t) * topk;
     const int d = find_doc(docs, ndocs, t);
@@ -344,19 +349,30 @@ __global__ __launch_bounds__(256) void topk_prefill_kernel(const float *__restri
     for (int i = 0; i < kMaxTopk; ++i) top[i] = 0;
     // candidates are read 32 at a time, all loads issued before they are
     // used (one load per candidate in a dependent loop waits a full memory
-    // latency each); the loads are unconditional, with the block index
-    // clamped into the scores' nb_max rows (entries past c are never used)
+    // latency each), and the next 32 are loaded while the current ones are
+    // processed; the loads are unconditional, with the block index clamped
+    // into the scores' nb_max rows (entries past c are never used)
     constexpr int kChunk = 32;
-    if (R > 0) {
-        for (int b0 = 0; b0 <= c; b0 += kChunk) {
-            float sv[kChunk];
+    auto load_chunk = [&](float (&dst)[kChunk], int b0) {
 #pragma unroll
-            for (int j = 0; j < kChunk; ++j) sv[j] = row[size_t(min(b0 + j, nb_max - 1)) * T];
+        for (int j = 0; j < kChunk; ++j) dst[j] = row[size_t(min(b0 + j, nb_max - 1)) * T];
+    };
+    float sa[kChunk], sb[kChunk];
+    if (R > 0) {
+        auto scan = [&](const float (&sv)[kChunk], int b0) {
 #pragma unroll
             for (int j = 0; j < kChunk; ++j) {
                 const int b = b0 + j;
                 if (b <= c && !is_forced(b, c, init, local)) topk_insert(top, float_order_bits(sv[j]));
             }
+        };
+        load_chunk(sa, 0);
+        for (int b0 = 0; b0 <= c; b0 += 2 * kChunk) {
+            load_chunk(sb, b0 + kChunk);
+            scan(sa, b0);
+            if (b0 + kChunk > c) break;
+            load_chunk(sa, b0 + 2 * kChunk);
+            scan(sb, b0 + kChunk);
         }
     }
     // R <= 0: the forced blocks fill the row and no candidate is taken
@@ -366,10 +382,7 @@ __global__ __launch_bounds__(256) void topk_prefill_kernel(const float *__restri
     for (int i = 0; i < kMaxTopk; ++i) n_gt += (i < R && top[i] > thr) ? 1 : 0;
     int quota = R > 0 ? R - n_gt : 0;
     int k = 0;
-    for (int b0 = 0; b0 <= c && k < topk; b0 += kChunk) {
-        float sv[kChunk];
-#pragma unroll
-        for (int j = 0; j < kChunk; ++j) sv[j] = R > 0 ? row[size_t(min(b0 + j, nb_max - 1)) * T] : 0.f;
+    auto emit = [&](const float (&sv)[kChunk], int b0) {
 #pragma unroll
         for (int j = 0; j < kChunk; ++j) {
             const int b = b0 + j;
@@ -386,6 +399,14 @@ __global__ __launch_bounds__(256) void topk_prefill_kernel(const float *__restri
             }
             if (take && k < topk) out[k++] = b;
         }
+    };
+    load_chunk(sa, 0);
+    for (int b0 = 0; b0 <= c && k < topk; b0 += 2 * kChunk) {
+        load_chunk(sb, b0 + kChunk);
+        emit(sa, b0);
+        if (b0 + kChunk > c || k >= topk) break;
+        load_chunk(sa, b0 + 2 * kChunk);
+        emit(sb, b0 + kChunk);
     }
     for (; k < topk; ++k) out[k] = -1;
 }
