@@ -191,6 +191,28 @@ def test_decode_tied_scores_take_lowest_ids(pattern):
     check_attention(out.float().cpu().numpy(), ref["out"], what=f"ties {pattern}")
 
 
+@pytest.mark.parametrize("init,local", [(0, 1), (2, 0)])
+def test_decode_all_tied_around_64_candidates(init, local):
+    """Every block's score tied, with 62 to 66 candidates per row.  The decode
+    top-k takes its fast path while at most 64 candidates reach the bound it
+    derives from the lane maxima, and its general path beyond that; both must
+    give the oracle's selection (the lowest ids) exactly."""
+    print(f"[decode ties 64] init={init} local={local}", flush=True)
+    lens = [8065, 8192, 8193, 8320, 8321, 8449]
+    d = W.make_decode(lens, 304, topk=16, init_blocks=init, local_blocks=local)
+    row_a = d.ik_cache[0].copy()  # first slots: never poisoned
+    for r, L in enumerate(lens):
+        for pg in range(-(-L // 128)):
+            slot0 = int(d.page_table[r, pg]) * 128
+            d.ik_cache[slot0:slot0 + 128] = row_a
+    out, q2k = msa.sparse_attend_decode_paged(
+        dev(d.q), dev(d.iq), dev(d.k_cache), dev(d.v_cache), dev(d.ik_cache), dev(d.page_table),
+        dev(d.context_lens), d.max_context_len, d.topk, init, local, d.scale, return_q2k=True)
+    ref = oracle.decode(d)
+    assert np.array_equal(_tok_major(q2k), ref["q2k"])
+    check_attention(out.float().cpu().numpy(), ref["out"], what=f"ties 64 init={init}")
+
+
 def test_decode_page_permutation_invariance():
     lens = [700, 1281, 256, 3000]
     a = W.make_decode(lens, 81, topk=5, identity_pages=True)
