@@ -22,7 +22,10 @@
 //       barrier per union block, while the next five units stream in.  A
 //       wave computes a block only for those of its two tokens that selected
 //       it, as one chain over the block's 128 keys (one softmax step); the K
-//       and V^T fragments it reads from LDS serve both tokens.
+//       and V^T fragments it reads from LDS serve both tokens.  Blocks that a
+//       single token selected skip the ring: that token's wave reads them
+//       straight from memory, one 32-key unit in each ring iteration where it
+//       has no token in the ring's block, and the rest after the ring.
 //
 // Per wave, token and 32-key unit (MFMA 16x16x32 bf16, key rows m, head
 // columns n):
@@ -181,16 +184,16 @@ __device__ __forceinline__ void attend_block(WaveState &st, const uint8_t *smem,
 }  // namespace
 
 namespace {
-// One block b < c for token t of a wave, read straight from memory (the
-// per-unit K rows and V^T rows are contiguous in the MFMA operand layouts), unit by
-// unit with the lazy online softmax.  Used for blocks a single token of the
-// tile selected, which would otherwise hold the whole workgroup at a
+// Unit q of a block b < c for token t of a wave, read straight from memory
+// (the per-unit K rows and V^T rows are contiguous in the MFMA operand
+// layouts), with the lazy online softmax.  Used for blocks a single token of
+// the tile selected, which would otherwise hold the whole workgroup at a
 // barrier for one wave's work.
-__device__ __forceinline__ void attend_block_global(WaveState &st, int t, const uint16_t *__restrict__ ku,
-                                                    const uint16_t *__restrict__ vt, int g,
-                                                    int uoff, int b, int n, int grp, float scale_log2) {
-#pragma unroll 1
-    for (int q = 0; q < kUnitsPerBlock; ++q) {
+template <int t>
+__device__ __forceinline__ void attend_unit_global(WaveState &st, const uint16_t *__restrict__ ku,
+                                                   const uint16_t *__restrict__ vt, int g, int uoff, int b,
+                                                   int q, int n, int grp, float scale_log2) {
+    {
         f32x4 sacc[2] = {f32x4{}, f32x4{}};
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
@@ -369,20 +372,28 @@ __global__ __launch_bounds__(kThreads) void attend_prefill_kernel(
     }
     __syncthreads();
     const int ns = s_ns;
-    // ---- blocks a single token of the tile selected: that token's wave
-    // alone, straight from memory (never the query's own block), before the
-    // ring starts (the online softmax takes the blocks in any order)
+    // ---- blocks a single token of the tile selected (never the query's own
+    // block): that token's wave alone, straight from memory, one unit at a
+    // time in the ring iterations where the wave has no token in the ring's
+    // block, and the rest after the ring (the online softmax takes blocks in
+    // any order).  The wave lists them as 2b + t, at most kMaxTopk per token.
+    __shared__ int s_dlist[kTok / 2][2 * kMaxTopk];
+    int nd = 0;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
         if (!tok_ok[t]) continue;
         const int bit = 1 << (2 * wave + t);
-        for (int u = 0; u < nu; ++u) {
-            const int um = __builtin_amdgcn_readfirstlane(s_umask[u]);
-            const int b = __builtin_amdgcn_readfirstlane(s_ublk[u]);
-            if (!(um & bit) || b == c || __popc(um) >= kSharedMin) continue;
-            attend_block_global(st, t, ku, vt, g, uoff, b, n, grp, scale_log2);
+        for (int u0 = 0; u0 < nu; u0 += 64) {
+            const int u = min(u0 + lane, nu - 1);
+            const int um = s_umask[u], ub = s_ublk[u];
+            const bool dir = u0 + lane < nu && (um & bit) && ub != c && __popc(um) < kSharedMin;
+            const uint64_t m = __ballot(dir);
+            if (dir) s_dlist[wave][nd + __popcll(m & ((1ull << lane) - 1ull))] = 2 * ub + t;
+            nd += __popcll(m);
         }
     }
+    const int nd_units = kUnitsPerBlock * nd;
+    int di = 0;
 
     // 32-key units: 4 per ring block, except that the query's own block c
     // (always last when present) stops at the unit holding p_last.
@@ -436,7 +447,14 @@ __global__ __launch_bounds__(kThreads) void attend_prefill_kernel(
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): query operands are in (no copy issued yet)
     int issued = min(nunits, kRing);
     for (int vu = 0; vu < issued; ++vu) issue_unit(vu);
-    for (int u = 0; u < ns; ++u) {
+    for (int u = 0; u < ns || di < nd_units; ++u) {
+        if (u >= ns) {  // past the ring (no more barriers): the wave's remaining units
+            const int e = __builtin_amdgcn_readfirstlane(s_dlist[wave][di >> 2]);
+            if (e & 1) attend_unit_global<1>(st, ku, vt, g, uoff, e >> 1, di & 3, n, grp, scale_log2);
+            else attend_unit_global<0>(st, ku, vt, g, uoff, e >> 1, di & 3, n, grp, scale_log2);
+            ++di;
+            continue;
+        }
         const int ustart = kUnitsPerBlock * u;
         const int nq = u == ns - 1 ? nunits - ustart : kUnitsPerBlock;
         wait_copies(2 * (issued - (ustart + nq)));  // copies complete in issue order
@@ -462,6 +480,12 @@ __global__ __launch_bounds__(kThreads) void attend_prefill_kernel(
         else if (act[1])
             attend_block<false, true, false>(st, smem, ustart, kUnitsPerBlock, k_row_off, v_off, n, grp,
                                              keyb, act, my_p, scale_log2);
+        else if (di < nd_units) {  // no token in this block: one unit of the wave's own blocks
+            const int e = __builtin_amdgcn_readfirstlane(s_dlist[wave][di >> 2]);
+            if (e & 1) attend_unit_global<1>(st, ku, vt, g, uoff, e >> 1, di & 3, n, grp, scale_log2);
+            else attend_unit_global<0>(st, ku, vt, g, uoff, e >> 1, di & 3, n, grp, scale_log2);
+            ++di;
+        }
     }
 
     // ---- epilogue: normalise and store bf16 (lane holds d = 16dt + 4grp + i)
