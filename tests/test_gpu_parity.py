@@ -123,6 +123,8 @@ DECODE_CASES = [
     # no local blocks, several init blocks
     ("init3_local0_topk7_bf16", [1, 300, 5000, 20000], 7, 3, 0, "bf16"),
     ("init2_local0_topk16_fp8", [129, 9000, 30000], 16, 2, 0, "fp8"),
+    # more than 64 requests: the bf16 scorer's multi-scan page partition
+    ("batch70_short_topk4_bf16", [1 + 53 * i for i in range(70)], 4, 0, 1, "bf16"),
 ]
 
 
