@@ -259,13 +259,35 @@ def bench_decode(args, hip, flush):
                 fp8kv=fp8kv)
 
 
-def bench_prefill(args, hip, flush):
+def prefill_flops(w):
+    """Algorithmic flops of one prefill pass over workload w: the causal
+    index dots (4 heads x 256 flop per (query, key) pair of a document) and
+    the selected-key attention (64 heads x 512 flop per attended key, with
+    keys(t) = 128 (min(topk, c+1) - 1) + (p mod 128) + 1: every chosen block
+    full except the query's own)."""
+    import numpy as np
+    lens = np.diff(w.cu_seqlens).astype(np.int64)
+    score = float(sum(4 * L * (L + 1) // 2 * 256 for L in lens))
+    keys = 0
+    for L in lens:
+        pos = np.arange(L)
+        keys += int((128 * (np.minimum(w.topk, pos // 128 + 1) - 1) + pos % 128 + 1).sum())
+    return score, 64.0 * 512 * keys
+
+
+PREFILL_KERNELS = {"doc_setup(select)": (0, 1), "block_scores": (1, 2), "topk_prefill": (2, 3),
+                   "doc_setup(attend)": (4, 5), "kv_units": (5, 6), "attend_prefill": (6, 7)}
+
+
+def bench_prefill(args, hip, flush, cfg=2, steps=None):
+    """One prefill pass (select + attend) of workload cfg, timed with HIP
+    events around each kernel on the stream they run on."""
     import numpy as np
     import torch
     import block_sparse_gqa_score_amd as msa
     import workloads as W
     t0 = time.time()
-    w = W.config(2)
+    w = W.config(cfg)
     gen_s = time.time() - t0
     iq, ik, cu = dev(w.iq), dev(w.ik), dev(w.cu_seqlens)
     q, k, v = dev(w.q), dev(w.k), dev(w.v)
@@ -295,22 +317,82 @@ def bench_prefill(args, hip, flush):
         if st != 0:
             raise RuntimeError(L.msa_last_error().decode())
 
-    step_ms, evs, _ = timed_steps(run, args.prefill_steps, args.warmup, hip, stream, flush, 8)
+    step_ms, evs, _ = timed_steps(run, steps or args.prefill_steps, args.warmup, hip, stream, flush, 8)
     kt = {}
     for arr in evs:
-        for nm, (a, b) in {"doc_setup(select)": (0, 1), "block_scores": (1, 2), "topk_prefill": (2, 3),
-                           "doc_setup(attend)": (4, 5), "kv_units": (5, 6),
-                           "attend_prefill": (6, 7)}.items():
+        for nm, (a, b) in PREFILL_KERNELS.items():
             kt.setdefault(nm, []).append(hip.elapsed_ms(arr[a], arr[b]))
-    # algorithmic flops (causal index dots + selected-key attention)
-    T = w.T
-    pos = np.arange(T)
-    keys = 128 * (np.minimum(w.topk, pos // 128 + 1) - 1) + pos % 128 + 1
-    score_flops = 4 * T * (T + 1) / 2 * 256
-    attn_flops = 64 * 512 * int(keys.sum())
+    score_flops, attn_flops = prefill_flops(w)
     per_kernel = {kk: stats(vv)["mean"] for kk, vv in kt.items()}
-    return dict(w=w, gen_s=gen_s, step=stats(step_ms), per_kernel_ms=per_kernel,
-                score_flops=score_flops, attn_flops=attn_flops, q2k=q2k, out=out)
+    res = dict(w=w, gen_s=gen_s, step=stats(step_ms), steps=len(step_ms), per_kernel_ms=per_kernel,
+               score_flops=score_flops, attn_flops=attn_flops, q2k=q2k, out=out)
+    if "planted_blocks" in w.meta:
+        res["planted_gap"] = planted_gap_gpu(w, iq, ik, cu)
+    return res
+
+
+def planted_gap_gpu(w, iq, ik, cu):
+    """Realised planted-vs-unplanted separation from the GPU's own block
+    scores (one extra select call with scores_out, outside any timing): mean
+    block score of planted and unplanted candidate entries, and the share of
+    the chosen non-forced slots held by planted blocks."""
+    import torch
+    import block_sparse_gqa_score_amd as msa
+    q2k, S = msa.select_blocks(iq, ik, cu, w.max_seqlen, w.topk, w.init_blocks, w.local_blocks,
+                               scores=True)
+    nb = S.shape[1]
+    pos = torch.arange(w.T, device="cuda")  # one document
+    c = pos // 128
+    cand = torch.arange(nb, device="cuda")[:, None] <= c[None, :]          # [nb, T]
+    planted = torch.zeros(nb, dtype=torch.bool, device="cuda")
+    planted[torch.tensor(w.meta["planted_blocks"], device="cuda")] = True
+    pl = cand & planted[:, None]
+    un = cand & ~planted[:, None]
+    s_pl = S[:, pl].double()
+    s_un = S[:, un].double()
+    forced = (q2k < w.init_blocks) | (q2k >= (c[None, :, None] - w.local_blocks + 1))
+    free = (q2k >= 0) & ~forced
+    chosen_pl = planted[q2k.clamp(min=0).long()] & free
+    return {"planted_blocks": len(w.meta["planted_blocks"]),
+            "planted_mean_block_score": round(float(s_pl.mean()), 3),
+            "unplanted_mean_block_score": round(float(s_un.mean()), 3),
+            "gap": round(float(s_pl.mean() - s_un.mean()), 3),
+            "gap_in_unplanted_sd": round(float((s_pl.mean() - s_un.mean()) / s_un.std()), 3),
+            "planted_share_of_free_slots": round(float(chosen_pl.sum()) / max(1, int(free.sum())), 4)}
+
+
+def prefill_summary(pres, name):
+    """The JSON object of one prefill workload: tok/s over real tokens, the
+    path's and each kernel's bf16 MFMA fraction on the algorithmic flops."""
+    w = pres["w"]
+    p_ms = pres["step"]["mean"]
+    a_ms = pres["per_kernel_ms"]["attend_prefill"]
+    s_ms = pres["per_kernel_ms"]["block_scores"]
+    total_flops = pres["score_flops"] + pres["attn_flops"]
+    out = {
+        "workload": name, "tokens": w.T, "documents": w.num_docs, "topk": w.topk,
+        "init_blocks": w.init_blocks, "local_blocks": w.local_blocks,
+        "value": round(w.T / (p_ms * 1e-3), 1), "unit": "tok/s",
+        "ms_per_step": round(p_ms, 6), "steps": pres["steps"],
+        "per_kernel_us": {k: round(v * 1e3, 3) for k, v in pres["per_kernel_ms"].items()},
+        "alg_flops": {"score": pres["score_flops"], "attention": pres["attn_flops"]},
+        "path_mfma_frac": round(total_flops / (p_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "roofline": {"bound": "mfma", "kernel": "attend_prefill",
+                     "achieved": round(pres["attn_flops"] / (a_ms * 1e-3) / 1e12, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(pres["attn_flops"] / (a_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic("attend_prefill") if name == "prefill_32k_planted" else None,
+                     "alg_flops_per_launch": pres["attn_flops"], "avg_launch_us": round(a_ms * 1e3, 3),
+                     "mfma_busy_counter": (measured_counter("attend_prefill", "mfma_busy_frac")
+                                           if name == "prefill_32k_planted" else None)},
+        "block_scores": {"achieved_tflops": round(pres["score_flops"] / (s_ms * 1e-3) / 1e12, 2),
+                         "frac": round(pres["score_flops"] / (s_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                         "mfma_busy_counter": (measured_counter("block_scores", "mfma_busy_frac")
+                                               if name == "prefill_32k_planted" else None)},
+    }
+    if "planted_gap" in pres:
+        out["planted_gap"] = pres["planted_gap"]
+    return out
 
 
 def bench_select_fp8(args, hip, flush, pres):
@@ -421,7 +503,23 @@ def bench_decode_fp8_indexer(args, hip, flush):
                                 "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                 "frac": round(kv_bytes / (a_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                                 "alg_bytes_per_launch": kv_bytes, "avg_launch_us": round(a_ms * 1e3, 3)},
-            "data": "seeded torch generator on the GPU (timing leg)"}
+            "data": "seeded torch generator on the GPU (timing leg)",
+            "_host_workload": lambda: host_decode(q, iq, kc, vc, ikc, pt, ctx, topk, "fp8")}
+
+
+def host_decode(q, iq, kc, vc, ikc, pt, ctx, topk, index_dtype):
+    """Host (numpy) copy of a decode batch drawn on the GPU, as a
+    workloads.Decode for the oracle's CPU baseline."""
+    import torch
+    import workloads as W
+
+    def h(t):
+        return t.cpu().view(torch.int16).numpy().view("uint16") if t.dtype == torch.bfloat16 \
+            else t.cpu().numpy()
+
+    return W.Decode(name="decode_fp8idx_b8_ctx128k", q=h(q), iq=h(iq), k_cache=h(kc), v_cache=h(vc),
+                    ik_cache=h(ikc), page_table=h(pt), context_lens=h(ctx), index_dtype=index_dtype,
+                    topk=topk, init_blocks=0, local_blocks=1)
 
 
 def bench_backward(args, hip, flush, pres):
@@ -466,7 +564,7 @@ def bench_backward(args, hip, flush, pres):
     return dict(step=stats(step_ms), per_kernel_ms=per_kernel)
 
 
-def cpu_baseline_decode(d, seconds):
+def cpu_baseline_decode(d, seconds, reps_max=20):
     import numpy as np
     import oracle
     t0 = time.time()
@@ -474,27 +572,30 @@ def cpu_baseline_decode(d, seconds):
     while True:
         oracle.decode(d)
         reps += 1
-        if time.time() - t0 >= seconds or reps >= 20:
+        if time.time() - t0 >= seconds or reps >= reps_max:
             break
     el = time.time() - t0
     return dict(value=el / reps * 1e6, unit="us/step", cores=oracle.num_threads(), kind="oracle",
                 sample=f"{reps} full decode step(s) of the same batch (all {d.B} requests)")
 
 
-def cpu_baseline_prefill(w, seconds):
+def cpu_baseline_prefill(w, seconds, what):
+    """The oracle on a bounded sample of the workload's tokens: uniform
+    draws of 16 tokens at a time until ``seconds`` of CPU work (or every
+    token) is done; tok/s over the tokens done."""
     import numpy as np
     import oracle
     rng = np.random.default_rng(0)
     n = 16
     t0 = time.time()
     done = 0
-    while time.time() - t0 < seconds and done < 4096:
-        toks = np.sort(rng.integers(0, w.T, size=n)).astype(np.int32)
+    while time.time() - t0 < seconds and done < min(4096, w.T):
+        toks = np.sort(rng.choice(w.T, size=min(n, w.T), replace=False)).astype(np.int32)
         oracle.prefill(w, tokens=toks)
-        done += n
+        done += len(toks)
     el = time.time() - t0
     return dict(value=done / el, unit="tok/s", cores=oracle.num_threads(), kind="oracle",
-                sample=f"{done} tokens drawn uniformly from the 32768-token document")
+                sample=f"{done} tokens drawn uniformly from the {w.T} tokens of {what}")
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
@@ -618,28 +719,8 @@ def main():
         "path_hbm_frac": round(dres["total_bytes"] / (step_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
     }
     if not args.no_prefill:
-        pres = bench_prefill(args, hip, flush)
-        w = pres["w"]
-        p_ms = pres["step"]["mean"]
-        a_ms = pres["per_kernel_ms"]["attend_prefill"]
-        s_ms = pres["per_kernel_ms"]["block_scores"]
-        total_flops = pres["score_flops"] + pres["attn_flops"]
-        line["prefill_32k"] = {
-            "workload": "prefill_32k_planted", "value": round(w.T / (p_ms * 1e-3), 1), "unit": "tok/s",
-            "ms_per_step": round(p_ms, 6), "steps": args.prefill_steps,
-            "per_kernel_us": {k: round(v * 1e3, 3) for k, v in pres["per_kernel_ms"].items()},
-            "path_mfma_frac": round(total_flops / (p_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-            "roofline": {"bound": "mfma", "kernel": "attend_prefill",
-                         "achieved": round(pres["attn_flops"] / (a_ms * 1e-3) / 1e12, 2),
-                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(pres["attn_flops"] / (a_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                         "traffic": measured_traffic("attend_prefill"), "alg_flops_per_launch": pres["attn_flops"],
-                         "avg_launch_us": round(a_ms * 1e3, 3),
-                         "mfma_busy_counter": measured_counter("attend_prefill", "mfma_busy_frac")},
-            "block_scores": {"achieved_tflops": round(pres["score_flops"] / (s_ms * 1e-3) / 1e12, 2),
-                             "frac": round(pres["score_flops"] / (s_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                             "mfma_busy_counter": measured_counter("block_scores", "mfma_busy_frac")},
-        }
+        pres = bench_prefill(args, hip, flush, cfg=2)
+        line["prefill_32k"] = prefill_summary(pres, "prefill_32k_planted")
         line["prefill_32k"]["block_scores_fp8"] = bench_select_fp8(args, hip, flush, pres)
         if not args.no_backward:
             bres = bench_backward(args, hip, flush, pres)
@@ -660,12 +741,28 @@ def main():
                 "bwd_dkdv_tflops": round(2.0 * pres["attn_flops"] / (pk["bwd_dkdv"] * 1e-3) / 1e12, 2),
                 "train_attention_ms": round(b_ms + pres["per_kernel_ms"]["attend_prefill"], 3),
             }
+    small = {}
+    if not args.no_prefill:
+        # the 2048-token prefill (topk 4) and the packed 2 x 16384 microbatch
+        # (documents log-uniform in [256, 8192], init 1, local 1)
+        for cfg, name in ((0, "prefill_2k"), (3, "packed_2x16k")):
+            small[name] = bench_prefill(args, hip, flush, cfg=cfg, steps=max(args.prefill_steps, 20))
+            line[name] = prefill_summary(small[name], small[name]["w"].name)
+    fp8 = None
     if not args.no_fp8_decode:
-        line["decode_fp8_indexer"] = bench_decode_fp8_indexer(args, hip, flush)
+        fp8 = bench_decode_fp8_indexer(args, hip, flush)
+        line["decode_fp8_indexer"] = {k: v for k, v in fp8.items() if not k.startswith("_")}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_decode(d, args.cpu_seconds)
         if not args.no_prefill:
-            line["prefill_32k"]["cpu_baseline"] = cpu_baseline_prefill(pres["w"], args.cpu_seconds)
+            line["prefill_32k"]["cpu_baseline"] = cpu_baseline_prefill(
+                pres["w"], args.cpu_seconds, "the 32768-token document")
+            for name, res in small.items():
+                line[name]["cpu_baseline"] = cpu_baseline_prefill(
+                    res["w"], args.cpu_seconds, f"{res['w'].num_docs} document(s)")
+        if fp8 is not None:
+            line["decode_fp8_indexer"]["cpu_baseline"] = cpu_baseline_decode(
+                fp8["_host_workload"](), args.cpu_seconds, reps_max=3)
     print(json.dumps(line), flush=True)
 
 

@@ -22,6 +22,9 @@ Entry points (names follow the C ABI):
                 page_table, context_lens, max_context_len, ...) -> out [B,64,128]
                 (K/V caches as E4M3 bytes with per-tensor scales)
   cache_insert(k, v, index_k, slot_mapping, k_cache, v_cache, index_k_cache) -> None (in place)
+  validate_prefill_inputs(cu_seqlens, total_tokens, max_seqlen) -> (bits, first)
+  validate_decode_inputs(page_table, context_lens, max_context_len, num_pages) -> (bits, first)
+                (debug checks of the device-side data contract; bits 0 = valid)
 """
 from __future__ import annotations
 
@@ -35,7 +38,7 @@ __all__ = [
     "select_blocks", "sparse_attend_prefill", "sparse_attend_decode_paged",
     "sparse_attend_prefill_backward", "prefill_backward_workspace_bytes",
     "sparse_attend_decode_paged_mxfp8", "sparse_attend_decode_paged_fp8kv", "mxfp8_quantize",
-    "cache_insert",
+    "cache_insert", "validate_prefill_inputs", "validate_decode_inputs", "INVALID_BITS",
     "unsupported_reason", "library_path", "MsaError",
     "select_blocks_workspace_bytes", "prefill_workspace_bytes", "decode_workspace_bytes",
 ]
@@ -47,6 +50,13 @@ _lib = None
 MSA_INDEX_BF16, MSA_INDEX_FP8_E4M3 = 0, 1
 _STATUS = {0: "MSA_OK", 1: "MSA_ERR_INVALID_ARG", 2: "MSA_ERR_UNSUPPORTED",
            3: "MSA_ERR_WORKSPACE", 4: "MSA_ERR_HIP"}
+
+
+# msa_invalid_bits of the debug validators
+INVALID_BITS = {1: "cu_seqlens[0] != 0", 2: "cu_seqlens[num_docs] != total_tokens",
+                4: "empty document", 8: "document longer than max_seqlen",
+                16: "offset outside [0, total_tokens]", 32: "context length outside [0, max_context_len]",
+                64: "page id outside [0, num_pages)"}
 
 
 class MsaError(RuntimeError):
@@ -108,6 +118,10 @@ def lib():
                                                            f, P, P, P, sz, P]
         L.msa_cache_insert.restype = i
         L.msa_cache_insert.argtypes = [P, P, P, P, i, i, P, P, P, i, P]
+        L.msa_validate_prefill_inputs.restype = i
+        L.msa_validate_prefill_inputs.argtypes = [P, i, i, i, P, P]
+        L.msa_validate_decode_inputs.restype = i
+        L.msa_validate_decode_inputs.argtypes = [P, i, P, i, i, i, P, P]
         _lib = L
     return _lib
 
@@ -329,6 +343,37 @@ def cache_insert(k, v, index_k, slot_mapping, k_cache, v_cache, index_k_cache):
     _check(lib().msa_cache_insert(_ptr(k), _ptr(v), _ptr(index_k), _ptr(slot_mapping), N,
                                   _index_code(index_k_cache), _ptr(k_cache), _ptr(v_cache),
                                   _ptr(index_k_cache), slots, _stream(device)))
+
+
+def validate_prefill_inputs(cu_seqlens, total_tokens, max_seqlen):
+    """Debug check of a document map on the device -> (bits, first): the OR of
+    the violated rules (INVALID_BITS; 0 = valid) and the lowest offending
+    document (-1 when valid).  Synchronises to read the result back."""
+    _dev_tensor("cu_seqlens", cu_seqlens, None, (torch.int32,))
+    status = torch.empty(2, dtype=torch.int32, device=cu_seqlens.device)
+    _check(lib().msa_validate_prefill_inputs(_ptr(cu_seqlens), int(cu_seqlens.numel()) - 1,
+                                             int(total_tokens), int(max_seqlen), _ptr(status),
+                                             _stream(cu_seqlens.device)))
+    bits, first = status.tolist()
+    return int(bits), int(first)
+
+
+def validate_decode_inputs(page_table, context_lens, max_context_len, num_pages):
+    """Debug check of a decode batch's page table and context lengths on the
+    device -> (bits, first): INVALID_BITS (0 = valid) and the lowest offending
+    request (-1 when valid).  Synchronises to read the result back."""
+    device = page_table.device
+    if page_table.dim() != 2:
+        raise ValueError("page_table must be 2-D [B, max_pages]")
+    B = int(page_table.shape[0])
+    _dev_tensor("page_table", page_table, None, (torch.int32,))
+    _dev_tensor("context_lens", context_lens, (B,), (torch.int32,), device)
+    status = torch.empty(2, dtype=torch.int32, device=device)
+    _check(lib().msa_validate_decode_inputs(_ptr(page_table), int(page_table.shape[1]),
+                                            _ptr(context_lens), B, int(max_context_len),
+                                            int(num_pages), _ptr(status), _stream(device)))
+    bits, first = status.tolist()
+    return int(bits), int(first)
 
 
 def _decode(q, index_q, k_cache, v_cache, index_k_cache, page_table, context_lens, max_context_len,

@@ -52,12 +52,14 @@ __global__ __launch_bounds__(64 * kPpw) void decode_scores_kernel(
     // the page-table entry is fetched together with the context length (an
     // entry past the context is in bounds and simply unused)
     const int page = pt[size_t(r) * max_pages + min(pi, max_pages - 1)];
-    const int L = min(max(ctx[r], 1), max_ctx);
+    const int L = min(ctx[r], max_ctx);  // <= 0: an empty request, nothing to score
     asm volatile("" ::"v"(page), "v"(L));  // keep the two loads ahead of the branch
-    const int nb = (L + kBlock - 1) / kBlock;
+    const int nb = L > 0 ? (L + kBlock - 1) / kBlock : 0;
     if (pi >= nb) return;
     const int n = lane & 15, qd = lane >> 4;
-    const size_t slot0 = size_t(page) * kBlock;
+    // a negative page id marks an absent block: its keys are read from page 0
+    // (in bounds) and its score is -inf
+    const size_t slot0 = size_t(max(page, 0)) * kBlock;
     constexpr int kRowBytes = kFp8 ? 128 : 256;
     const uint8_t *kbase = ikc + slot0 * kRowBytes;
     const uint8_t *qrow = iq + (size_t(r) * kIdxHeads + (n & 3)) * kRowBytes;
@@ -116,6 +118,7 @@ __global__ __launch_bounds__(64 * kPpw) void decode_scores_kernel(
         }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (page < 0) mx = -INFINITY;
     if (qd == 0 && n < kIdxHeads) S[(size_t(r) * kIdxHeads + n) * nb_max + pi] = mx;
 }
 
@@ -130,10 +133,13 @@ constexpr int kScoreWaves = 2048;
 
 struct HalfPage {
     u32x4 k[4][4];  // [M-tile][k-step]: keys 16mt + n of the half page, chunk 4ks + qd
+    bool absent;    // negative page id: the keys came from page 0 and do not count
 };
 
+// Pages of request r; a context length <= 0 marks an empty request (none).
 __device__ __forceinline__ int pages_of(const int32_t *ctx, int r, int max_ctx) {
-    return (min(max(ctx[r], 1), max_ctx) + kBlock - 1) / kBlock;
+    const int L = min(ctx[r], max_ctx);
+    return L > 0 ? (L + kBlock - 1) / kBlock : 0;
 }
 }  // namespace
 
@@ -175,7 +181,7 @@ __global__ __launch_bounds__(64) void decode_scores_stream_kernel(
         }
         before += __shfl(x, 63);
     }
-    int Lr = min(max(ctx[r], 1), max_ctx);
+    int Lr = min(ctx[r], max_ctx);  // >= 1: request r holds page p0
     int npr = (Lr + kBlock - 1) / kBlock;
 
     auto load_q = [&](int rr, bf16x8 (&qb)[4]) {
@@ -187,7 +193,8 @@ __global__ __launch_bounds__(64) void decode_scores_stream_kernel(
     };
     auto load_half = [&](int rr, int pg, int half, HalfPage &h) {
         const int page = pt[size_t(rr) * max_pages + pg];
-        const uint16_t *kbase = ikc + (size_t(page) * kBlock + 64 * half) * kDim;
+        h.absent = page < 0;
+        const uint16_t *kbase = ikc + (size_t(max(page, 0)) * kBlock + 64 * half) * kDim;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -209,7 +216,8 @@ __global__ __launch_bounds__(64) void decode_scores_stream_kernel(
             }
         }
         mx = fmaxf(mx, __shfl_xor(mx, 16));
-        return fmaxf(mx, __shfl_xor(mx, 32));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        return h.absent ? -INFINITY : mx;
     };
 
     bf16x8 qb[4];
@@ -223,13 +231,16 @@ __global__ __launch_bounds__(64) void decode_scores_stream_kernel(
         float pmax = half_max(h0, qb, pg, 0, Lr);
         // next page's first half loads while the second half is contracted
         int rn = r, pgn = pg + 1;
-        if (pgn == npr) { rn = r + 1; pgn = 0; }
+        if (pgn == npr && p + 1 < p1) {  // the next non-empty request holds page p + 1
+            pgn = 0;
+            do { ++rn; } while (pages_of(ctx, rn, max_ctx) == 0);
+        }
         if (p + 1 < p1) load_half(rn, pgn, 0, h0);
         pmax = fmaxf(pmax, half_max(h1, qb, pg, 1, Lr));
         if (qd == 0 && n < kIdxHeads) S[(size_t(r) * kIdxHeads + n) * nb_max + pg] = pmax;
-        if (rn != r && p + 1 < p1) {
+        if (rn != r) {
             r = rn;
-            Lr = min(max(ctx[r], 1), max_ctx);
+            Lr = min(ctx[r], max_ctx);
             npr = (Lr + kBlock - 1) / kBlock;
             load_q(r, qb);
         }
@@ -482,7 +493,22 @@ __global__ __launch_bounds__(256) void decode_attend_stream_kernel(
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 15, qd = lane >> 4;
-    const int L = min(max(ctx[r], 1), max_ctx);
+    const int L = min(ctx[r], max_ctx);
+    if (L <= 0) {
+        // an empty (padding) request: nothing is read; an empty partial
+        // (m = -inf, l = 0, O = 0) makes its output row zero, and its q2k
+        // row is all -1
+        if (q2k_out && sg == 0 && tid < topk) q2k_out[(size_t(g) * B + r) * topk + tid] = -1;
+        float *po = part_o + ((size_t(r) * kKvHeads + g) * nparts + sg) * (kGroup * kDim);
+        float *pml = part_ml + ((size_t(r) * kKvHeads + g) * nparts + sg) * (kGroup * 2);
+        *(f32x4 *)(po + 8 * tid) = f32x4{};
+        *(f32x4 *)(po + 8 * tid + 4) = f32x4{};
+        if (tid < kGroup) {
+            pml[2 * tid] = -INFINITY;
+            pml[2 * tid + 1] = 0.f;
+        }
+        return;
+    }
     const int c = (L - 1) / kBlock;
     const int key0 = 32 * wave;
     uint8_t *ring = smem + wave * SL::kWave;
@@ -499,20 +525,23 @@ __global__ __launch_bounds__(256) void decode_attend_stream_kernel(
     select_row<kCpl>(S + (size_t(r) * kIdxHeads + g) * nb_max, nb_max, c, topk, init, local, lane, s_sel[wave]);
     __builtin_amdgcn_wave_barrier();
     if (q2k_out && sg == 0 && wave == 0 && lane < topk) q2k_out[(size_t(g) * B + r) * topk + lane] = s_sel[0][lane];
-    // the workgroup's slots (wave-uniform): block id, or -1 when unselected
-    int bsel[kStreamSlots];
+    // the workgroup's slots (wave-uniform): block id, or -1 when unselected,
+    // and the block's physical page (a negative page id marks an absent
+    // block: its copies read page 0, in bounds, and all its keys are masked)
+    int bsel[kStreamSlots], bpage[kStreamSlots];
 #pragma unroll
     for (int j = 0; j < kStreamSlots; ++j) {
         const int s = sg * spw + j;
         const int b = (j < spw && s < topk) ? __builtin_amdgcn_readfirstlane(s_sel[wave][s]) : -1;
         bsel[j] = (b >= 0 && b <= c) ? b : -1;
+        bpage[j] = bsel[j] >= 0 ? pt[size_t(r) * max_pages + bsel[j]] : 0;
     }
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): q is in before any copy is issued
     // copies of slot j into stage st: K rows key0..key0+31 (8 one-KiB copies)
     // then V rows (8); rows past L re-read the last valid row (masked)
     auto issue = [&](int j, int st) {
         const int b = bsel[j];
-        const size_t slot0 = size_t(pt[size_t(r) * max_pages + b]) * kBlock;
+        const size_t slot0 = size_t(max(bpage[j], 0)) * kBlock;
         const int kmax = L - 1 - b * kBlock;
         uint8_t *kb = ring + st * SL::kStage;
         constexpr int kRowsPerCopy = 1024 / SL::kRowBytes;  // 4 (bf16) or 8 (E4M3)
@@ -551,7 +580,7 @@ __global__ __launch_bounds__(256) void decode_attend_stream_kernel(
         }
         const uint8_t *kb = ring + (j & 1) * SL::kStage;
         const uint8_t *vt = kFp8Kv ? ring + SL::kVbf : kb + SL::kHalf;
-        const int kmax = L - 1 - bsel[j] * kBlock;
+        const int kmax = bpage[j] < 0 ? -1 : L - 1 - bsel[j] * kBlock;
         if constexpr (kFp8Kv) {
             // widen this wave's 32 V rows into the bf16 buffer: lane -> row
             // lane/2, byte chunks 4(lane%2)..+3 (16 E4M3 values each)

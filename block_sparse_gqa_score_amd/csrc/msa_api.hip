@@ -6,6 +6,7 @@
 #include <stdio.h>
 #include <string.h>
 
+
 #include "msa.h"
 #include "msa_internal.hpp"
 
@@ -476,6 +477,34 @@ msa_status msa_cache_insert(const uint16_t *k, const uint16_t *v, const uint16_t
                                              index_dtype == MSA_INDEX_FP8_E4M3, k_cache, v_cache,
                                              index_k_cache, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "cache_insert");
+    return MSA_OK;
+}
+
+msa_status msa_validate_prefill_inputs(const int32_t *cu_seqlens, int num_docs, int total_tokens,
+                                       int max_seqlen, int32_t *status, void *stream) {
+    if (!status) return fail(MSA_ERR_INVALID_ARG, "status must be non-NULL");
+    msa_status st = check_geometry(cu_seqlens, num_docs, total_tokens, max_seqlen);
+    if (st != MSA_OK) return st;
+    const hipError_t e = launch_validate_prefill(cu_seqlens, num_docs, total_tokens, max_seqlen, status,
+                                                 (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "validate_prefill");
+    return MSA_OK;
+}
+
+msa_status msa_validate_decode_inputs(const int32_t *page_table, int max_pages_per_seq,
+                                      const int32_t *context_lens, int batch, int max_context_len,
+                                      int num_pages, int32_t *status, void *stream) {
+    if (!page_table || !context_lens || !status)
+        return fail(MSA_ERR_INVALID_ARG, "page_table, context_lens and status must be non-NULL");
+    if (batch < 1) return fail(MSA_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", batch);
+    if (max_context_len < 1) return fail(MSA_ERR_INVALID_ARG, "max_context_len must be >= 1");
+    if (num_pages < 1) return fail(MSA_ERR_INVALID_ARG, "num_pages must be >= 1 (got %d)", num_pages);
+    if (max_pages_per_seq < ceil_div(max_context_len, kBlock))
+        return fail(MSA_ERR_INVALID_ARG, "max_pages_per_seq (%d) < ceil(max_context_len/128) (%d)",
+                    max_pages_per_seq, ceil_div(max_context_len, kBlock));
+    const hipError_t e = launch_validate_decode(page_table, max_pages_per_seq, context_lens, batch,
+                                                max_context_len, num_pages, status, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "validate_decode");
     return MSA_OK;
 }
 

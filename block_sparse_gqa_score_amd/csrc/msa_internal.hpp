@@ -97,6 +97,13 @@ hipError_t launch_cache_insert(const uint16_t *k, const uint16_t *v, const uint1
                                int n, int num_slots, bool fp8, uint16_t *kc, uint16_t *vc, void *ikc,
                                hipStream_t stream);
 
+// Debug validators of the device-side contract: status[0] = violation bits
+// (msa_invalid_bits), status[1] = lowest offending document / request.
+hipError_t launch_validate_prefill(const int32_t *cu, int ndocs, int T, int max_seqlen, int32_t *status,
+                                   hipStream_t stream);
+hipError_t launch_validate_decode(const int32_t *pt, int max_pages, const int32_t *ctx, int B, int max_ctx,
+                                  int num_pages, int32_t *status, hipStream_t stream);
+
 // MXFP8 encoding of n bf16 values (n a multiple of 32): q [n] E4M3, scale [n/32] E8M0.
 hipError_t launch_mxfp8_quantize(const uint16_t *in, int64_t n, uint8_t *q, uint8_t *scale,
                                  hipStream_t stream);

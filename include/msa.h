@@ -34,9 +34,12 @@
  *    GPU work is enqueued; msa_last_error() then returns a message
  *    (thread-local).  Contract violations in device data (e.g. a
  *    cu_seqlens that is not increasing, a page id out of range) are not
- *    detected: kernels clamp document bounds to [0, total_tokens] so they
- *    never read outside the buffers the host scalars describe, but the
- *    output is then unspecified.  Page ids must lie in the cache.
+ *    detected by the compute calls: kernels clamp document bounds to
+ *    [0, total_tokens] so they never read outside the buffers the host
+ *    scalars describe, but the output is then unspecified.  Page ids must
+ *    lie in the cache; a negative page id reads nothing (see the decode
+ *    call).  msa_validate_prefill_inputs / msa_validate_decode_inputs check
+ *    the device data on request (a debugging aid, off the hot path).
  *  - The same inputs give bitwise identical outputs on every call (no
  *    atomics in any reduction).
  */
@@ -202,7 +205,12 @@ msa_status msa_sparse_attend_prefill_backward(
  *      [num_pages*128,1,128] in index_dtype.  Slots past L are never used
  *      (they may hold anything, NaN included).
  *  page_table int32 [B,max_pages_per_seq]; entries past ceil(L/128) unread.
- *  context_lens int32 [B], each in [1, max_context_len].
+ *      Ids must lie in [0, num_pages); a negative id marks an absent page:
+ *      nothing of it is read, its block scores -inf and, if forced or
+ *      selected, adds no key.
+ *  context_lens int32 [B], each in [0, max_context_len]; 0 (or less) marks an
+ *      empty (padding) request: nothing of it is read, its out row is zero
+ *      and its q2k_out row is all -1.
  *  out [B,64,128] bf16.  q2k_out optional int32 [4,B,topk] (NULL to skip).
  */
 msa_status msa_sparse_attend_decode_paged(
@@ -286,6 +294,45 @@ msa_status msa_cache_insert(const uint16_t *k, const uint16_t *v, const uint16_t
  */
 msa_status msa_mxfp8_quantize(const uint16_t *in, int rows, int cols, uint8_t *out_q,
                               uint8_t *out_scale, void *stream);
+
+/*
+ * Debug validators of the device-side data contract (a debugging aid: the
+ * compute calls never run them).  Each enqueues one small kernel on
+ * `stream` that reads the device data and writes a status pair:
+ *   status[0] = OR of msa_invalid_bits (0 when the data is valid),
+ *   status[1] = the lowest offending document (prefill) or request
+ *               (decode), -1 when valid.
+ * `status` is caller-owned device memory of 2 int32; both words are
+ * overwritten (no clearing needed).  The host scalars are those of the
+ * compute call; host-side errors return MSA_ERR_INVALID_ARG as there.
+ *
+ * msa_validate_prefill_inputs follows the document-map rules of the NeMo
+ * msa page (the document-map classmethod's ValueErrors: no empty or
+ * interrupted document, coordinates within range): cu_seqlens[0] == 0,
+ * strictly increasing, cu_seqlens[num_docs] == total_tokens, every length
+ * <= max_seqlen.
+ *
+ * msa_validate_decode_inputs checks, for every request, context_lens[r] in
+ * [0, max_context_len] and every page id it uses (blocks below
+ * ceil(L/128)) in [0, num_pages), num_pages being the caches' page count
+ * (TensorRT-LLM config class description: main K/V and side index-K share
+ * the slots).
+ */
+typedef enum {
+    MSA_INVALID_CU_START = 1,     /* cu_seqlens[0] != 0                       */
+    MSA_INVALID_CU_END = 2,       /* cu_seqlens[num_docs] != total_tokens     */
+    MSA_INVALID_DOC_EMPTY = 4,    /* a document of length <= 0                */
+    MSA_INVALID_DOC_LONG = 8,     /* a document longer than max_seqlen        */
+    MSA_INVALID_CU_RANGE = 16,    /* an offset outside [0, total_tokens]      */
+    MSA_INVALID_CONTEXT_LEN = 32, /* a context length outside [0, max_ctx]    */
+    MSA_INVALID_PAGE_ID = 64      /* a used page id outside [0, num_pages)    */
+} msa_invalid_bits;
+
+msa_status msa_validate_prefill_inputs(const int32_t *cu_seqlens, int num_docs, int total_tokens,
+                                       int max_seqlen, int32_t *status, void *stream);
+msa_status msa_validate_decode_inputs(const int32_t *page_table, int max_pages_per_seq,
+                                      const int32_t *context_lens, int batch, int max_context_len,
+                                      int num_pages, int32_t *status, void *stream);
 
 /*
  * Benchmark instrumentation (not part of the method).  Arms the NEXT

@@ -260,3 +260,29 @@ def subset_decode(w, requests):
     d.page_table = np.ascontiguousarray(w.page_table[requests])
     d.context_lens = np.ascontiguousarray(w.context_lens[requests])
     return d
+
+
+def planted_gap(w, tokens):
+    """Realised separation of the planted blocks in a planted prefill workload
+    (``w.meta['planted_blocks']``), from the oracle's block scores of the
+    listed tokens: over every (token, index head) candidate entry, the mean
+    block score of planted and of unplanted blocks, their difference, the
+    difference in units of the unplanted block scores' standard deviation,
+    and the share of the chosen free slots that went to planted blocks."""
+    planted = np.asarray(w.meta["planted_blocks"], dtype=np.int64)
+    r = prefill_select(w, tokens)
+    S = r["S"]                                   # [n,4,nb]
+    nb = S.shape[2]
+    is_pl = np.zeros(nb, dtype=bool)
+    is_pl[planted[planted < nb]] = True
+    cand = np.isfinite(S)
+    pl = S[cand & is_pl[None, None, :]]
+    un = S[cand & ~is_pl[None, None, :]]
+    q2k = r["q2k"]
+    c = r["c"][:, None, None]
+    forced = (q2k >= 0) & ((q2k < w.init_blocks) | (q2k >= c - w.local_blocks + 1))
+    free = (q2k >= 0) & ~forced
+    chosen_pl = is_pl[np.clip(q2k, 0, nb - 1)] & free
+    return dict(tokens=int(len(r["tokens"])), planted_mean=float(pl.mean()), unplanted_mean=float(un.mean()),
+                gap=float(pl.mean() - un.mean()), gap_in_unplanted_sd=float((pl.mean() - un.mean()) / un.std()),
+                planted_share_of_free_slots=float(chosen_pl.sum() / max(1, free.sum())))

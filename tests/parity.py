@@ -91,3 +91,28 @@ def sample_tokens(cu, per_doc=24, seed=0):
         if L > 2:
             out.update((s + rng.integers(0, L, size=min(per_doc, L))).tolist())
     return np.array(sorted(out), dtype=np.int32)
+
+
+def sample_tiles(cu, n_tiles=128, tile=16, seed=0):
+    """Tokens of whole document-aligned tiles of ``tile`` consecutive tokens
+    (the prefill attention's work unit), about ``n_tiles`` in all, spread over
+    every document in proportion to its length: each document's first and
+    last tile (the last one may be partial), the tiles holding its block
+    edges 127/128 and its last block's start, and seeded random tiles
+    elsewhere.  Returns sorted token indices."""
+    rng = np.random.default_rng(seed)
+    cu = np.asarray(cu, dtype=np.int64)
+    T = int(cu[-1])
+    out = set()
+    for d in range(len(cu) - 1):
+        s, e = int(cu[d]), int(cu[d + 1])
+        L = e - s
+        nt = -(-L // tile)
+        pick = {0, nt - 1, 127 // tile, 128 // tile, ((L - 1) // 128) * 128 // tile}
+        want = max(2, int(round(n_tiles * L / T)))
+        extra = rng.choice(nt, size=min(nt, want), replace=False)
+        pick.update(int(x) for x in extra)
+        for i in pick:
+            if 0 <= i < nt:
+                out.update(range(s + i * tile, min(e, s + (i + 1) * tile)))
+    return np.array(sorted(out), dtype=np.int32)

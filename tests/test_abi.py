@@ -263,3 +263,27 @@ def test_backward_workspace_bytes():
     assert msa.prefill_backward_workspace_bytes(T, D, T, 17) == 0
     assert msa.prefill_backward_workspace_bytes((1 << 22) + 1, 1, 100, 16) == 0
     assert msa.prefill_backward_workspace_bytes(0, 1, 1, 16) == 0
+
+
+@pytest.mark.parametrize("args,needle", [
+    ((None, 1, 10, 10, FAKE), "cu_seqlens"),
+    ((FAKE, 0, 10, 10, FAKE), "num_docs"),
+    ((FAKE, 1, 10, 11, FAKE), "max_seqlen"),
+    ((FAKE, 1, 10, 10, None), "status"),
+])
+def test_validate_prefill_rejects_host_errors(args, needle):
+    assert msa.lib().msa_validate_prefill_inputs(*args, None) == 1
+    assert needle in msa.lib().msa_last_error().decode()
+
+
+@pytest.mark.parametrize("args,needle", [
+    ((None, 1, FAKE, 1, 128, 1, FAKE), "page_table"),
+    ((FAKE, 1, FAKE, 0, 128, 1, FAKE), "batch"),
+    ((FAKE, 1, FAKE, 1, 0, 1, FAKE), "max_context_len"),
+    ((FAKE, 1, FAKE, 1, 128, 0, FAKE), "num_pages"),
+    ((FAKE, 1, FAKE, 1, 129, 5, FAKE), "max_pages_per_seq"),
+    ((FAKE, 1, FAKE, 1, 128, 1, None), "status"),
+])
+def test_validate_decode_rejects_host_errors(args, needle):
+    assert msa.lib().msa_validate_decode_inputs(*args, None) == 1
+    assert needle in msa.lib().msa_last_error().decode()

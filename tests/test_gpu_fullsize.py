@@ -11,14 +11,24 @@ import torch
 import block_sparse_gqa_score_amd as msa
 import oracle
 import workloads as W
-from parity import check_attention, check_scores, check_selection, dev, sample_tokens
+from parity import check_attention, check_scores, check_selection, dev, sample_tiles, sample_tokens
 
 pytestmark = pytest.mark.gpu
 
 
+_CONFIGS = {}
+
+
+def _config(i):
+    if i not in _CONFIGS:
+        _CONFIGS.clear()
+        _CONFIGS[i] = W.config(i)
+    return _CONFIGS[i]
+
+
 def _prefill_case(i, tokens=None):
     t0 = time.time()
-    w = W.config(i)
+    w = _config(i)
     print(f"[config {i}: {w.name}] T={w.T} docs={w.num_docs} generated in {time.time() - t0:.1f}s",
           flush=True)
     iq, ik, cu = dev(w.iq), dev(w.ik), dev(w.cu_seqlens)
@@ -51,14 +61,46 @@ def test_config0_prefill_2k_all_tokens():
     assert same.mean() > 0.99
 
 
+def _tiles_and_edges(cu):
+    """About 2048 tokens as whole 16-token tiles (at least 8 of them, down to
+    the last block of every document), plus the block-edge tokens."""
+    toks = np.union1d(sample_tiles(cu, n_tiles=128), sample_tokens(cu))
+    assert len(toks) >= 2048
+    return toks.astype(np.int32)
+
+
 def test_config2_prefill_32k_planted_sampled():
-    w, same = _prefill_case(2)
+    w = _config(2)
+    tokens = _tiles_and_edges(w.cu_seqlens)
+    w, same = _prefill_case(2, tokens=tokens)
     assert same.mean() > 0.95
 
 
 def test_config3_packed_documents_sampled():
-    w, same = _prefill_case(3)
+    w = _config(3)
+    tokens = _tiles_and_edges(w.cu_seqlens)
+    w, same = _prefill_case(3, tokens=tokens)
     assert w.num_docs >= 2
+    assert same.mean() > 0.95
+
+
+def test_config2_selection_e4m3_index():
+    """The 32768-token planted document with its index q/k stored as E4M3FN
+    bytes (the fp8 indexer's unscaled E4M3 values, FP32 accumulation): the
+    E4M3 block scorer and the top-k at the size the benchmark times them,
+    against the oracle on sampled rows (whole 16-token tiles and block
+    edges)."""
+    w = W.with_e4m3_index(_config(2))
+    print(f"[config 2, E4M3 index] T={w.T}", flush=True)
+    q2k, S = msa.select_blocks(dev(w.iq), dev(w.ik), dev(w.cu_seqlens), w.max_seqlen, w.topk,
+                               w.init_blocks, w.local_blocks, scores=True)
+    torch.cuda.synchronize()
+    tokens = np.union1d(sample_tiles(w.cu_seqlens, n_tiles=64), sample_tokens(w.cu_seqlens)).astype(np.int32)
+    ref = oracle.prefill_select(w, tokens=tokens)
+    print(f"  oracle rows: {len(tokens)}", flush=True)
+    check_scores(S.cpu().numpy(), ref, tokens)
+    same = check_selection(q2k.cpu().numpy()[:, tokens].transpose(1, 0, 2), ref, w.topk,
+                           w.init_blocks, w.local_blocks)
     assert same.mean() > 0.95
 
 

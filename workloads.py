@@ -295,6 +295,22 @@ def make_prefill(doc_lens, seed: int, *, topk=16, init_blocks=0, local_blocks=1,
                    local_blocks=local_blocks, meta=meta)
 
 
+def with_e4m3_index(w: Prefill) -> Prefill:
+    """The same prefill batch with its bf16 index q/k re-encoded as E4M3FN
+    bytes (nearest value, ties to the even code): the fp8 indexer's unscaled
+    E4M3 storage of the same index vectors.  The main q/k/v are shared."""
+    if w.index_dtype != "bf16":
+        raise ValueError("expects bf16 index vectors")
+
+    def dec(bits):
+        return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+    return Prefill(name=w.name + "_e4m3_index", cu_seqlens=w.cu_seqlens, q=w.q, k=w.k, v=w.v,
+                   iq=e4m3_bytes(dec(w.iq)), ik=e4m3_bytes(dec(w.ik)), index_dtype="fp8",
+                   topk=w.topk, init_blocks=w.init_blocks, local_blocks=w.local_blocks,
+                   scale=w.scale, meta=dict(w.meta))
+
+
 def packed_doc_lengths(seed: int, rows: int = 2, seq: int = 16384,
                        lo: int = 256, hi: int = 8192):
     """Document lengths of a packed BSHD microbatch.
