@@ -118,6 +118,9 @@ def lib():
                                                            f, P, P, P, sz, P]
         L.msa_cache_insert.restype = i
         L.msa_cache_insert.argtypes = [P, P, P, P, i, i, P, P, P, i, P]
+        L.msa_sparse_attend_decode_paged_noalloc.restype = i
+        L.msa_sparse_attend_decode_paged_noalloc.argtypes = [P, P, P, P, P, i, P, i, P, i, i, i, i, i, f,
+                                                             P, P, P]
         L.msa_validate_prefill_inputs.restype = i
         L.msa_validate_prefill_inputs.argtypes = [P, i, i, i, P, P]
         L.msa_validate_decode_inputs.restype = i

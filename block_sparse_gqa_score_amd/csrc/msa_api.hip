@@ -6,6 +6,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 
 #include "msa.h"
 #include "msa_internal.hpp"
@@ -433,6 +434,67 @@ msa_status msa_sparse_attend_decode_paged(
                              max_pages_per_seq, context_lens, batch, max_context_len, topk, init_blocks,
                              local_blocks, softmax_scale, out, nullptr, nullptr, q2k_out, workspace,
                              workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Allocation-free decode: the workspace is a file-scope device array of
+// MSA_NOALLOC_SCRATCH_BYTES per GPU (held from library load to process end).
+// Host code never uses the array's name as an address: on a device's first
+// call, with that device current, hipGetSymbolAddress gives the device
+// address, which is kept per device and passed to the kernels.
+// ---------------------------------------------------------------------------
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[MSA_NOALLOC_SCRATCH_BYTES];
+
+static msa_status scratch_of_current_device(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(MSA_ERR_UNSUPPORTED, "device %d is beyond the %d devices the scratch table holds", dev,
+                    kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!p) return fail(MSA_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return MSA_OK;
+}
+
+extern "C" {
+
+msa_status msa_sparse_attend_decode_paged_noalloc(
+    const uint16_t *q, const void *index_q, const uint16_t *k_cache, const uint16_t *v_cache,
+    const void *index_k_cache, int index_dtype, const int32_t *page_table, int max_pages_per_seq,
+    const int32_t *context_lens, int batch, int max_context_len, int topk, int init_blocks,
+    int local_blocks, float softmax_scale, uint16_t *out, int32_t *q2k_out, void *stream) {
+    if (!out) return fail(MSA_ERR_INVALID_ARG, "out must be non-NULL");
+    const size_t need = msa_decode_workspace_bytes(batch, max_context_len, topk);
+    if (need > MSA_NOALLOC_SCRATCH_BYTES)
+        return fail(MSA_ERR_UNSUPPORTED,
+                    "this batch needs %zu bytes of scratch; the allocation-free decode holds %zu "
+                    "(use msa_sparse_attend_decode_paged with a workspace)",
+                    need, size_t(MSA_NOALLOC_SCRATCH_BYTES));
+    void *ws = nullptr;
+    const msa_status st = scratch_of_current_device(&ws);
+    if (st != MSA_OK) return st;
+    // every scratch byte the kernels read is written earlier in the same
+    // call (scores, then partials), so nothing needs clearing
+    return decode_paged_impl(q, index_q, k_cache, v_cache, false, 1.f, 1.f, index_k_cache, index_dtype, page_table,
+                             max_pages_per_seq, context_lens, batch, max_context_len, topk, init_blocks,
+                             local_blocks, softmax_scale, out, nullptr, nullptr, q2k_out, ws,
+                             MSA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 msa_status msa_sparse_attend_decode_paged_mxfp8(

@@ -221,6 +221,32 @@ msa_status msa_sparse_attend_decode_paged(
     int32_t *q2k_out, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * msa_sparse_attend_decode_paged without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  The same kernels run
+ * with their scratch (block scores, attention partials) in a device array
+ * of MSA_NOALLOC_SCRATCH_BYTES that the library holds per GPU from load to
+ * process end; the call allocates nothing.
+ *
+ *  Arguments, outputs and errors are those of msa_sparse_attend_decode_paged;
+ *  in addition MSA_ERR_UNSUPPORTED when msa_decode_workspace_bytes(batch,
+ *  max_context_len, topk) exceeds MSA_NOALLOC_SCRATCH_BYTES (e.g. batch 128
+ *  at 131072 tokens fits; batch 256 at 131072 does not).
+ *  The scratch of a GPU is that of the device current on the calling thread
+ *  (call with the stream's device current).  Every call on one GPU shares
+ *  its array, so calls that overlap on one GPU (several streams, or several
+ *  threads) race: serialise them.  No byte of the array needs to start at
+ *  zero: each call writes what it reads.
+ */
+#define MSA_NOALLOC_SCRATCH_BYTES (16u << 20)
+msa_status msa_sparse_attend_decode_paged_noalloc(
+    const uint16_t *q, const void *index_q, const uint16_t *k_cache, const uint16_t *v_cache,
+    const void *index_k_cache, int index_dtype, const int32_t *page_table,
+    int max_pages_per_seq, const int32_t *context_lens, int batch, int max_context_len,
+    int topk, int init_blocks, int local_blocks, float softmax_scale, uint16_t *out,
+    int32_t *q2k_out, void *stream);
+
+/*
  * The same decode step with its output emitted as MXFP8 for the projection
  * that follows (vLLM MiniMax-M3 page, MiniMaxM3SparseRocmNvfp4Impl,
  * forward_decode_mxfp8): equal to msa_mxfp8_quantize of the bf16 output
