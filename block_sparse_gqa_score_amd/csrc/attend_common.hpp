@@ -18,7 +18,7 @@ __device__ __forceinline__ void barrier_keep_prefetch() {
 }
 
 // Wait until at most n of this wave's copies are outstanding (copies
-// complete in issue order).  n > 16 falls back to a full wait.
+// complete in issue order).  n > 40 falls back to a full wait.
 __device__ __forceinline__ void wait_copies(int n) {
 #define MSA_WAIT_CASE(i) \
     case i: asm volatile("s_waitcnt vmcnt(" #i ")" ::: "memory"); break;
@@ -27,6 +27,9 @@ __device__ __forceinline__ void wait_copies(int n) {
         MSA_WAIT_CASE(5) MSA_WAIT_CASE(6) MSA_WAIT_CASE(7) MSA_WAIT_CASE(8)
         MSA_WAIT_CASE(9) MSA_WAIT_CASE(10) MSA_WAIT_CASE(11) MSA_WAIT_CASE(12)
         MSA_WAIT_CASE(13) MSA_WAIT_CASE(14) MSA_WAIT_CASE(15) MSA_WAIT_CASE(16)
+        MSA_WAIT_CASE(17) MSA_WAIT_CASE(18) MSA_WAIT_CASE(19) MSA_WAIT_CASE(20)
+        MSA_WAIT_CASE(24) MSA_WAIT_CASE(28) MSA_WAIT_CASE(32) MSA_WAIT_CASE(36)
+        MSA_WAIT_CASE(40)
         default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
     }
 #undef MSA_WAIT_CASE

@@ -13,50 +13,65 @@
 //       that a unit's K rows of one head are 8 KiB contiguous (in the input
 //       they are 256 B apart from each other by the other heads' rows).  Keys
 //       past the document end are 0 in both.
-//   attend_prefill_kernel - workgroup = (KV head g, 16 consecutive tokens of
-//       one document inside one 128-token block, so all share the query
-//       block c); 8 waves, each owning 2 tokens x 16 heads.  The workgroup
-//       walks the UNION of its tokens' selected blocks in ascending order as
-//       32-key units (K rows 8 KiB + V^T rows 8 KiB), copied HBM -> LDS by
-//       global_load_lds_dwordx4 into a 9-slot ring; the waves meet at one
-//       barrier per union block, while the next five units stream in.  A
-//       wave computes a block only for those of its two tokens that selected
-//       it, as one chain over the block's 128 keys (one softmax step); the K
-//       and V^T fragments it reads from LDS serve both tokens.  Blocks that a
-//       single token selected skip the ring: that token's wave reads them
-//       straight from memory, one 32-key unit in each ring iteration where it
-//       has no token in the ring's block, and the rest after the ring.
+//   attend_prefill_kernel - workgroup = (KV head g, a tile of up to 24
+//       consecutive tokens of one document inside one 128-token block, so all
+//       share the query block c; a query block is cut into 6 near-equal
+//       tiles); 8 waves, two per SIMD, each owning 3 token slots x 16 heads
+//       (tile token i is slot i/8 of wave i%8): their Q^T operands stay in
+//       VGPRs and their O^T accumulators in AGPRs.  The workgroup streams the
+//       union of its tokens' selected blocks, ascending, as 32-key units (K
+//       rows 8 KiB + V^T rows 8 KiB) HBM -> LDS by global_load_lds_dwordx4
+//       through a 9-slot ring, with no workgroup barrier: every unit has an
+//       LDS state word (ready bit, count of the waves that still need it).
+//       Each wave walks only the units its tokens need.  A wave that needs a
+//       unit nobody has copied yet claims it and issues its 16 copies once
+//       every wave needing the unit 9 places earlier is done with that slot;
+//       before computing a unit it claims its next one the same way, so the
+//       copies land during the compute.  A wave computes a unit for those of
+//       its tokens that selected the block; the K and V^T fragments it reads
+//       from LDS once serve all of them.  The slowest wave can always claim
+//       its next unit, so the waits end; each is also bounded by a poll limit.
 //
 // Per wave, token and 32-key unit (MFMA 16x16x32 bf16, key rows m, head
 // columns n):
 //   S^T[32 x 16] = K . Q^T       2 M-tiles x 4 k-steps; M-tile mt row i is key
 //                                 8(i/4) + 4mt + i%4, so lane (n, grp) holds
 //                                 keys 8grp..8grp+7 of column n in order;
-//   causal mask in the query's own block, online softmax in the exp2 domain
-//   with lazy rescaling (the reference max only moves when it grows by more
-//   than 2^8), P^T packed to bf16 straight from the accumulators,
+//   causal mask in the tile's own units of the query block, online softmax
+//   per unit in the exp2 domain with lazy rescaling (the reference max only
+//   moves when it grows by more than 2^8), P^T packed to bf16 straight from
+//   the accumulators,
 //   O^T[128 x 16] += V^T . P^T   8 d-tiles x 1 k-step.
 #include "attend_common.hpp"
 
 namespace msa {
 
 namespace {
-constexpr int kTok = kAttnTile;                        // 16 tokens per workgroup
-constexpr int kWaves = kTok / 2;                       // 8 waves, 2 tokens each
-constexpr int kThreads = 64 * kWaves;                  // 512
+constexpr int kTok = kFwdTile;                         // most tokens per workgroup
+constexpr int kWaves = kFwdWaves;                      // waves per workgroup
+constexpr int kTpw = kTok / kWaves;                    // token slots per wave
+constexpr int kBitsPerWave = 32 / kWaves;              // a wave's field in a 32-bit token mask
+constexpr int kTilesPerBlock = (kBlock + kTok - 1) / kTok;  // tiles per 128-token query block
+constexpr int kThreads = 64 * kWaves;
 constexpr int kUnitsPerBlock = kBlock / kAttnUnit;     // 4
 constexpr int kKUnitBytes = kAttnUnit * kDim * 2;      // 8 KiB of K rows
 constexpr int kVUnitBytes = kDim * kAttnUnit * 2;      // 8 KiB of V^T rows
 constexpr int kUnitBytes = kKUnitBytes + kVUnitBytes;  // 16 KiB
-constexpr int kRing = 9;  // LDS ring slots of one unit each (144 KiB)
-constexpr int kLoadsPerWave = kUnitBytes / 1024 / kWaves;  // 2 one-KiB copies
+constexpr int kRing = 9;  // LDS ring slots of one unit each (144 KiB, with the tables below < 160 KiB)
+constexpr int kMaxUnion = kTok * kMaxTopk;             // distinct blocks of a tile at most
+constexpr int kUnionListBytes = kMaxUnion * 8;         // (block, token mask) pairs
+// Block-id window of the union's mask table (it shares the ring's LDS with
+// the union list, before any copy is issued).
+constexpr int kTableIds = (kRing * kUnitBytes - kUnionListBytes) / 4;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazyLog2 = 8.f;  // rescale only when the max grows by > 2^8
-constexpr int kSharedMin = 2;     // union blocks this many tokens selected go through the ring
+constexpr int kMaxUnits = kUnitsPerBlock * kMaxUnion;  // ring units of a tile at most
+// Unit state words in LDS: bits 0-7 count the waves that still have to read
+// the unit, kClaimed / kReady mark its copy issued / landed.
+constexpr uint32_t kClaimed = 0x100u, kReady = 0x200u;
+constexpr int kSpinLimit = 1 << 14;  // polls before a wait gives up (never reached in a correct run)
 
-static_assert(kLoadsPerWave == 2, "unit copy split assumes 2 copies per wave");
-static_assert(kRing == 2 * kUnitsPerBlock + 1, "one unit of the block after next streams ahead");
-static_assert(kRing * kUnitBytes <= 144 * 1024, "ring must leave LDS for the union tables");
+static_assert(kTpw * kWaves == kTok && kTpw <= kBitsPerWave && kTpw <= 8, "slots fit the mask fields");
 
 // K unit in LDS: row r (key), 16-byte chunk c (d 8c..8c+7) at slot
 // 16r + (c ^ kswz(r)).  The 16 lanes of an operand read hold rows
@@ -66,178 +81,199 @@ __device__ __forceinline__ int kswz(int r) { return (((r >> 3) & 3) << 2) | (r &
 // 16 consecutive rows at one chunk cover all 16 chunk positions of 256 B.
 __device__ __forceinline__ int vswz(int d) { return (d >> 2) & 3; }
 
-// Per-wave state: query operands and running softmax of the wave's two
+// Per-wave state: query operands and running softmax of the wave's 8
 // tokens (column n of each is head n of the KV group).
 struct WaveState {
-    bf16x8 qb[2][4];
-    f32x4 acc_o[2][8];
-    float m_ref[2];  // raw-score reference of the exponentials
-    float l_run[2];
+    bf16x8 qb[kTpw][4];
+    f32x4 acc_o[kTpw][8];
+    float m_ref[kTpw];  // raw-score reference of the exponentials
+    float l_run[kTpw];
 };
 
-// One union block for one wave.  kA0/kA1: which tokens compute (fixed at
-// compile time, so the whole chain is straight-line code the scheduler can
-// overlap: LDS reads of unit q+1 run under the MFMAs of unit q).  kDiag:
-// the query's own block, with nq <= 4 units, the causal mask, and the
-// active tokens taken from act_rt at run time.
-template <bool kA0, bool kA1, bool kDiag>
-__device__ __forceinline__ void attend_block(WaveState &st, const uint8_t *smem, int ustart, int nq,
-                                             const int (&k_row_off)[2], int v_off, int n, int grp,
-                                             int keyb, const bool (&act_rt)[2],
-                                             const int (&my_p)[2], float scale_log2) {
-    const bool act[2] = {kDiag ? act_rt[0] : kA0, kDiag ? act_rt[1] : kA1};
-    // S^T for the block: unit q, M-tile mt of token t
-    f32x4 sacc[2][kUnitsPerBlock][2];
+// S^T of one unit for token t: K fragments ka (shared by the wave's tokens).
+template <int t>
+__device__ __forceinline__ void unit_scores(const WaveState &st, const bf16x8 (&ka)[4][2], f32x4 (&s)[2]) {
+    s[0] = f32x4{};
+    s[1] = f32x4{};
 #pragma unroll
-    for (int q = 0; q < kUnitsPerBlock; ++q) {
-        if (kDiag && q >= nq) break;
-        const uint8_t *Ku = smem + ((ustart + q) % kRing) * kUnitBytes;
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) s[mt] = mfma_16x16x32(ka[ks][mt], st.qb[t][ks], s[mt]);
+}
+
+// Online-softmax step of token t over one unit's 32 keys (this lane: keys
+// e = 0..7 at unit offset 8grp + e, sacc[e/4][e%4]).  With `mask` (wave-
+// uniform: the tile's own unit of the query block) keys past the token drop
+// (block-relative key offset kofs + e > pos).  Returns P^T packed as the PV
+// operand.
+template <int t>
+__device__ __forceinline__ bf16x8 unit_softmax(WaveState &st, const f32x4 (&sacc)[2], bool mask, int kofs,
+                                               int pos, float scale_log2) {
+    float sv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sv[e] = sacc[e >> 2][e & 3];
+    if (mask) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sv[e] = kofs + e <= pos ? sv[e] : -INFINITY;
+    }
+    float mloc = sv[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) mloc = fmaxf(mloc, sv[e]);
+    mloc = row_max4(mloc);
+    // lazy reference: move it (and rescale) only on a large increase
+    const bool grow = mloc > st.m_ref[t] &&
+                      (st.m_ref[t] == -INFINITY || (mloc - st.m_ref[t]) * scale_log2 > kLazyLog2);
+    if (__ballot(grow)) {
+        const float m_new = grow ? mloc : st.m_ref[t];
+        const float alpha =
+            st.m_ref[t] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((st.m_ref[t] - m_new) * scale_log2);
+        st.l_run[t] *= alpha;
+        // The accumulators live in AGPRs; pinning the value to AGPRs on both
+        // sides of the multiply keeps the register allocator from moving the
+        // whole O^T state to VGPRs around this rarely taken path.
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+            f32x4 x = st.acc_o[t][dt];
+            asm volatile("" : "+a"(x));
+            x *= alpha;
+            asm volatile("" : "+a"(x));
+            st.acc_o[t][dt] = x;
+        }
+        st.m_ref[t] = m_new;
+    }
+    const float mb = st.m_ref[t] == -INFINITY ? 0.f : st.m_ref[t] * scale_log2;
+    float psum = 0.f;
+    bf16x8 pb;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float pv = __builtin_amdgcn_exp2f(sv[e] * scale_log2 - mb);
+        psum += pv;
+        pb[e] = (__bf16)pv;
+    }
+    st.l_run[t] += psum;
+    return pb;
+}
+
+// Scores and softmax of one unit for slot t, when the slot's token selected
+// the block (act bit t); P^T goes to pb[t].
+template <int t>
+__device__ __forceinline__ void token_unit(WaveState &st, const bf16x8 (&ka)[4][2], bf16x8 (&pb)[kTpw],
+                                           uint32_t act, bool mask, int kofs, int pos0, float scale_log2) {
+    if constexpr (t < kTpw) {
+        if (!((act >> t) & 1u)) return;
+        f32x4 s[2];
+        unit_scores<t>(st, ka, s);
+        pb[t] = unit_softmax<t>(st, s, mask, kofs, pos0 + kWaves * t, scale_log2);
+    }
+}
+
+// One ring unit for the wave's active tokens `act` (bit t = slot t of the
+// wave, wave-uniform): K fragments read once from LDS, scores and softmax
+// token by token, then V^T fragments read once and O^T += V^T P^T per token.
+// mask: the tile's own unit of the query block (keys past a token drop).
+__device__ __forceinline__ void ring_unit(WaveState &st, const uint8_t *Ku, uint32_t act, const int (&k_row_off)[2],
+                                          int v_off, int n, int grp, bool mask, int kofs, int pos0,
+                                          float scale_log2) {
+    bf16x8 pb[kTpw];
+    {
         bf16x8 ka[4][2];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
-                ka[ks][mt] = __builtin_bit_cast(
-                    bf16x8, *(const u32x4 *)(Ku + k_row_off[mt] + (((4 * ks + grp) ^ n) << 4)));
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            if (!act[t]) continue;
-            sacc[t][q][0] = f32x4{};
-            sacc[t][q][1] = f32x4{};
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-                for (int mt = 0; mt < 2; ++mt)
-                    sacc[t][q][mt] = mfma_16x16x32(ka[ks][mt], st.qb[t][ks], sacc[t][q][mt]);
-        }
+                ka[ks][mt] = __builtin_bit_cast(bf16x8,
+                                                *(const u32x4 *)(Ku + k_row_off[mt] + (((4 * ks + grp) ^ n) << 4)));
+        token_unit<0>(st, ka, pb, act, mask, kofs, pos0, scale_log2);
+        token_unit<1>(st, ka, pb, act, mask, kofs, pos0, scale_log2);
+        token_unit<2>(st, ka, pb, act, mask, kofs, pos0, scale_log2);
+        token_unit<3>(st, ka, pb, act, mask, kofs, pos0, scale_log2);
+        token_unit<4>(st, ka, pb, act, mask, kofs, pos0, scale_log2);
+        token_unit<5>(st, ka, pb, act, mask, kofs, pos0, scale_log2);
+        token_unit<6>(st, ka, pb, act, mask, kofs, pos0, scale_log2);
+        token_unit<7>(st, ka, pb, act, mask, kofs, pos0, scale_log2);
     }
+    const uint8_t *Vu = Ku + kKUnitBytes;
+    bf16x8 va[8];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) va[dt] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(Vu + 1024 * dt + v_off));
+#pragma unroll
+    for (int t = 0; t < kTpw; ++t) {
+        if (!((act >> t) & 1u)) continue;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) st.acc_o[t][dt] = mfma_16x16x32(va[dt], pb[t], st.acc_o[t][dt]);
+    }
+}
 
-    // online softmax over the block's keys; this lane holds keys
-    // keyb + 32q + e (e < 8) of head column n
-    bf16x8 pb[2][kUnitsPerBlock];
+// Exclusive prefix sum over the workgroup of one int per thread; the total
+// goes to *total.  s_w: kWaves ints of LDS.  Ends with a barrier.
+__device__ __forceinline__ int block_exclusive_scan(int v, int tid, int *s_w, int *total) {
+    const int lane = tid & 63, wave = tid >> 6;
+    int x = v;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        if (!act[t]) continue;
-        float sv[kUnitsPerBlock][8];
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) s_w[wave] = x;
+    __syncthreads();
+    int before = 0, tot = 0;
 #pragma unroll
-        for (int q = 0; q < kUnitsPerBlock; ++q)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) sv[q][e] = sacc[t][q][e >> 2][e & 3];
-        if (kDiag) {  // causal mask; also drops units q >= nq
-#pragma unroll
-            for (int q = 0; q < kUnitsPerBlock; ++q)
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    sv[q][e] = keyb + kAttnUnit * q + e <= my_p[t] ? sv[q][e] : -INFINITY;
+    for (int w = 0; w < kWaves; ++w) {
+        before += w < wave ? s_w[w] : 0;
+        tot += s_w[w];
+    }
+    *total = tot;
+    __syncthreads();
+    return before + x - v;
+}
+
+// Union of the selected blocks of a tile of ntok <= 28 consecutive tokens
+// (first token tok0, all in query block c of one document) for KV head g:
+// ublk[0..nu) ascending, umask[u] bit kBitsPerWave (i % kWaves) + i / kWaves
+// set when tile token i selected ublk[u] (token i belongs to wave
+// i % kWaves, slot i / kWaves).
+// Ids outside 0..c and -1 are dropped; repeats count once.  The 32-bit
+// masks are gathered in an LDS table indexed by block id (windows of
+// kTableIds ids), then compacted in ascending order.  Called by every
+// thread of the workgroup; returns nu to all of them.
+__device__ __forceinline__ int tile_union32(const int32_t *__restrict__ q2k, int T, int topk, int g, int tok0,
+                                            int ntok, int c, int tid, uint32_t *table, int *ublk,
+                                            uint32_t *umask, int *s_w) {
+    int nu = 0;
+    for (int b0 = 0; b0 <= c; b0 += kTableIds) {
+        const int W = min(kTableIds, c + 1 - b0);
+        for (int i = tid; i < W; i += kThreads) table[i] = 0u;
+        __syncthreads();
+        for (int e = tid; e < ntok * topk; e += kThreads) {  // consecutive entries: coalesced
+            const int tok = e / topk;
+            const int id = q2k[(size_t(g) * T + tok0) * topk + e];
+            if (id >= b0 && id < b0 + W)
+                atomicOr(&table[id - b0], 1u << (kBitsPerWave * (tok % kWaves) + tok / kWaves));
         }
-        float mloc = sv[0][0];
-#pragma unroll
-        for (int q = 0; q < kUnitsPerBlock; ++q)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) mloc = fmaxf(mloc, sv[q][e]);
-        mloc = row_max4(mloc);
-        // lazy reference: move it (and rescale) only on a large increase
-        const bool grow = mloc > st.m_ref[t] &&
-                          (st.m_ref[t] == -INFINITY || (mloc - st.m_ref[t]) * scale_log2 > kLazyLog2);
-        if (__ballot(grow)) {
-            const float m_new = grow ? mloc : st.m_ref[t];
-            const float alpha = st.m_ref[t] == -INFINITY
-                                    ? 0.f
-                                    : __builtin_amdgcn_exp2f((st.m_ref[t] - m_new) * scale_log2);
-            st.l_run[t] *= alpha;
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt) st.acc_o[t][dt] *= alpha;
-            st.m_ref[t] = m_new;
+        __syncthreads();
+        const int per = (W + kThreads - 1) / kThreads;  // thread tid: ids [tid*per, tid*per+per)
+        int cnt = 0;
+        for (int i = 0; i < per; ++i) {
+            const int idx = tid * per + i;
+            cnt += (idx < W && table[idx] != 0u) ? 1 : 0;
         }
-        const float mb = st.m_ref[t] == -INFINITY ? 0.f : st.m_ref[t] * scale_log2;
-        float psum = 0.f;
-#pragma unroll
-        for (int q = 0; q < kUnitsPerBlock; ++q)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float pv = __builtin_amdgcn_exp2f(sv[q][e] * scale_log2 - mb);
-                psum += pv;
-                pb[t][q][e] = (__bf16)pv;
+        int tot;
+        int pos = nu + block_exclusive_scan(cnt, tid, s_w, &tot);
+        for (int i = 0; i < per; ++i) {
+            const int idx = tid * per + i;
+            const uint32_t m = idx < W ? table[idx] : 0u;
+            if (m != 0u) {
+                ublk[pos] = b0 + idx;
+                umask[pos] = m;
+                ++pos;
             }
-        st.l_run[t] += psum;
-    }
-
-    // O^T += V^T . P^T, unit by unit
-#pragma unroll
-    for (int q = 0; q < kUnitsPerBlock; ++q) {
-        if (kDiag && q >= nq) break;
-        const uint8_t *Vu = smem + ((ustart + q) % kRing) * kUnitBytes + kKUnitBytes;
-        bf16x8 va[8];
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
-            va[dt] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(Vu + 1024 * dt + v_off));
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            if (!act[t]) continue;
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt)
-                st.acc_o[t][dt] = mfma_16x16x32(va[dt], pb[t][q], st.acc_o[t][dt]);
         }
+        nu += tot;
+        __syncthreads();
     }
+    return nu;
 }
 
-}  // namespace
-
-namespace {
-// Unit q of a block b < c for token t of a wave, read straight from memory
-// (the per-unit K rows and V^T rows are contiguous in the MFMA operand
-// layouts), with the lazy online softmax.  Used for blocks a single token of
-// the tile selected, which would otherwise hold the whole workgroup at a
-// barrier for one wave's work.
-template <int t>
-__device__ __forceinline__ void attend_unit_global(WaveState &st, const uint16_t *__restrict__ ku,
-                                                   const uint16_t *__restrict__ vt, int g, int uoff, int b,
-                                                   int q, int n, int grp, float scale_log2) {
-    {
-        f32x4 sacc[2] = {f32x4{}, f32x4{}};
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-            const uint16_t *src = ku + ((size_t(uoff + kUnitsPerBlock * b + q) * kKvHeads + g) * kAttnUnit +
-                                        8 * (n >> 2) + 4 * mt + (n & 3)) * kDim;
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-                sacc[mt] = mfma_16x16x32(__builtin_bit_cast(bf16x8, *(const u32x4 *)(src + 8 * (4 * ks + grp))),
-                                         st.qb[t][ks], sacc[mt]);
-        }
-        const uint16_t *vsrc = vt + ((size_t(uoff + kUnitsPerBlock * b + q) * kKvHeads + g) * kDim + n) * kAttnUnit + 8 * grp;
-        bf16x8 va[8];
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) va[dt] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(vsrc + 16 * dt * kAttnUnit));
-        float mloc = -INFINITY;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) mloc = fmaxf(mloc, sacc[e >> 2][e & 3]);
-        mloc = row_max4(mloc);
-        const bool grow = mloc > st.m_ref[t] &&
-                          (st.m_ref[t] == -INFINITY || (mloc - st.m_ref[t]) * scale_log2 > kLazyLog2);
-        if (__ballot(grow)) {
-            const float m_new = grow ? mloc : st.m_ref[t];
-            const float alpha = st.m_ref[t] == -INFINITY
-                                    ? 0.f
-                                    : __builtin_amdgcn_exp2f((st.m_ref[t] - m_new) * scale_log2);
-            st.l_run[t] *= alpha;
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt) st.acc_o[t][dt] *= alpha;
-            st.m_ref[t] = m_new;
-        }
-        const float mb = st.m_ref[t] == -INFINITY ? 0.f : st.m_ref[t] * scale_log2;
-        float psum = 0.f;
-        bf16x8 pb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float pv = __builtin_amdgcn_exp2f(sacc[e >> 2][e & 3] * scale_log2 - mb);
-            psum += pv;
-            pb[e] = (__bf16)pv;
-        }
-        st.l_run[t] += psum;
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) st.acc_o[t][dt] = mfma_16x16x32(va[dt], pb, st.acc_o[t][dt]);
-    }
-}
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -295,51 +331,62 @@ __global__ __launch_bounds__(kThreads) void attend_prefill_kernel(
     const int32_t *__restrict__ tile_off, const int32_t *__restrict__ unit_off, int ndocs, int T,
     float scale_log2, uint16_t *__restrict__ out, float *__restrict__ lse) {
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
-    constexpr int kEntries = kTok * kMaxTopk;  // 256 (token, slot) pairs
-    static_assert(kThreads >= kEntries, "one thread per (token, slot) pair");
-    __shared__ int s_id[kEntries];
-    __shared__ int s_first[kEntries];
-    __shared__ int s_mask[kEntries];
-    __shared__ int s_ublk[kEntries];
-    __shared__ int s_umask[kEntries];
-    __shared__ int s_sblk[kEntries];   // the ring's blocks: shared ones and the query's own
-    __shared__ int s_smask[kEntries];
-    __shared__ int s_nu, s_ns;
+    __shared__ int s_sblk[kMaxUnion];             // the ring's blocks (the tile's union), ascending
+    __shared__ uint32_t s_smask[kMaxUnion];       // their token masks
+    __shared__ uint32_t s_unit[kMaxUnits];        // per ring unit: state bits | waves still to read it
+    __shared__ int s_wlist[kWaves][kTpw * kMaxTopk];  // per wave: the ring blocks it needs, ascending
+    __shared__ int s_w[kWaves];
 
     // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs; XCD x
-    // serves KV head x/2 and alternate groups of 8 tiles (one 128-token query
+    // serves KV head x/2 and alternate groups of 5 tiles (one 128-token query
     // block) of that head, longest first, so the tiles sharing a query block
     // share one L2.
     const int bid = blockIdx.x;
     const int xcd = bid & 7, xslot = bid >> 3;
     const int g = xcd >> 1;
-    const int tile = 16 * (xslot >> 3) + 8 * (xcd & 1) + (xslot & 7);
+    const int tile = 2 * kTilesPerBlock * (xslot / kTilesPerBlock) + kTilesPerBlock * (xcd & 1) +
+                     xslot % kTilesPerBlock;
     if (tile >= tile_off[ndocs]) return;
     const int d = prefix_doc(tile_off, ndocs, tile);
     const int nt_doc = tile_off[d + 1] - tile_off[d];
     const int local_tile = nt_doc - 1 - (tile - tile_off[d]);
     const DocSpan doc = docs[d];
     const int uoff = unit_off[d];
-    const int p0 = local_tile * kTok;
-    const int c = p0 / kBlock;
-    const int ntok = min(kTok, doc.len - p0);
-    const int p_last = p0 + ntok - 1;
+    // tile i of query block c: positions [c*128 + Lb*i/nt, c*128 + Lb*(i+1)/nt)
+    // of the block's Lb tokens cut into nt near-equal tiles
+    const int nb_full = doc.len / kBlock;
+    int c, ti, nt, Lb;
+    if (local_tile < kTilesPerBlock * nb_full) {
+        c = local_tile / kTilesPerBlock;
+        ti = local_tile % kTilesPerBlock;
+        Lb = kBlock;
+        nt = kTilesPerBlock;
+    } else {
+        c = nb_full;
+        ti = local_tile - kTilesPerBlock * nb_full;
+        Lb = doc.len - kBlock * c;
+        nt = (Lb + kTok - 1) / kTok;
+    }
+    const int r0 = Lb * ti / nt;                   // block-relative first position
+    const int p0 = c * kBlock + r0;
+    const int ntok = Lb * (ti + 1) / nt - r0;      // 1..28
+    const int q_lo = r0 / kAttnUnit;               // own-block units q >= q_lo take the causal mask
+    const int q_hi = (r0 + ntok - 1) / kAttnUnit;  // the own block stops at unit q_hi
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
     const int n = lane & 15, grp = lane >> 4;
+    // slot t of this wave is tile token kWaves t + wave, at position
+    // p0 + kWaves t + wave
+    const int pos0 = p0 + wave;
 
     // ---- this wave's tokens and their query operands (column n = head n)
     const int head = g * kGroup + n;
-    int my_p[2];
-    bool tok_ok[2];
     WaveState st;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        my_p[t] = p0 + 2 * wave + t;
-        tok_ok[t] = 2 * wave + t < ntok;
-        const uint16_t *src =
-            q + (size_t(doc.start + (tok_ok[t] ? my_p[t] : p0)) * kHeads + head) * kDim;
+    for (int t = 0; t < kTpw; ++t) {
+        const int p = kWaves * t + wave < ntok ? pos0 + kWaves * t : p0;
+        const uint16_t *src = q + (size_t(doc.start + p) * kHeads + head) * kDim;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
             st.qb[t][ks] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(src + 32 * ks + 8 * grp));
@@ -349,87 +396,42 @@ __global__ __launch_bounds__(kThreads) void attend_prefill_kernel(
         st.l_run[t] = 0.f;
     }
 
-    // ---- union of the tile's selected blocks (ascending, with token masks)
-    const int nu = tile_union(q2k, T, topk, g, doc.start + p0, ntok, c, tid, s_id, s_first, s_mask,
-                              s_ublk, s_umask, &s_nu);
-    // Split the union: blocks at least kSharedMin tokens selected, and the
-    // query's own block, go through the LDS ring (ascending); a block one
-    // token selected is read by that token's wave straight from memory.
-    if (wave == 0) {
-        int base = 0;
-        for (int u0 = 0; u0 < nu; u0 += 64) {
-            const int u = u0 + lane;
-            const bool sh = u < nu && (__popc(s_umask[u]) >= kSharedMin || s_ublk[u] == c);
-            const uint64_t m = __ballot(sh);
-            if (sh) {
-                const int pos = base + __popcll(m & ((1ull << lane) - 1ull));
-                s_sblk[pos] = s_ublk[u];
-                s_smask[pos] = s_umask[u];
-            }
-            base += __popcll(m);
-        }
-        if (lane == 0) s_ns = base;
+    // ---- union of the tile's selected blocks (ascending, with token masks);
+    // the table and the list live in the ring's LDS until the walk starts
+    int *ublk = (int *)(smem + kRing * kUnitBytes - kUnionListBytes);
+    uint32_t *umask = (uint32_t *)(ublk + kMaxUnion);
+    const int nu = tile_union32(q2k, T, topk, g, doc.start + p0, ntok, c, tid, (uint32_t *)smem, ublk, umask, s_w);
+    // The ring holds every union block, ascending; the query's own block c is
+    // last when present and stops at the unit of the tile's last token.
+    for (int u = tid; u < nu; u += kThreads) {
+        s_sblk[u] = ublk[u];
+        s_smask[u] = umask[u];
     }
-    __syncthreads();
-    const int ns = s_ns;
-    // ---- blocks a single token of the tile selected (never the query's own
-    // block): that token's wave alone, straight from memory, one unit at a
-    // time in the ring iterations where the wave has no token in the ring's
-    // block, and the rest after the ring (the online softmax takes blocks in
-    // any order).  The wave lists them as 2b + t, at most kMaxTopk per token.
-    __shared__ int s_dlist[kTok / 2][2 * kMaxTopk];
-    int nd = 0;
+    const int ns = nu;
+    const int last_units = (ns > 0 && ublk[ns - 1] == c) ? q_hi + 1 : kUnitsPerBlock;
+    // unit counts: the waves whose tokens selected the unit's block
+    for (int u = tid; u < kUnitsPerBlock * ns; u += kThreads) {
+        const int bi = u / kUnitsPerBlock;
+        const uint32_t m = umask[bi];
+        int nw = 0;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        if (!tok_ok[t]) continue;
-        const int bit = 1 << (2 * wave + t);
+        for (int w = 0; w < kWaves; ++w) nw += ((m >> (kBitsPerWave * w)) & ((1u << kBitsPerWave) - 1u)) ? 1 : 0;
+        const bool exists = bi < ns - 1 || u % kUnitsPerBlock < last_units;
+        s_unit[u] = exists ? uint32_t(nw) : 0u;
+    }
+    // each wave lists the ring blocks its tokens selected, ascending
+    int nwb = 0;
+    {
+        const uint32_t wbits = ((1u << kBitsPerWave) - 1u) << (kBitsPerWave * wave);
         for (int u0 = 0; u0 < nu; u0 += 64) {
             const int u = min(u0 + lane, nu - 1);
-            const int um = s_umask[u], ub = s_ublk[u];
-            const bool dir = u0 + lane < nu && (um & bit) && ub != c && __popc(um) < kSharedMin;
-            const uint64_t m = __ballot(dir);
-            if (dir) s_dlist[wave][nd + __popcll(m & ((1ull << lane) - 1ull))] = 2 * ub + t;
-            nd += __popcll(m);
+            const bool mine = u0 + lane < nu && (umask[u] & wbits);
+            const uint64_t m = __ballot(mine);
+            if (mine) s_wlist[wave][nwb + __popcll(m & ((1ull << lane) - 1ull))] = u;
+            nwb += __popcll(m);
         }
     }
-    const int nd_units = kUnitsPerBlock * nd;
-    int di = 0;
-
-    // 32-key units: 4 per ring block, except that the query's own block c
-    // (always last when present) stops at the unit holding p_last.
-    const int last_units =
-        (ns > 0 && s_sblk[ns - 1] == c) ? (p_last - c * kBlock) / kAttnUnit + 1 : kUnitsPerBlock;
-    const int nunits = ns > 0 ? kUnitsPerBlock * (ns - 1) + last_units : 0;
-
-    // ---- HBM -> LDS unit copies: 16 one-KiB copies per unit.  Copy i < 8
-    // fills K rows 4i..4i+3 (lane l: row 4i + l/16, slot position l%16, i.e.
-    // chunk (l%16) ^ kswz(row)); copy i >= 8 fills V^T rows 16(i-8)..+15
-    // (lane l: row 16(i-8) + l/4, chunk (l%4) ^ vswz(row)).  Both come from
-    // the per-unit copies, whose rows past the document end are zero.
-    auto issue_copy = [&](int vu, int ub, int i) {
-        const int qq = vu & 3;
-        uint8_t *slot = smem + (vu % kRing) * kUnitBytes;
-        if (i < 8) {
-            const int r = 4 * i + (lane >> 4);
-            const int ch = (lane & 15) ^ kswz(r);
-            const size_t unit = size_t(uoff + ub * kUnitsPerBlock + qq);
-            const uint16_t *src = ku + ((unit * kKvHeads + g) * kAttnUnit + r) * kDim + 8 * ch;
-            copy_to_lds(src, slot + i * 1024);
-        } else {
-            const int jv = i - 8;
-            const int dd = 16 * jv + (lane >> 2);
-            const int ch = (lane & 3) ^ vswz(dd);
-            const size_t unit = size_t(uoff + ub * kUnitsPerBlock + qq);
-            const uint16_t *src = vt + ((unit * kKvHeads + g) * kDim + dd) * kAttnUnit + 8 * ch;
-            copy_to_lds(src, slot + kKUnitBytes + jv * 1024);
-        }
-    };
-    // Wave w issues copies 2w and 2w+1 of every unit.
-    auto issue_unit = [&](int vu) {
-        const int ub = __builtin_amdgcn_readfirstlane(s_sblk[vu >> 2]);
-        issue_copy(vu, ub, 2 * wave);
-        issue_copy(vu, ub, 2 * wave + 1);
-    };
+    __syncthreads();  // lists and counts are set; the union's LDS is free for the ring
 
     // Lane-constant LDS byte offsets of the operand reads.
     // K: M-tile mt row n is key 8(n/4) + 4mt + n%4, whose kswz is n.
@@ -438,69 +440,125 @@ __global__ __launch_bounds__(kThreads) void attend_prefill_kernel(
     for (int mt = 0; mt < 2; ++mt) k_row_off[mt] = (8 * (n >> 2) + 4 * mt + (n & 3)) * (kDim * 2);
     // V^T: d-tile dt reads row 16dt + n, chunk grp.
     const int v_off = 64 * n + 16 * (grp ^ vswz(n));
+    const int tok_ok = (ntok - wave + kWaves - 1) / kWaves;  // slots t < tok_ok of this wave hold a token
+    const uint32_t ok_mask = (1u << tok_ok) - 1u;
 
-    // Block loop: union block u occupies units 4u..4u+nq-1 (nq < 4 only for
-    // the query's own block).  At the barrier of block u its units have
-    // landed (each wave waited for its own copies of them) and every wave is
-    // done with block u-1; the ring then takes every unit up to 4u + 8, so
-    // five units stream in during the compute.
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): query operands are in (no copy issued yet)
-    int issued = min(nunits, kRing);
-    for (int vu = 0; vu < issued; ++vu) issue_unit(vu);
-    for (int u = 0; u < ns || di < nd_units; ++u) {
-        if (u >= ns) {  // past the ring (no more barriers): the wave's remaining units
-            const int e = __builtin_amdgcn_readfirstlane(s_dlist[wave][di >> 2]);
-            if (e & 1) attend_unit_global<1>(st, ku, vt, g, uoff, e >> 1, di & 3, n, grp, scale_log2);
-            else attend_unit_global<0>(st, ku, vt, g, uoff, e >> 1, di & 3, n, grp, scale_log2);
-            ++di;
-            continue;
+    // ---- HBM -> LDS copy of ring unit u (16 one-KiB copies, all issued by
+    // the wave that claimed it) into slot u % kRing, copy i to slot byte
+    // 1024 i.  Copy i < 8 fills K rows 4i..4i+3 (lane l: row 4i + l/16,
+    // slot position l%16, i.e. chunk (l%16) ^ kswz(row)); copy i >= 8 fills
+    // V^T rows 16(i-8)..+15 (lane l: row 16(i-8) + l/4, chunk
+    // (l%4) ^ vswz(row)).  Both come from the per-unit copies (8 KiB per
+    // unit and head in either), whose rows past the document end are zero.
+    auto issue_unit = [&](int u) {
+        const int ub = __builtin_amdgcn_readfirstlane(s_sblk[u / kUnitsPerBlock]);
+        const size_t unit = size_t(uoff + ub * kUnitsPerBlock + u % kUnitsPerBlock) * kKvHeads + g;
+        const uint16_t *ksrc = ku + unit * (kAttnUnit * kDim);
+        const uint16_t *vsrc = vt + unit * (kAttnUnit * kDim);
+        uint8_t *slot = smem + (u % kRing) * kUnitBytes;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = 4 * i + (lane >> 4);
+            copy_to_lds(ksrc + r * kDim + 8 * ((lane & 15) ^ kswz(r)), slot + i * 1024);
         }
-        const int ustart = kUnitsPerBlock * u;
-        const int nq = u == ns - 1 ? nunits - ustart : kUnitsPerBlock;
-        wait_copies(2 * (issued - (ustart + nq)));  // copies complete in issue order
-        barrier_keep_prefetch();
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int dd = 16 * i + (lane >> 2);
+            copy_to_lds(vsrc + dd * kAttnUnit + 8 * ((lane & 3) ^ vswz(dd)), slot + kKUnitBytes + i * 1024);
+        }
+    };
+    // Unit state, read by every lane (LDS broadcast); changed by lane 0.
+    auto unit_word = [&](int u) {
+        return __builtin_amdgcn_readfirstlane(
+            __hip_atomic_load(&s_unit[u], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP));
+    };
+    // Slot u % kRing is free for unit u once every wave needing unit u - kRing is done with it.
+    auto fillable = [&](int u) { return u < kRing || (unit_word(u - kRing) & 0xFFu) == 0u; };
+    auto try_claim = [&](int u) {
+        uint32_t old = kClaimed;
+        if (lane == 0) old = __hip_atomic_fetch_or(&s_unit[u], kClaimed, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+        return (__builtin_amdgcn_readfirstlane(old) & kClaimed) == 0u;
+    };
+    auto publish = [&](int u) {  // the copies of u have landed (this wave waited for them)
+        if (lane == 0) __hip_atomic_fetch_or(&s_unit[u], kReady, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    };
+    auto release = [&](int u) {  // this wave is done reading unit u
+        if (lane == 0) __hip_atomic_fetch_sub(&s_unit[u], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    };
+    // Wait until unit u has landed; claim and copy it when nobody has and its
+    // slot is free.  Every wait is bounded (kSpinLimit polls).
+    auto acquire = [&](int u) {
+        for (int spin = 0; spin < kSpinLimit; ++spin) {
+            const uint32_t wd = unit_word(u);
+            if (wd & kReady) return;
+            if (!(wd & kClaimed) && fillable(u) && try_claim(u)) {
+                issue_unit(u);
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                publish(u);
+                return;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+    };
 
-        const int b = __builtin_amdgcn_readfirstlane(s_sblk[u]);
-        const int umask = __builtin_amdgcn_readfirstlane(s_smask[u]);
-        const bool act[2] = {tok_ok[0] && ((umask >> (2 * wave)) & 1),
-                             tok_ok[1] && ((umask >> (2 * wave + 1)) & 1)};
-        // refill the slots of block u-1 (every wave is past it)
-        for (const int ifront = min(nunits, ustart + kRing); issued < ifront; ++issued)
-            issue_unit(issued);
-        const int keyb = b * kBlock + 8 * grp;
-        if (b == c)
-            attend_block<true, true, true>(st, smem, ustart, nq, k_row_off, v_off, n, grp, keyb, act, my_p,
-                                           scale_log2);
-        else if (act[0] && act[1])
-            attend_block<true, true, false>(st, smem, ustart, kUnitsPerBlock, k_row_off, v_off, n, grp, keyb,
-                                            act, my_p, scale_log2);
-        else if (act[0])
-            attend_block<true, false, false>(st, smem, ustart, kUnitsPerBlock, k_row_off, v_off, n, grp,
-                                             keyb, act, my_p, scale_log2);
-        else if (act[1])
-            attend_block<false, true, false>(st, smem, ustart, kUnitsPerBlock, k_row_off, v_off, n, grp,
-                                             keyb, act, my_p, scale_log2);
-        else if (di < nd_units) {  // no token in this block: one unit of the wave's own blocks
-            const int e = __builtin_amdgcn_readfirstlane(s_dlist[wave][di >> 2]);
-            if (e & 1) attend_unit_global<1>(st, ku, vt, g, uoff, e >> 1, di & 3, n, grp, scale_log2);
-            else attend_unit_global<0>(st, ku, vt, g, uoff, e >> 1, di & 3, n, grp, scale_log2);
-            ++di;
+    // ---- the wave's walk over its needed units, in ring order.  Before
+    // computing a unit it claims the next one it needs, when free, and
+    // publishes it after the compute (its copies land meanwhile).
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): query operands are in (no copy issued yet)
+    for (int k = 0; k < nwb; ++k) {
+        // keep every O^T accumulator in AGPRs across the loop (the register
+        // allocator would otherwise carry some of them in VGPRs, which the
+        // query operands and the working set need)
+#pragma unroll
+        for (int t = 0; t < kTpw; ++t)
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) asm volatile("" : "+a"(st.acc_o[t][dt]));
+        const int bi = __builtin_amdgcn_readfirstlane(s_wlist[wave][k]);
+        const int b = __builtin_amdgcn_readfirstlane(s_sblk[bi]);
+        const uint32_t act = (__builtin_amdgcn_readfirstlane(s_smask[bi]) >> (kBitsPerWave * wave)) & ok_mask;
+        const int nq = bi == ns - 1 ? last_units : kUnitsPerBlock;
+        const bool own = b == c;
+        const int nxt_bi = k + 1 < nwb ? __builtin_amdgcn_readfirstlane(s_wlist[wave][k + 1]) : -1;
+#pragma unroll 1
+        for (int qq = 0; qq < nq; ++qq) {
+            const int u = kUnitsPerBlock * bi + qq;
+            acquire(u);
+            const int v = qq + 1 < nq ? u + 1 : (nxt_bi >= 0 ? kUnitsPerBlock * nxt_bi : -1);
+            bool ahead = false;
+            if (v >= 0) {
+                const uint32_t wd = unit_word(v);
+                if (!(wd & (kClaimed | kReady)) && fillable(v) && try_claim(v)) {
+                    issue_unit(v);
+                    ahead = true;
+                }
+            }
+            const uint8_t *Ku = smem + (u % kRing) * kUnitBytes;
+            // the tile's own units of the query block: keys past each token drop
+            if (act)
+                ring_unit(st, Ku, act, k_row_off, v_off, n, grp, own && qq >= q_lo, kAttnUnit * qq + 8 * grp,
+                          pos0 - c * kBlock, scale_log2);
+            release(u);
+            if (ahead) {
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                publish(v);
+            }
         }
     }
 
     // ---- epilogue: normalise and store bf16 (lane holds d = 16dt + 4grp + i)
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < kTpw; ++t) {
         const float l_tot = row_sum4(st.l_run[t]);
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        if (lse && tok_ok[t] && grp == 0) {
+        const bool ok = t < tok_ok;
+        const size_t row = size_t(doc.start + pos0 + kWaves * t) * kHeads + head;
+        if (lse && ok && grp == 0) {
             // sum_j e^(scale s_j) = 2^(m_ref * scale_log2) * l_tot
             const float mb = st.m_ref[t] == -INFINITY ? 0.f : st.m_ref[t] * scale_log2;
-            lse[size_t(doc.start + my_p[t]) * kHeads + head] =
-                l_tot > 0.f ? (mb + __log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
+            lse[row] = l_tot > 0.f ? (mb + __log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
         }
-        if (tok_ok[t]) {
-            uint16_t *dst = out + (size_t(doc.start + my_p[t]) * kHeads + head) * kDim;
+        if (ok) {
+            uint16_t *dst = out + row * kDim;
 #pragma unroll
             for (int dt = 0; dt < 8; ++dt) {
                 bf16x4 o;
@@ -531,8 +589,10 @@ hipError_t launch_attend_prefill(const uint16_t *q, const uint16_t *vt,
                                  const int32_t *q2k, int topk, const DocSpan *docs,
                                  const int32_t *tile_off, const int32_t *unit_off, int ndocs, int T,
                                  float scale, uint16_t *out, float *lse, hipStream_t stream) {
-    const int max_tiles = ceil_div(T, kTok) + ndocs;  // document-aligned tiles (upper bound)
-    const int grid = 8 * 8 * ceil_div(max_tiles, 16);  // 8 XCDs x slots
+    // document-aligned tiles (upper bound): 5 per 128-token query block
+    const int max_tiles = kTilesPerBlock * (ceil_div(T, kBlock) + ndocs);
+    // 8 XCDs x slots; an XCD pair serves 2 groups of 5 tiles per 5 slots
+    const int grid = 8 * kTilesPerBlock * ceil_div(max_tiles, 2 * kTilesPerBlock);
     const size_t lds = size_t(kRing) * kUnitBytes;
     hipLaunchKernelGGL(attend_prefill_kernel, dim3(grid), dim3(kThreads), lds, stream, q,
                        vt + unit_elems(T, ndocs), vt, q2k, topk, docs, tile_off, unit_off, ndocs, T,

@@ -279,7 +279,7 @@ static msa_status prefill_impl(const uint16_t *q, const uint16_t *k, const uint1
     uint16_t *vt = (uint16_t *)(base + ws.vt);
     TimingScope tm;
     tm.mark(s, "doc_setup");
-    hipError_t e = launch_doc_setup(cu_seqlens, num_docs, total_tokens, max_seqlen, kAttnTile,
+    hipError_t e = launch_doc_setup(cu_seqlens, num_docs, total_tokens, max_seqlen, kFwdTile,
                                     kAttnUnit, docs, off, uoff, s);
     if (e != hipSuccess) return hip_fail(e, "doc_setup");
     tm.mark(s, "kv_units");

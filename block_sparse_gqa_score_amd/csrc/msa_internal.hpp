@@ -10,7 +10,10 @@
 namespace msa {
 
 constexpr int kScoreTile = 64;   // query tokens per block-scorer workgroup
-constexpr int kAttnTile = 16;    // query tokens per prefill-attention workgroup
+constexpr int kAttnTile = 16;    // query tokens per backward dQ workgroup
+constexpr int kFwdTile = 24;     // most query tokens per prefill-attention (forward) workgroup:
+                                 // a 128-token query block is cut into 6 tiles of 21-22
+constexpr int kFwdWaves = 8;     // waves per prefill-attention workgroup (two per SIMD)
 constexpr int kAttnUnit = 32;    // keys per prefill-attention pipeline unit
 
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }

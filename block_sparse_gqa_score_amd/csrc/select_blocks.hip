@@ -30,6 +30,15 @@ namespace msa {
 // ---------------------------------------------------------------------------
 // G0: document spans and tile offsets
 // ---------------------------------------------------------------------------
+// Tiles of a document of len tokens when every 128-token query block is cut
+// into ceil(128/tile) tiles of near-equal size (a partial last block into
+// ceil(rest/tile)); equal to ceil(len/tile) whenever tile divides 128.
+__device__ __forceinline__ int tiles_in_doc(int len, int tile) {
+    const int per_block = (kBlock + tile - 1) / tile;
+    const int rest = len % kBlock;
+    return (len / kBlock) * per_block + (rest + tile - 1) / tile;
+}
+
 __global__ __launch_bounds__(1024) void doc_setup_kernel(const int32_t *__restrict__ cu, int ndocs,
                                                          int T, int max_seqlen, int tile_a,
                                                          int tile_b, DocSpan *__restrict__ docs,
@@ -53,8 +62,8 @@ __global__ __launch_bounds__(1024) void doc_setup_kernel(const int32_t *__restri
             int e = min(max(cu[d + 1], s), T);
             int len = min(e - s, max_seqlen);
             docs[d] = DocSpan{s, len};
-            na = (len + tile_a - 1) / tile_a;
-            nb = tile_b > 0 ? (len + tile_b - 1) / tile_b : 0;
+            na = tiles_in_doc(len, tile_a);
+            nb = tile_b > 0 ? tiles_in_doc(len, tile_b) : 0;
         }
         // inclusive wave scans
 #pragma unroll
