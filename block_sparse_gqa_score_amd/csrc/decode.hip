@@ -525,16 +525,18 @@ __global__ __launch_bounds__(256) void decode_attend_stream_kernel(
     select_row<kCpl>(S + (size_t(r) * kIdxHeads + g) * nb_max, nb_max, c, topk, init, local, lane, s_sel[wave]);
     __builtin_amdgcn_wave_barrier();
     if (q2k_out && sg == 0 && wave == 0 && lane < topk) q2k_out[(size_t(g) * B + r) * topk + lane] = s_sel[0][lane];
-    // the workgroup's slots (wave-uniform): block id, or -1 when unselected,
-    // and the block's physical page (a negative page id marks an absent
-    // block: its copies read page 0, in bounds, and all its keys are masked)
+    // the workgroup's slots (wave-uniform): block id, or -1 when unselected
+    // or absent (a negative page id: nothing of it is read), and the block's
+    // physical page
     int bsel[kStreamSlots], bpage[kStreamSlots];
 #pragma unroll
     for (int j = 0; j < kStreamSlots; ++j) {
         const int s = sg * spw + j;
         const int b = (j < spw && s < topk) ? __builtin_amdgcn_readfirstlane(s_sel[wave][s]) : -1;
-        bsel[j] = (b >= 0 && b <= c) ? b : -1;
-        bpage[j] = bsel[j] >= 0 ? pt[size_t(r) * max_pages + bsel[j]] : 0;
+        const int bb = (b >= 0 && b <= c) ? b : -1;
+        const int page = bb >= 0 ? __builtin_amdgcn_readfirstlane(pt[size_t(r) * max_pages + bb]) : -1;
+        bsel[j] = page >= 0 ? bb : -1;
+        bpage[j] = page;
     }
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): q is in before any copy is issued
     // copies of slot j into stage st: K rows key0..key0+31 (8 one-KiB copies)
@@ -580,7 +582,7 @@ __global__ __launch_bounds__(256) void decode_attend_stream_kernel(
         }
         const uint8_t *kb = ring + (j & 1) * SL::kStage;
         const uint8_t *vt = kFp8Kv ? ring + SL::kVbf : kb + SL::kHalf;
-        const int kmax = bpage[j] < 0 ? -1 : L - 1 - bsel[j] * kBlock;
+        const int kmax = L - 1 - bsel[j] * kBlock;
         if constexpr (kFp8Kv) {
             // widen this wave's 32 V rows into the bf16 buffer: lane -> row
             // lane/2, byte chunks 4(lane%2)..+3 (16 E4M3 values each)

@@ -50,14 +50,23 @@ def test_decode_empty_requests_read_nothing(idt):
     assert bool((q2k[:, pad] == -1).all())
 
 
-def test_decode_absent_page_adds_no_keys():
+@pytest.mark.parametrize("nan_page0", [False, True])
+def test_decode_absent_page_adds_no_keys(nan_page0):
     """A negative page id inside a request's context: nothing of that page is
     read; the block scores -inf, so it is never chosen over a real block, and
     when forced (here the local block of a 1-page request and the init block)
-    it adds no key.  The other requests are unaffected."""
-    print("[absent page]", flush=True)
+    it adds no key.  The other requests are unaffected.  With nan_page0 the
+    caches gain a physical page 0 that no request owns, all NaN: an absent
+    block must not read it (a zero weight times NaN would still be NaN)."""
+    print(f"[absent page] nan_page0={nan_page0}", flush=True)
     lens = [1000, 3000, 100, 9000]
     d = W.make_decode(lens, 502, topk=6, init_blocks=1, local_blocks=1)
+    if nan_page0:
+        nan_bf16 = np.uint16(0x7FC0)
+        for name in ("k_cache", "v_cache", "ik_cache"):
+            a = getattr(d, name)
+            setattr(d, name, np.concatenate([np.full((128,) + a.shape[1:], nan_bf16, a.dtype), a]))
+        d.page_table = np.where(d.page_table >= 0, d.page_table + 1, d.page_table).astype(np.int32)
     out_ref, q2k_ref = _decode(d, d.context_lens, d.page_table)
     pt = d.page_table.copy()
     pt[0, 3] = -1          # a free (non-forced) block of request 0: never selected now
