@@ -15,15 +15,16 @@
 //   block_scores_kernel - S^T = K . IQ^T on MFMA (bf16 32x32x16 or E4M3
 //                         32x32x64 with unit scales), fused causal mask and
 //                         per-block row max; one workgroup = 64 query tokens
-//                         x 4 index heads of one document, looping over key
-//                         blocks 0..c, each prefetched two blocks ahead into
-//                         registers and staged through double-buffered LDS.
+//                         x 4 index heads of one document, two per CU,
+//                         looping over key blocks 0..c, each copied from
+//                         global memory into LDS (swizzled, double-buffered)
+//                         while the block before it is computed.
 //   topk_prefill_kernel - one lane per (head, token) row: top-R insertion
 //                         over 32-bit order keys of the scores, then an
 //                         ascending emit pass that takes every candidate
 //                         above the R-th key and the first (lowest-id)
 //                         candidates equal to it, up to the quota.
-#include "msa_internal.hpp"
+#include "attend_common.hpp"
 
 namespace msa {
 
@@ -109,22 +110,37 @@ __device__ __forceinline__ int tile_doc(const int32_t *off, int ndocs, int t) {
 // ---------------------------------------------------------------------------
 template <bool kFp8>
 struct ScoreLayout {
-    static constexpr int kRowBytes = kFp8 ? 128 : 256;         // one index row
-    static constexpr int kPitch = kRowBytes + 16;              // LDS row pitch (bank spread)
-    static constexpr int kChunksPerRow = kRowBytes / 16;
-    static constexpr int kChunksPerThread = kBlock * kChunksPerRow / 256;
-    static constexpr int kBufBytes = kBlock * kPitch;
+    static constexpr int kRowBytes = kFp8 ? 128 : 256;           // one index row
+    static constexpr int kChunks = kRowBytes / 16;               // 16-byte chunks per row
+    static constexpr int kRowsPerCopy = 1024 / kRowBytes;        // rows per one-KiB copy
+    static constexpr int kCopiesPerWave = kBlock * kRowBytes / 1024 / 4;
+    static constexpr int kBufBytes = kBlock * kRowBytes;
 };
 
+// LDS position of 16-byte chunk c of key row r: c ^ sswz(r).  The 16 rows a
+// quarter-wave reads at one chunk then land on 16 distinct bank groups (bf16:
+// 256-byte rows; E4M3: 128-byte rows, two rows per bank cycle).
 template <bool kFp8>
-__global__ __launch_bounds__(256) void block_scores_kernel(
-    const uint8_t *__restrict__ iq, const uint8_t *__restrict__ ik, const DocSpan *__restrict__ docs,
-    const int32_t *__restrict__ tile_off, int ndocs, int T, int nb_max, float *__restrict__ S) {
-    using L = ScoreLayout<kFp8>;
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+__device__ __forceinline__ int sswz(int r) {
+    return kFp8 ? ((r >> 1) & 7) : (r & 15);
+}
 
-    const int tile = blockIdx.x;
-    if (tile >= tile_off[ndocs]) return;
+template <bool kFp8>
+__global__ __launch_bounds__(256, 2) void block_scores_kernel(
+    const uint8_t *__restrict__ iq, const uint8_t *__restrict__ ik, const DocSpan *__restrict__ docs,
+    const int32_t *__restrict__ tile_off, int ndocs, int T, int nb_max, int ncu, float *__restrict__ S) {
+    using L = ScoreLayout<kFp8>;
+    extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];  // two key blocks
+
+    // Two workgroups share a CU, and the first 2*ncu start at once, the
+    // second ncu on the CUs of the first.  Tiles come longest first, so
+    // workgroup ncu + k takes tile 2*ncu - 1 - k: the pair on a CU then holds
+    // about the same total of key blocks.  Later workgroups take the
+    // remaining tiles in order as CUs free up.
+    const int n_tiles = tile_off[ndocs];
+    const int bid = blockIdx.x;
+    const int tile = (n_tiles >= 2 * ncu && bid >= ncu && bid < 2 * ncu) ? 3 * ncu - 1 - bid : bid;
+    if (tile >= n_tiles) return;
     const int d = tile_doc(tile_off, ndocs, tile);
     const int nt_doc = tile_off[d + 1] - tile_off[d];
     const int local_tile = nt_doc - 1 - (tile - tile_off[d]);  // longest rows first
@@ -133,8 +149,27 @@ __global__ __launch_bounds__(256) void block_scores_kernel(
     const int c = p0 / kBlock;                                  // query block (shared by tile)
     const int key_end = min(doc.len, p0 + kScoreTile);          // keys past this never count
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 31, hb = lane >> 5;
+
+    // Key block b -> LDS buffer buf: wave w issues copies kCopiesPerWave*w ..
+    // (one KiB each, kRowsPerCopy rows); lane l of a copy fills row
+    // l / kChunks at position l % kChunks, i.e. chunk (l % kChunks) ^ sswz.
+    // Rows at or past key_end occur only in the query's own block, where the
+    // causal mask drops them: they re-read row key_end - 1, in the document.
+    auto issue_block = [&](int b, int buf) {
+#pragma unroll
+        for (int i = 0; i < L::kCopiesPerWave; ++i) {
+            const int cp = L::kCopiesPerWave * wave + i;
+            const int r = L::kRowsPerCopy * cp + lane / L::kChunks;
+            const int chunk = (lane % L::kChunks) ^ sswz<kFp8>(r);
+            const int kp = min(b * kBlock + r, key_end - 1);
+            copy_to_lds(ik + size_t(doc.start + kp) * L::kRowBytes + 16 * chunk,
+                        smem + buf * L::kBufBytes + cp * 1024);
+        }
+    };
+    issue_block(0, 0);
 
     // Index-query operand (B), kept in registers for the whole key loop.
     // Column n of N-tile nt is row (token p0+16*wave+8*nt+n/4, head n%4).
@@ -161,108 +196,76 @@ __global__ __launch_bounds__(256) void block_scores_kernel(
         }
     }
 
-    // Stage key block b (rows doc.start + 128b + r, r < 128) into registers.
-    // Rows at or past key_end occur only in the query's own block, where the
-    // causal mask drops them: they re-read row key_end - 1, so every load is
-    // unconditional and stays in the document.
-    // Two register stages: block b+1 waits in one while block b+2 loads into
-    // the other (two blocks of compute cover a load's latency).
-    typedef u32x4 Stage[L::kChunksPerThread];
-    Stage stA, stB;
-    auto load_block = [&](int b, Stage &stage) {
-#pragma unroll
-        for (int i = 0; i < L::kChunksPerThread; ++i) {
-            const int chunk = tid + 256 * i;
-            const int r = chunk / L::kChunksPerRow, col = chunk % L::kChunksPerRow;
-            const int kp = min(b * kBlock + r, key_end - 1);
-            stage[i] = *(const u32x4 *)(ik + size_t(doc.start + kp) * L::kRowBytes + 16 * col);
-        }
-    };
-    auto store_block = [&](int buf, const Stage &stage) {
-        uint8_t *dst = smem + buf * L::kBufBytes;
-#pragma unroll
-        for (int i = 0; i < L::kChunksPerThread; ++i) {
-            const int chunk = tid + 256 * i;
-            const int r = chunk / L::kChunksPerRow, col = chunk % L::kChunksPerRow;
-            *(u32x4 *)(dst + r * L::kPitch + 16 * col) = stage[i];
+    // A fragment of M-tile mt, k-step ks: row 32mt + n, this lane's 16 (bf16)
+    // or 32 (E4M3) bytes of the step
+    auto load_frag = [&](const uint8_t *kb, int mt, int ks) {
+        const int r = 32 * mt + n;
+        const uint8_t *row = kb + r * L::kRowBytes;
+        if constexpr (kFp8) {
+            const int c0 = 4 * ks + 2 * hb;
+            const u32x4 lo = *(const u32x4 *)(row + ((c0 ^ sswz<kFp8>(r)) << 4));
+            const u32x4 hi = *(const u32x4 *)(row + (((c0 + 1) ^ sswz<kFp8>(r)) << 4));
+            return Frag{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        } else {
+            return __builtin_bit_cast(bf16x8, *(const u32x4 *)(row + (((2 * ks + hb) ^ sswz<kFp8>(r)) << 4)));
         }
     };
 
-    load_block(0, stA);
-    store_block(0, stA);
-    load_block(min(1, c), stB);
-    __syncthreads();
+    // Block loop: at the barrier of block b its copies have landed (each
+    // wave waited for its own) and every wave is done with block b-1, whose
+    // buffer then receives block b+1 while block b is computed.
+    for (int b = 0; b <= c; ++b) {
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's copies of block b (and its score stores)
+        barrier_keep_prefetch();
+        if (b < c) issue_block(b + 1, (b + 1) & 1);
+        const uint8_t *kb = smem + (b & 1) * L::kBufBytes;
 
-    // block b from LDS buffer b&1; nxt holds block b+1, far receives block
-    // b+2 (clamped to c: past the end it re-reads the last block, so the
-    // load is unconditional and the compiler's waits stay exact)
-    auto step = [&](int b, Stage &nxt, Stage &far) {
-        const int buf = b & 1;
-        load_block(min(b + 2, c), far);
-
-        f32x16 acc[4][2];
+        // M-tile by M-tile (32 keys): a tile's max over its keys is taken
+        // while the next tile's MFMAs run.  Lane (n, hb) of an N-tile
+        // accumulator holds keys 32mt + 8(r/4) + 4hb + r%4 of column n.
+        float mxv[2] = {-INFINITY, -INFINITY};
+        Frag fa = load_frag(kb, 0, 0);
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < 4; ++mt) {
+            f32x16 acc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f32x16{};
-
-        const uint8_t *kb = smem + buf * L::kBufBytes;
-#pragma unroll
-        for (int ks = 0; ks < kSteps; ++ks) {
-            Frag a[4];
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                const uint8_t *src = kb + (32 * mt + n) * L::kPitch;
-                if constexpr (kFp8) {
-                    u32x4 lo = *(const u32x4 *)(src + 64 * ks + 32 * hb);
-                    u32x4 hi = *(const u32x4 *)(src + 64 * ks + 32 * hb + 16);
-                    a[mt] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                                  (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-                } else {
-                    a[mt] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(src + 2 * (16 * ks + 8 * hb)));
-                }
-            }
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
+            for (int ks = 0; ks < kSteps; ++ks) {
+                const Frag cur = fa;
+                if (ks + 1 < kSteps) fa = load_frag(kb, mt, ks + 1);
+                else if (mt + 1 < 4) fa = load_frag(kb, mt + 1, 0);
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt) {
                     if constexpr (kFp8)
-                        acc[mt][nt] = mfma_32x32x64_e4m3(a[mt], qb[nt][ks], acc[mt][nt]);
+                        acc[nt] = mfma_32x32x64_e4m3(cur, qb[nt][ks], acc[nt]);
                     else
-                        acc[mt][nt] = mfma_32x32x16(a[mt], qb[nt][ks], acc[mt][nt]);
+                        acc[nt] = mfma_32x32x16(cur, qb[nt][ks], acc[nt]);
                 }
-        }
-
-        // Per query column: max over the block's 128 keys (rows), causal in
-        // the query's own block only (one branch per block, so the other
-        // blocks take a plain max).
-        float mxv[2];
-        if (b == c) {
+                // interleave: the next fragment's LDS read, then each MFMA
+                // with a few VALU ops (the previous M-tile's max)
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
+            }
+            if (b == c) {  // the query's own block: keys past the column's token drop
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-                const int p = p0 + 16 * wave + 8 * nt + n / 4;
-                float mx = -INFINITY;
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt)
+                for (int nt = 0; nt < 2; ++nt) {
+                    const int p = p0 + 16 * wave + 8 * nt + n / 4;
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int kp = b * kBlock + 32 * mt + 8 * (r >> 2) + 4 * hb + (r & 3);
-                        mx = fmaxf(mx, kp > p ? -INFINITY : acc[mt][nt][r]);
+                        mxv[nt] = fmaxf(mxv[nt], kp > p ? -INFINITY : acc[nt][r]);
                     }
-                mxv[nt] = mx;
-            }
-        } else {
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-                float m4[4];
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt) {
-                    float m = acc[mt][nt][0];
-#pragma unroll
-                    for (int r = 1; r < 16; ++r) m = fmaxf(m, acc[mt][nt][r]);
-                    m4[mt] = m;
                 }
-                mxv[nt] = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+            } else {
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    float m = acc[nt][0];
+#pragma unroll
+                    for (int r = 1; r < 16; ++r) m = fmaxf(m, acc[nt][r]);
+                    mxv[nt] = fmaxf(mxv[nt], m);
+                }
             }
         }
 #pragma unroll
@@ -272,14 +275,6 @@ __global__ __launch_bounds__(256) void block_scores_kernel(
             if (hb == 0 && p < doc.len)
                 S[(size_t(n & 3) * nb_max + b) * T + doc.start + p] = mx;
         }
-
-        if (b < c) store_block(buf ^ 1, nxt);
-        __syncthreads();
-    };
-    for (int b = 0; b <= c; b += 2) {
-        step(b, stB, stA);
-        if (b + 1 > c) break;
-        step(b + 1, stA, stB);
     }
 }
 
@@ -288,16 +283,20 @@ hipError_t launch_block_scores(const void *iq, const void *ik, bool fp8, const D
                                float *S, hipStream_t stream) {
     const int nb_max = ceil_div(max_seqlen, kBlock);
     const int grid = ceil_div(T, kScoreTile) + ndocs;  // upper bound on document-aligned tiles
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu < 1)
+        ncu = 0;  // no pairing
     if (fp8) {
-        const size_t lds = 2 * ScoreLayout<true>::kBufBytes;
+        const size_t lds = 2 * ScoreLayout<true>::kBufBytes;  // two key blocks
         hipLaunchKernelGGL(block_scores_kernel<true>, dim3(grid), dim3(256), lds, stream,
                            (const uint8_t *)iq, (const uint8_t *)ik, docs, tile_off, ndocs, T,
-                           nb_max, S);
+                           nb_max, ncu, S);
     } else {
         const size_t lds = 2 * ScoreLayout<false>::kBufBytes;
         hipLaunchKernelGGL(block_scores_kernel<false>, dim3(grid), dim3(256), lds, stream,
                            (const uint8_t *)iq, (const uint8_t *)ik, docs, tile_off, ndocs, T,
-                           nb_max, S);
+                           nb_max, ncu, S);
     }
     return hipGetLastError();
 }
