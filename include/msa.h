@@ -90,7 +90,10 @@ const char *msa_last_error(void);
 /* Library version, major*10000 + minor*100 + patch. */
 int msa_version(void);
 
-/* Workspace sizes in bytes (0 if the arguments are invalid). */
+/* Workspace sizes in bytes (0 if the arguments are invalid).  The select
+ * query takes num_docs besides the token count and the longest document:
+ * the workspace holds the sanitised document spans and the per-document
+ * tile offsets, whose size grows with the number of documents. */
 size_t msa_select_blocks_workspace_bytes(int total_tokens, int num_docs, int max_seqlen);
 size_t msa_prefill_workspace_bytes(int total_tokens, int num_docs, int max_seqlen);
 /* also 0 above 4194304 tokens */
@@ -117,7 +120,10 @@ size_t msa_decode_workspace_bytes(int batch, int max_context_len, int topk);
  *  scores_out  optional out fp32 [4, ceil(max_seqlen/128), T] (head, block,
  *              token): the block score max_{j in block b, j<=t} iq.ik
  *              (raw dot, FP32 accumulation) for b <= c; entries b > c are
- *              left unwritten.  NULL to skip.
+ *              left unwritten.  NULL to skip.  Blocks before tokens (rather
+ *              than [4, T, nb]): the scorer writes one block's scores for
+ *              consecutive tokens and the top-k reads one block for
+ *              consecutive tokens, both coalesced.
  */
 msa_status msa_select_blocks(const void *index_q, const void *index_k, int index_dtype,
                              const int32_t *cu_seqlens, int num_docs, int total_tokens,
