@@ -396,6 +396,10 @@ def planted_gap_gpu(w, iq, ik, cu):
             "planted_share_of_free_slots": round(float(chosen_pl.sum()) / max(1, int(free.sum())), 4)}
 
 
+# counter entries (profiles/hbm_traffic.json) of each prefill workload's attention kernel
+COUNTER_KEYS = {"prefill_32k_planted": "attend_prefill", "packed_2x16k": "attend_prefill_packed"}
+
+
 def prefill_summary(pres, name):
     """The JSON object of one prefill workload: tok/s over real tokens, the
     path's and each kernel's bf16 MFMA fraction on the algorithmic flops."""
@@ -416,10 +420,9 @@ def prefill_summary(pres, name):
                      "achieved": round(pres["attn_flops"] / (a_ms * 1e-3) / 1e12, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(pres["attn_flops"] / (a_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic("attend_prefill") if name == "prefill_32k_planted" else None,
+                     "traffic": measured_traffic(COUNTER_KEYS.get(name, "")),
                      "alg_flops_per_launch": pres["attn_flops"], "avg_launch_us": round(a_ms * 1e3, 3),
-                     "mfma_busy_counter": (measured_counter("attend_prefill", "mfma_busy_frac")
-                                           if name == "prefill_32k_planted" else None)},
+                     "mfma_busy_counter": measured_counter(COUNTER_KEYS.get(name, ""), "mfma_busy_frac")},
         "block_scores": {"achieved_tflops": round(pres["score_flops"] / (s_ms * 1e-3) / 1e12, 2),
                          "frac": round(pres["score_flops"] / (s_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                          "mfma_busy_counter": (measured_counter("block_scores", "mfma_busy_frac")
