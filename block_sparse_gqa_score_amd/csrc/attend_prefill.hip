@@ -22,15 +22,19 @@
 //       union of its tokens' selected blocks, ascending, as 32-key units (K
 //       rows 8 KiB + V^T rows 8 KiB) HBM -> LDS by global_load_lds_dwordx4
 //       through a 9-slot ring, with no workgroup barrier: every unit has an
-//       LDS state word (ready bit, count of the waves that still need it).
-//       Each wave walks only the units its tokens need.  A wave that needs a
-//       unit nobody has copied yet claims it and issues its 16 copies once
-//       every wave needing the unit 9 places earlier is done with that slot;
-//       before computing a unit it claims its next one the same way, so the
-//       copies land during the compute.  A wave computes a unit for those of
-//       its tokens that selected the block; the K and V^T fragments it reads
-//       from LDS once serve all of them.  The slowest wave can always claim
-//       its next unit, so the waits end; each is also bounded by a poll limit.
+//       LDS state word (claimed bit, count of the waves that still need it)
+//       and every slot a flag, the id of the unit whose copies last landed
+//       there (a 17th copy, of the id, issued after the unit's 16: a wave's
+//       copies land in issue order).  Each wave walks only the units its
+//       tokens need.  A wave that needs a unit nobody has copied yet claims
+//       it and issues its copies once every wave needing the unit 9 places
+//       earlier is done with that slot; before computing a unit it claims its
+//       next one the same way, so the copies land during the compute.  A unit
+//       only one wave needs is claimed without a returning atomic.  A wave
+//       computes a unit for those of its tokens that selected the block; the
+//       K and V^T fragments it reads from LDS once serve all of them.  The
+//       slowest wave can always claim its next unit, so the waits end; each
+//       is also bounded by a poll limit.
 //
 // Per wave, token and 32-key unit (MFMA 16x16x32 bf16, key rows m, head
 // columns n):
@@ -67,9 +71,21 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazyLog2 = 8.f;  // rescale only when the max grows by > 2^8
 constexpr int kMaxUnits = kUnitsPerBlock * kMaxUnion;  // ring units of a tile at most
 // Unit state words in LDS: bits 0-7 count the waves that still have to read
-// the unit, kClaimed / kReady mark its copy issued / landed.
-constexpr uint32_t kClaimed = 0x100u, kReady = 0x200u;
+// the unit, kClaimed marks its copy issued.  Whether the copy has landed is
+// read from the ring slot's flag.
+constexpr uint32_t kClaimed = 0x100u;
 constexpr int kSpinLimit = 1 << 14;  // polls before a wait gives up (never reached in a correct run)
+
+// Unit ids 0..kMaxUnits-1 in device memory: the source of the ready flags'
+// copies (the flag of a ring slot holds the id of the unit whose data last
+// landed there).
+struct UnitIds {
+    int v[kMaxUnits];
+    constexpr UnitIds() : v() {
+        for (int i = 0; i < kMaxUnits; ++i) v[i] = i;
+    }
+};
+__device__ const UnitIds kUnitIds = UnitIds();
 
 static_assert(kTpw * kWaves == kTok && kTpw <= kBitsPerWave && kTpw <= 8, "slots fit the mask fields");
 
@@ -336,6 +352,7 @@ __global__ __launch_bounds__(kThreads) void attend_prefill_kernel(
     __shared__ uint32_t s_unit[kMaxUnits];        // per ring unit: state bits | waves still to read it
     __shared__ int s_wlist[kWaves][kTpw * kMaxTopk];  // per wave: the ring blocks it needs, ascending
     __shared__ int s_w[kWaves];
+    __shared__ int s_flag[kRing][64];             // per ring slot: id of the unit that has landed there
 
     // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs; XCD x
     // serves KV head x/2 and alternate groups of 5 tiles (one 128-token query
@@ -431,7 +448,8 @@ __global__ __launch_bounds__(kThreads) void attend_prefill_kernel(
             nwb += __popcll(m);
         }
     }
-    __syncthreads();  // lists and counts are set; the union's LDS is free for the ring
+    for (int i = tid; i < kRing * 64; i += kThreads) (&s_flag[0][0])[i] = -1;
+    __syncthreads();  // lists, counts and flags are set; the union's LDS is free for the ring
 
     // Lane-constant LDS byte offsets of the operand reads.
     // K: M-tile mt row n is key 8(n/4) + 4mt + n%4, whose kswz is n.
@@ -442,6 +460,15 @@ __global__ __launch_bounds__(kThreads) void attend_prefill_kernel(
     const int v_off = 64 * n + 16 * (grp ^ vswz(n));
     const int tok_ok = (ntok - wave + kWaves - 1) / kWaves;  // slots t < tok_ok of this wave hold a token
     const uint32_t ok_mask = (1u << tok_ok) - 1u;
+    // The wave's list in one VGPR, entry i in lane i (read back with
+    // readlane): the wave's slots that selected the block (bits 0-2), its
+    // ring block index (bits 3-11) and its id (bits 12-31).
+    static_assert(kTpw <= 3 && kMaxUnion <= 512, "list entry fields");
+    uint32_t wl = 0u;
+    if (lane < nwb) {
+        const int bi = s_wlist[wave][lane];
+        wl = ((s_smask[bi] >> (kBitsPerWave * wave)) & ok_mask) | (uint32_t(bi) << 3) | (uint32_t(s_sblk[bi]) << 12);
+    }
 
     // ---- HBM -> LDS copy of ring unit u (16 one-KiB copies, all issued by
     // the wave that claimed it) into slot u % kRing, copy i to slot byte
@@ -466,6 +493,9 @@ __global__ __launch_bounds__(kThreads) void attend_prefill_kernel(
             const int dd = 16 * i + (lane >> 2);
             copy_to_lds(vsrc + dd * kAttnUnit + 8 * ((lane & 3) ^ vswz(dd)), slot + kKUnitBytes + i * 1024);
         }
+        // Copies land in issue order: once the flag holds u, the data has landed.
+        const uint32_t m0 = (uint32_t)reinterpret_cast<uintptr_t>((lds_void *)&s_flag[u % kRing][0]);
+        asm volatile("global_load_lds_dword %0, off" ::"v"(&kUnitIds.v[u]), "{m0}"(m0) : "memory");
     };
     // Unit state, read by every lane (LDS broadcast); changed by lane 0.
     auto unit_word = [&](int u) {
@@ -479,31 +509,24 @@ __global__ __launch_bounds__(kThreads) void attend_prefill_kernel(
         if (lane == 0) old = __hip_atomic_fetch_or(&s_unit[u], kClaimed, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
         return (__builtin_amdgcn_readfirstlane(old) & kClaimed) == 0u;
     };
-    auto publish = [&](int u) {  // the copies of u have landed (this wave waited for them)
-        if (lane == 0) __hip_atomic_fetch_or(&s_unit[u], kReady, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-    };
-    auto release = [&](int u) {  // this wave is done reading unit u
-        if (lane == 0) __hip_atomic_fetch_sub(&s_unit[u], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    auto landed = [&](int u) {
+        return __builtin_amdgcn_readfirstlane(
+                   __hip_atomic_load(&s_flag[u % kRing][lane], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP)) == u;
     };
     // Wait until unit u has landed; claim and copy it when nobody has and its
     // slot is free.  Every wait is bounded (kSpinLimit polls).
     auto acquire = [&](int u) {
         for (int spin = 0; spin < kSpinLimit; ++spin) {
+            if (landed(u)) return;
             const uint32_t wd = unit_word(u);
-            if (wd & kReady) return;
-            if (!(wd & kClaimed) && fillable(u) && try_claim(u)) {
-                issue_unit(u);
-                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                publish(u);
-                return;
-            }
+            if (!(wd & kClaimed) && fillable(u) && try_claim(u)) issue_unit(u);
             __builtin_amdgcn_s_sleep(1);
         }
     };
 
     // ---- the wave's walk over its needed units, in ring order.  Before
-    // computing a unit it claims the next one it needs, when free, and
-    // publishes it after the compute (its copies land meanwhile).
+    // computing a unit it claims the next one it needs, when that unit's slot
+    // is free, and issues its copies, which land during the compute.
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): query operands are in (no copy issued yet)
     for (int k = 0; k < nwb; ++k) {
         // keep every O^T accumulator in AGPRs across the loop (the register
@@ -513,23 +536,34 @@ __global__ __launch_bounds__(kThreads) void attend_prefill_kernel(
         for (int t = 0; t < kTpw; ++t)
 #pragma unroll
             for (int dt = 0; dt < 8; ++dt) asm volatile("" : "+a"(st.acc_o[t][dt]));
-        const int bi = __builtin_amdgcn_readfirstlane(s_wlist[wave][k]);
-        const int b = __builtin_amdgcn_readfirstlane(s_sblk[bi]);
-        const uint32_t act = (__builtin_amdgcn_readfirstlane(s_smask[bi]) >> (kBitsPerWave * wave)) & ok_mask;
+        const uint32_t e = __builtin_amdgcn_readlane(wl, k);
+        const int bi = (e >> 3) & 511u;
+        const uint32_t act = e & 7u;
         const int nq = bi == ns - 1 ? last_units : kUnitsPerBlock;
-        const bool own = b == c;
-        const int nxt_bi = k + 1 < nwb ? __builtin_amdgcn_readfirstlane(s_wlist[wave][k + 1]) : -1;
+        const bool own = int(e >> 12) == c;
+        const int nxt_bi = k + 1 < nwb ? int((__builtin_amdgcn_readlane(wl, k + 1) >> 3) & 511u) : -1;
 #pragma unroll 1
         for (int qq = 0; qq < nq; ++qq) {
             const int u = kUnitsPerBlock * bi + qq;
-            acquire(u);
             const int v = qq + 1 < nq ? u + 1 : (nxt_bi >= 0 ? kUnitsPerBlock * nxt_bi : -1);
-            bool ahead = false;
-            if (v >= 0) {
-                const uint32_t wd = unit_word(v);
-                if (!(wd & (kClaimed | kReady)) && fillable(v) && try_claim(v)) {
+            // One LDS round trip: u's flag, v's state and the state of the unit
+            // before v in its slot (v = -1: none; below kRing: the slot is new).
+            const int vs = v >= 0 ? v : u;
+            const int vp = v >= kRing ? v - kRing : u;
+            const int fl = __hip_atomic_load(&s_flag[u % kRing][lane], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+            const uint32_t wv = __hip_atomic_load(&s_unit[vs], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            const uint32_t wp = __hip_atomic_load(&s_unit[vp], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            if (__builtin_amdgcn_readfirstlane(fl) != u) acquire(u);
+            // claim v ahead when its slot is free: a unit that only this wave
+            // needs (count 1, nobody has read it) is marked without a returning
+            // atomic; a shared one goes to whichever wave claims it first
+            const uint32_t wvs = __builtin_amdgcn_readfirstlane(wv);
+            if (v >= 0 && !(wvs & kClaimed) && (v < kRing || (__builtin_amdgcn_readfirstlane(wp) & 0xFFu) == 0u)) {
+                if ((wvs & 0xFFu) == 1u) {
+                    if (lane == 0) __hip_atomic_fetch_or(&s_unit[v], kClaimed, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
                     issue_unit(v);
-                    ahead = true;
+                } else if (try_claim(v)) {
+                    issue_unit(v);
                 }
             }
             const uint8_t *Ku = smem + (u % kRing) * kUnitBytes;
@@ -537,13 +571,12 @@ __global__ __launch_bounds__(kThreads) void attend_prefill_kernel(
             if (act)
                 ring_unit(st, Ku, act, k_row_off, v_off, n, grp, own && qq >= q_lo, kAttnUnit * qq + 8 * grp,
                           pos0 - c * kBlock, scale_log2);
-            release(u);
-            if (ahead) {
-                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                publish(v);
-            }
+            // done reading unit u: its slot may be refilled once every wave needing it is done
+            if (lane == 0)
+                __hip_atomic_fetch_sub(&s_unit[u], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
         }
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // every copy this wave issued has landed
 
     // ---- epilogue: normalise and store bf16 (lane holds d = 16dt + 4grp + i)
 #pragma unroll
