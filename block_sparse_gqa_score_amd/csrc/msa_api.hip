@@ -63,15 +63,18 @@ struct TimingScope {
 constexpr int kDecodeMaxBlocks = 64 * 128;
 
 struct SelectWs {
-    size_t docs, off, scores, total;
+    size_t docs, off, work_off, scores, total;
 };
 
+// document spans; per document, prefix counts of the scorer's tiles and of
+// its (tile, key block) work items; block scores
 SelectWs select_layout(int T, int ndocs, int max_seqlen) {
     SelectWs w;
     const int nb_max = ceil_div(max_seqlen, kBlock);
     w.docs = 0;
     w.off = align256(w.docs + sizeof(DocSpan) * size_t(ndocs));
-    w.scores = align256(w.off + sizeof(int32_t) * (size_t(ndocs) + 1));
+    w.work_off = align256(w.off + sizeof(int32_t) * (size_t(ndocs) + 1));
+    w.scores = align256(w.work_off + sizeof(int32_t) * (size_t(ndocs) + 1));
     w.total = align256(w.scores + sizeof(float) * size_t(kIdxHeads) * nb_max * size_t(T));
     return w;
 }
@@ -237,16 +240,17 @@ msa_status msa_select_blocks(const void *index_q, const void *index_k, int index
     uint8_t *base = (uint8_t *)workspace;
     DocSpan *docs = (DocSpan *)(base + ws.docs);
     int32_t *off = (int32_t *)(base + ws.off);
+    int32_t *work_off = (int32_t *)(base + ws.work_off);
     float *S = scores_out ? scores_out : (float *)(base + ws.scores);
     const int nb_max = ceil_div(max_seqlen, kBlock);
     TimingScope tm;
     tm.mark(s, "doc_setup");
-    hipError_t e = launch_doc_setup(cu_seqlens, num_docs, total_tokens, max_seqlen, kScoreTile, 0,
-                                    docs, off, nullptr, s);
+    hipError_t e = launch_doc_setup(cu_seqlens, num_docs, total_tokens, max_seqlen, kScoreTile, -1,
+                                    docs, off, work_off, s);
     if (e != hipSuccess) return hip_fail(e, "doc_setup");
     tm.mark(s, "block_scores");
-    e = launch_block_scores(index_q, index_k, index_dtype == MSA_INDEX_FP8_E4M3, docs, off, num_docs,
-                            total_tokens, max_seqlen, S, s);
+    e = launch_block_scores(index_q, index_k, index_dtype == MSA_INDEX_FP8_E4M3, docs, off, work_off,
+                            num_docs, total_tokens, max_seqlen, S, s);
     if (e != hipSuccess) return hip_fail(e, "block_scores");
     tm.mark(s, "topk_prefill");
     e = launch_topk_prefill(S, docs, num_docs, total_tokens, nb_max, topk, init_blocks, local_blocks,

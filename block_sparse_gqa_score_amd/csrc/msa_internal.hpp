@@ -27,8 +27,8 @@ hipError_t launch_doc_setup(const int32_t *cu, int ndocs, int T, int max_seqlen,
 
 // Block scores S[h][b][t] (fp32, [4][nb_max][T]) for b <= c(t).
 hipError_t launch_block_scores(const void *iq, const void *ik, bool fp8, const DocSpan *docs,
-                               const int32_t *tile_off, int ndocs, int T, int max_seqlen,
-                               float *S, hipStream_t stream);
+                               const int32_t *tile_off, const int32_t *work_off, int ndocs, int T,
+                               int max_seqlen, float *S, hipStream_t stream);
 
 // Forced blocks + top-k from S into q2k [4][T][topk].
 hipError_t launch_topk_prefill(const float *S, const DocSpan *docs, int ndocs, int T, int nb_max,

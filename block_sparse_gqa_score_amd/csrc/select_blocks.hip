@@ -11,14 +11,18 @@
 // ascending, padded with -1.
 //
 // Kernels:
-//   doc_setup_kernel    - sanitised document spans + tile prefix counts.
+//   doc_setup_kernel    - sanitised document spans + tile prefix counts
+//                         (for the scorer also the prefix counts of its
+//                         (tile, key block) work items).
 //   block_scores_kernel - S^T = K . IQ^T on MFMA (bf16 32x32x16 or E4M3
 //                         32x32x64 with unit scales), fused causal mask and
-//                         per-block row max; one workgroup = 64 query tokens
-//                         x 4 index heads of one document, two per CU,
-//                         looping over key blocks 0..c, each copied from
+//                         per-block row max for (tile, key block) items; a
+//                         tile is 64 query tokens x 4 index heads of one
+//                         document and its items are blocks 0..c.  Two
+//                         workgroups per CU, each taking an equal contiguous
+//                         range of all items; each key block is copied from
 //                         global memory into LDS (swizzled, double-buffered)
-//                         while the block before it is computed.
+//                         while the item before it is computed.
 //   topk_prefill_kernel - one lane per (head, token) row: top-R insertion
 //                         over 32-bit order keys of the scores, then an
 //                         ascending emit pass that takes every candidate
@@ -38,6 +42,16 @@ __device__ __forceinline__ int tiles_in_doc(int len, int tile) {
     const int per_block = (kBlock + tile - 1) / tile;
     const int rest = len % kBlock;
     return (len / kBlock) * per_block + (rest + tile - 1) / tile;
+}
+
+// Block-scorer work of a document of len tokens: its kScoreTile-token tiles,
+// tile j in query block j/2, each scored against blocks 0..j/2.  With m = nt/2,
+// tiles 0..2m-1 hold 2(1 + 2 + ... + m) = m(m+1) (tile, block) pairs, and an
+// odd last tile m + 1 more.
+__device__ __forceinline__ int score_work_in_doc(int len) {
+    const int nt = tiles_in_doc(len, kScoreTile);
+    const int m = nt >> 1;
+    return m * (m + 1) + ((nt & 1) ? m + 1 : 0);
 }
 
 __global__ __launch_bounds__(1024) void doc_setup_kernel(const int32_t *__restrict__ cu, int ndocs,
@@ -64,7 +78,8 @@ __global__ __launch_bounds__(1024) void doc_setup_kernel(const int32_t *__restri
             int len = min(e - s, max_seqlen);
             docs[d] = DocSpan{s, len};
             na = tiles_in_doc(len, tile_a);
-            nb = tile_b > 0 ? tiles_in_doc(len, tile_b) : 0;
+            // tile_b < 0: the block scorer's (tile, block) pairs instead of tiles
+            nb = tile_b > 0 ? tiles_in_doc(len, tile_b) : tile_b < 0 ? score_work_in_doc(len) : 0;
         }
         // inclusive wave scans
 #pragma unroll
@@ -125,76 +140,115 @@ __device__ __forceinline__ int sswz(int r) {
     return kFp8 ? ((r >> 1) & 7) : (r & 15);
 }
 
+static_assert(kScoreTile * 2 == kBlock, "two scorer tiles per query block");
+
+// Tile j and block b of a document's local work index x (tiles in order,
+// each over its blocks 0..j/2): tiles 2m and 2m+1 start at m(m+1) and
+// m(m+1) + m + 1.
+__device__ __forceinline__ void score_work_at(int x, int &j, int &b) {
+    int m = int((__builtin_sqrtf(4.f * float(x) + 1.f) - 1.f) * 0.5f);
+    while (m > 0 && m * (m + 1) > x) --m;
+    while ((m + 1) * (m + 2) <= x) ++m;
+    const int rem = x - m * (m + 1);
+    const bool second = rem >= m + 1;
+    j = 2 * m + (second ? 1 : 0);
+    b = second ? rem - (m + 1) : rem;
+}
+
 template <bool kFp8>
 __global__ __launch_bounds__(256, 2) void block_scores_kernel(
     const uint8_t *__restrict__ iq, const uint8_t *__restrict__ ik, const DocSpan *__restrict__ docs,
-    const int32_t *__restrict__ tile_off, int ndocs, int T, int nb_max, int ncu, float *__restrict__ S) {
+    const int32_t *__restrict__ tile_off, const int32_t *__restrict__ work_off, int ndocs, int T, int nb_max,
+    float *__restrict__ S) {
     using L = ScoreLayout<kFp8>;
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];  // two key blocks
 
-    // Two workgroups share a CU, and the first 2*ncu start at once, the
-    // second ncu on the CUs of the first.  Tiles come longest first, so
-    // workgroup ncu + k takes tile 2*ncu - 1 - k: the pair on a CU then holds
-    // about the same total of key blocks.  Later workgroups take the
-    // remaining tiles in order as CUs free up.
-    const int n_tiles = tile_off[ndocs];
-    const int bid = blockIdx.x;
-    const int tile = (n_tiles >= 2 * ncu && bid >= ncu && bid < 2 * ncu) ? 3 * ncu - 1 - bid : bid;
-    if (tile >= n_tiles) return;
-    const int d = tile_doc(tile_off, ndocs, tile);
-    const int nt_doc = tile_off[d + 1] - tile_off[d];
-    const int local_tile = nt_doc - 1 - (tile - tile_off[d]);  // longest rows first
-    const DocSpan doc = docs[d];
-    const int p0 = local_tile * kScoreTile;                     // doc-local first query
-    const int c = p0 / kBlock;                                  // query block (shared by tile)
-    const int key_end = min(doc.len, p0 + kScoreTile);          // keys past this never count
+    // The work is the list of (tile, key block) pairs: documents in order, a
+    // document's tiles in order, a tile's blocks 0..c.  Workgroup w takes the
+    // w-th of gridDim.x equal contiguous ranges, so that the two workgroups of
+    // every CU run (two waves per SIMD) until the end.
+    const int total = work_off[ndocs];
+    const int bid = blockIdx.x, nwg = gridDim.x;
+    const int g0 = int((int64_t(total) * bid) / nwg);
+    const int g1 = int((int64_t(total) * (bid + 1)) / nwg);
+    if (g0 >= g1) return;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 31, hb = lane >> 5;
 
-    // Key block b -> LDS buffer buf: wave w issues copies kCopiesPerWave*w ..
-    // (one KiB each, kRowsPerCopy rows); lane l of a copy fills row
-    // l / kChunks at position l % kChunks, i.e. chunk (l % kChunks) ^ sswz.
-    // Rows at or past key_end occur only in the query's own block, where the
-    // causal mask drops them: they re-read row key_end - 1, in the document.
-    auto issue_block = [&](int b, int buf) {
+    // position of a work item: document d, its tile j (query block c = j/2),
+    // key block b
+    struct Pos {
+        int d, j, b;
+    };
+    auto locate = [&](int g) {
+        Pos p;
+        p.d = tile_doc(work_off, ndocs, g);
+        score_work_at(g - work_off[p.d], p.j, p.b);
+        return p;
+    };
+    // the item after p (items within [g0, g1) only: a document with work left)
+    auto next = [&](Pos p) {
+        if (p.b < p.j / 2) {
+            ++p.b;
+        } else if (p.j + 1 < tile_off[p.d + 1] - tile_off[p.d]) {
+            ++p.j;
+            p.b = 0;
+        } else {
+            do { ++p.d; } while (work_off[p.d + 1] == work_off[p.d]);
+            p.j = 0;
+            p.b = 0;
+        }
+        return p;
+    };
+
+    // Key block b of tile p -> LDS buffer buf: wave w issues copies
+    // kCopiesPerWave*w .. (one KiB each, kRowsPerCopy rows); lane l of a copy
+    // fills row l / kChunks at position l % kChunks, i.e. chunk
+    // (l % kChunks) ^ sswz.  Rows at or past the tile's key end occur only in
+    // its own query block, where the causal mask drops them: they re-read the
+    // row before that end, in the document.
+    auto issue_block = [&](const Pos &p, int buf) {
+        const DocSpan doc = docs[p.d];
+        const int key_end = min(doc.len, (p.j + 1) * kScoreTile);
 #pragma unroll
         for (int i = 0; i < L::kCopiesPerWave; ++i) {
             const int cp = L::kCopiesPerWave * wave + i;
             const int r = L::kRowsPerCopy * cp + lane / L::kChunks;
             const int chunk = (lane % L::kChunks) ^ sswz<kFp8>(r);
-            const int kp = min(b * kBlock + r, key_end - 1);
+            const int kp = min(p.b * kBlock + r, key_end - 1);
             copy_to_lds(ik + size_t(doc.start + kp) * L::kRowBytes + 16 * chunk,
                         smem + buf * L::kBufBytes + cp * 1024);
         }
     };
-    issue_block(0, 0);
 
-    // Index-query operand (B), kept in registers for the whole key loop.
-    // Column n of N-tile nt is row (token p0+16*wave+8*nt+n/4, head n%4).
+    // Index-query operand (B) of the current tile, in registers.  Column n of
+    // N-tile nt is row (token p0+16*wave+8*nt+n/4, head n%4).
     constexpr int kSteps = kFp8 ? 2 : 8;
     typedef typename std::conditional<kFp8, i32x8, bf16x8>::type Frag;
     Frag qb[2][kSteps];
+    auto load_q = [&](const DocSpan &doc, int p0) {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-        const int p = p0 + 16 * wave + 8 * nt + n / 4;
-        const bool ok = p < doc.len;
-        const size_t row = size_t(doc.start + (ok ? p : 0)) * kIdxHeads + (n & 3);
-        const uint8_t *src = iq + row * L::kRowBytes;
+        for (int nt = 0; nt < 2; ++nt) {
+            const int p = p0 + 16 * wave + 8 * nt + n / 4;
+            const bool ok = p < doc.len;
+            const size_t row = size_t(doc.start + (ok ? p : 0)) * kIdxHeads + (n & 3);
+            const uint8_t *src = iq + row * L::kRowBytes;
 #pragma unroll
-        for (int ks = 0; ks < kSteps; ++ks) {
-            if constexpr (kFp8) {
-                u32x4 lo = ok ? *(const u32x4 *)(src + 64 * ks + 32 * hb) : u32x4{0, 0, 0, 0};
-                u32x4 hi = ok ? *(const u32x4 *)(src + 64 * ks + 32 * hb + 16) : u32x4{0, 0, 0, 0};
-                qb[nt][ks] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                                   (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-            } else {
-                u32x4 v = ok ? *(const u32x4 *)(src + 2 * (16 * ks + 8 * hb)) : u32x4{0, 0, 0, 0};
-                qb[nt][ks] = __builtin_bit_cast(bf16x8, v);
+            for (int ks = 0; ks < kSteps; ++ks) {
+                if constexpr (kFp8) {
+                    u32x4 lo = ok ? *(const u32x4 *)(src + 64 * ks + 32 * hb) : u32x4{0, 0, 0, 0};
+                    u32x4 hi = ok ? *(const u32x4 *)(src + 64 * ks + 32 * hb + 16) : u32x4{0, 0, 0, 0};
+                    qb[nt][ks] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                       (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+                } else {
+                    u32x4 v = ok ? *(const u32x4 *)(src + 2 * (16 * ks + 8 * hb)) : u32x4{0, 0, 0, 0};
+                    qb[nt][ks] = __builtin_bit_cast(bf16x8, v);
+                }
             }
         }
-    }
+    };
 
     // A fragment of M-tile mt, k-step ks: row 32mt + n, this lane's 16 (bf16)
     // or 32 (E4M3) bytes of the step
@@ -211,14 +265,30 @@ __global__ __launch_bounds__(256, 2) void block_scores_kernel(
         }
     };
 
-    // Block loop: at the barrier of block b its copies have landed (each
-    // wave waited for its own) and every wave is done with block b-1, whose
-    // buffer then receives block b+1 while block b is computed.
-    for (int b = 0; b <= c; ++b) {
-        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's copies of block b (and its score stores)
+    Pos cur = locate(g0);
+    issue_block(cur, 0);
+    int tile_d = -1, tile_j = -1;  // the tile whose query operand is in qb
+    DocSpan doc{0, 0};
+    int p0 = 0, c = 0;
+
+    // Item loop: at the barrier of item g its copies have landed (each wave
+    // waited for its own) and every wave is done with item g-1, whose buffer
+    // then receives item g+1 while item g is computed.
+    for (int g = g0; g < g1; ++g) {
+        if (cur.d != tile_d || cur.j != tile_j) {  // a new tile (workgroup-uniform)
+            tile_d = cur.d;
+            tile_j = cur.j;
+            doc = docs[cur.d];
+            p0 = cur.j * kScoreTile;
+            c = cur.j / 2;
+            load_q(doc, p0);
+        }
+        const int b = cur.b;
+        const Pos nxt = g + 1 < g1 ? next(cur) : cur;
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's copies of item g (and its loads, stores)
         barrier_keep_prefetch();
-        if (b < c) issue_block(b + 1, (b + 1) & 1);
-        const uint8_t *kb = smem + (b & 1) * L::kBufBytes;
+        if (g + 1 < g1) issue_block(nxt, (g + 1 - g0) & 1);
+        const uint8_t *kb = smem + ((g - g0) & 1) * L::kBufBytes;
 
         // M-tile by M-tile (32 keys): a tile's max over its keys is taken
         // while the next tile's MFMAs run.  Lane (n, hb) of an N-tile
@@ -230,15 +300,15 @@ __global__ __launch_bounds__(256, 2) void block_scores_kernel(
             f32x16 acc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
             for (int ks = 0; ks < kSteps; ++ks) {
-                const Frag cur = fa;
+                const Frag fcur = fa;
                 if (ks + 1 < kSteps) fa = load_frag(kb, mt, ks + 1);
                 else if (mt + 1 < 4) fa = load_frag(kb, mt + 1, 0);
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt) {
                     if constexpr (kFp8)
-                        acc[nt] = mfma_32x32x64_e4m3(cur, qb[nt][ks], acc[nt]);
+                        acc[nt] = mfma_32x32x64_e4m3(fcur, qb[nt][ks], acc[nt]);
                     else
-                        acc[nt] = mfma_32x32x16(cur, qb[nt][ks], acc[nt]);
+                        acc[nt] = mfma_32x32x16(fcur, qb[nt][ks], acc[nt]);
                 }
                 // interleave: the next fragment's LDS read, then each MFMA
                 // with a few VALU ops (the previous M-tile's max)
@@ -275,28 +345,30 @@ __global__ __launch_bounds__(256, 2) void block_scores_kernel(
             if (hb == 0 && p < doc.len)
                 S[(size_t(n & 3) * nb_max + b) * T + doc.start + p] = mx;
         }
+        cur = nxt;
     }
 }
 
 hipError_t launch_block_scores(const void *iq, const void *ik, bool fp8, const DocSpan *docs,
-                               const int32_t *tile_off, int ndocs, int T, int max_seqlen,
-                               float *S, hipStream_t stream) {
+                               const int32_t *tile_off, const int32_t *work_off, int ndocs, int T,
+                               int max_seqlen, float *S, hipStream_t stream) {
     const int nb_max = ceil_div(max_seqlen, kBlock);
-    const int grid = ceil_div(T, kScoreTile) + ndocs;  // upper bound on document-aligned tiles
+    // two workgroups per CU, all resident at once, each with an equal share
     int dev = 0, ncu = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu < 1)
-        ncu = 0;  // no pairing
+        ncu = 256;
+    const int grid = 2 * ncu;
     if (fp8) {
         const size_t lds = 2 * ScoreLayout<true>::kBufBytes;  // two key blocks
         hipLaunchKernelGGL(block_scores_kernel<true>, dim3(grid), dim3(256), lds, stream,
-                           (const uint8_t *)iq, (const uint8_t *)ik, docs, tile_off, ndocs, T,
-                           nb_max, ncu, S);
+                           (const uint8_t *)iq, (const uint8_t *)ik, docs, tile_off, work_off, ndocs, T,
+                           nb_max, S);
     } else {
         const size_t lds = 2 * ScoreLayout<false>::kBufBytes;
         hipLaunchKernelGGL(block_scores_kernel<false>, dim3(grid), dim3(256), lds, stream,
-                           (const uint8_t *)iq, (const uint8_t *)ik, docs, tile_off, ndocs, T,
-                           nb_max, ncu, S);
+                           (const uint8_t *)iq, (const uint8_t *)ik, docs, tile_off, work_off, ndocs, T,
+                           nb_max, S);
     }
     return hipGetLastError();
 }
