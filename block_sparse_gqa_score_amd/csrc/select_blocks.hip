@@ -290,54 +290,65 @@ __global__ __launch_bounds__(256, 2) void block_scores_kernel(
         if (g + 1 < g1) issue_block(nxt, (g + 1 - g0) & 1);
         const uint8_t *kb = smem + ((g - g0) & 1) * L::kBufBytes;
 
-        // M-tile by M-tile (32 keys): a tile's max over its keys is taken
-        // while the next tile's MFMAs run.  Lane (n, hb) of an N-tile
-        // accumulator holds keys 32mt + 8(r/4) + 4hb + r%4 of column n.
+        // K-step by k-step over the 4 M-tiles (32 keys each): the fragment of
+        // step s + kD is read from LDS before step s's MFMAs are issued, and
+        // M-tile mt-1's max (its accumulators are complete by then) is taken
+        // in chunks after the first steps of mt; scheduling fences keep that
+        // order.  Lane (n, hb) of an N-tile accumulator holds keys
+        // 32mt + 8(r/4) + 4hb + r%4 of column n.  The query's own block
+        // (b == c) drops the keys past each column's token.
         float mxv[2] = {-INFINITY, -INFINITY};
-        Frag fa = load_frag(kb, 0, 0);
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            f32x16 acc[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-            for (int ks = 0; ks < kSteps; ++ks) {
-                const Frag fcur = fa;
-                if (ks + 1 < kSteps) fa = load_frag(kb, mt, ks + 1);
-                else if (mt + 1 < 4) fa = load_frag(kb, mt + 1, 0);
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt) {
-                    if constexpr (kFp8)
-                        acc[nt] = mfma_32x32x64_e4m3(fcur, qb[nt][ks], acc[nt]);
-                    else
-                        acc[nt] = mfma_32x32x16(fcur, qb[nt][ks], acc[nt]);
-                }
-                // interleave: the next fragment's LDS read, then each MFMA
-                // with a few VALU ops (the previous M-tile's max)
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
-            }
-            if (b == c) {  // the query's own block: keys past the column's token drop
+        auto item = [&](auto diag_tag) {
+            constexpr bool kDiag = decltype(diag_tag)::value;
+            constexpr int kD = kFp8 ? 2 : 3;           // fragment read distance (steps)
+            constexpr int kSt = 4 * kSteps;            // steps per item
+            constexpr int kChunk = kSteps >= 4 ? 4 : kSteps;  // steps carrying a part of the max
+            constexpr int kRows = 16 / kChunk;         // accumulator rows per part
+            Frag fr[kD + 1];
+            f32x16 acc[2][2];
+            // rows [kRows*part, kRows*(part+1)) of M-tile mt's accumulators into the max
+            auto max_part = [&](int mt, int part, const f32x16 (&a)[2]) {
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt) {
                     const int p = p0 + 16 * wave + 8 * nt + n / 4;
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int kp = b * kBlock + 32 * mt + 8 * (r >> 2) + 4 * hb + (r & 3);
-                        mxv[nt] = fmaxf(mxv[nt], kp > p ? -INFINITY : acc[nt][r]);
+                    for (int rr = 0; rr < kRows; ++rr) {
+                        const int r = kRows * part + rr;
+                        if constexpr (kDiag) {
+                            const int kp = b * kBlock + 32 * mt + 8 * (r >> 2) + 4 * hb + (r & 3);
+                            mxv[nt] = fmaxf(mxv[nt], kp > p ? -INFINITY : a[nt][r]);
+                        } else {
+                            mxv[nt] = fmaxf(mxv[nt], a[nt][r]);
+                        }
                     }
                 }
-            } else {
+            };
+#pragma unroll
+            for (int st = 0; st < kD; ++st) fr[st] = load_frag(kb, st / kSteps, st % kSteps);
+#pragma unroll
+            for (int st = 0; st < kSt; ++st) {
+                const int mt = st / kSteps, ks = st % kSteps;
+                if (st + kD < kSt) fr[(st + kD) % (kD + 1)] = load_frag(kb, (st + kD) / kSteps, (st + kD) % kSteps);
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt) {
-                    float m = acc[nt][0];
-#pragma unroll
-                    for (int r = 1; r < 16; ++r) m = fmaxf(m, acc[nt][r]);
-                    mxv[nt] = fmaxf(mxv[nt], m);
+                    const f32x16 cin = ks == 0 ? f32x16{} : acc[mt & 1][nt];
+                    if constexpr (kFp8)
+                        acc[mt & 1][nt] = mfma_32x32x64_e4m3(fr[st % (kD + 1)], qb[nt][ks], cin);
+                    else
+                        acc[mt & 1][nt] = mfma_32x32x16(fr[st % (kD + 1)], qb[nt][ks], cin);
                 }
+                __builtin_amdgcn_sched_barrier(0);
+                if (mt > 0 && ks < kChunk) max_part(mt - 1, ks, acc[(mt - 1) & 1]);
+                __builtin_amdgcn_sched_barrier(0);
             }
-        }
+#pragma unroll
+            for (int part = 0; part < kChunk; ++part) max_part(3, part, acc[1]);
+        };
+        if (b == c)
+            item(std::true_type{});
+        else
+            item(std::false_type{});
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
             const int p = p0 + 16 * wave + 8 * nt + n / 4;
