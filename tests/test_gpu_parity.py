@@ -34,11 +34,15 @@ PREFILL_CASES = [
     # them) occur here at small sizes
     ("topk16_init1_doc4096", [4096], 16, 1, 1, "bf16"),
     ("topk16_init1_two_docs", [3000, 2500], 16, 1, 1, "bf16"),
+    # many short documents (1..251 tokens): the block scorer's equal work
+    # ranges then start and end inside documents and cross dozens of them
+    ("many_short_docs", [1 + (37 * i) % 251 for i in range(64)], 4, 1, 1, "bf16"),
+    ("fp8_many_short_docs", [1 + (53 * i + 11) % 251 for i in range(64)], 3, 0, 1, "fp8"),
 ]
 E2E_CASES = [c for c in PREFILL_CASES
              if c[0] in ("one_doc_2k_topk4", "ragged_docs_topk4_init1", "docs_topk16_dense",
                          "fp8_ragged_topk4", "fp8_long_topk8", "topk1_local0_argmax",
-                         "topk16_init1_two_docs")]
+                         "topk16_init1_two_docs", "many_short_docs")]
 
 
 def _run_select(w, scores=True):
