@@ -520,6 +520,18 @@ __global__ __launch_bounds__(256) void decode_attend_stream_kernel(
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) qb[ks] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qrow + 8 * (4 * ks + qd)));
 
+    // The page-table entries of the row's candidates (block lane + 64i in
+    // register i, as the scores are held), loaded before the selection so
+    // that their latency overlaps it; an entry past the row is clamped and
+    // never used.  Above 8 candidates per lane (where the extra loads cost
+    // more than the round trip they save) the chosen blocks' entries are
+    // loaded after the selection instead.
+    constexpr bool kPtRegs = kCpl <= 8;
+    int ptv[kPtRegs ? kCpl : 1];
+    if constexpr (kPtRegs) {
+#pragma unroll
+        for (int i = 0; i < kCpl; ++i) ptv[i] = pt[size_t(r) * max_pages + min(lane + 64 * i, max_pages - 1)];
+    }
     // The row's selection from the scores of index head g: every wave computes
     // the same row into its own LDS slots, so no barrier is needed.
     select_row<kCpl>(S + (size_t(r) * kIdxHeads + g) * nb_max, nb_max, c, topk, init, local, lane, s_sel[wave]);
@@ -534,7 +546,17 @@ __global__ __launch_bounds__(256) void decode_attend_stream_kernel(
         const int s = sg * spw + j;
         const int b = (j < spw && s < topk) ? __builtin_amdgcn_readfirstlane(s_sel[wave][s]) : -1;
         const int bb = (b >= 0 && b <= c) ? b : -1;
-        const int page = bb >= 0 ? __builtin_amdgcn_readfirstlane(pt[size_t(r) * max_pages + bb]) : -1;
+        int page = -1;
+        if (bb >= 0) {
+            if constexpr (kPtRegs) {
+                int x = ptv[0];
+#pragma unroll
+                for (int i = 1; i < kCpl; ++i) x = (bb >> 6) == i ? ptv[i] : x;
+                page = __builtin_amdgcn_readlane(x, bb & 63);
+            } else {
+                page = __builtin_amdgcn_readfirstlane(pt[size_t(r) * max_pages + bb]);
+            }
+        }
         bsel[j] = page >= 0 ? bb : -1;
         bpage[j] = page;
     }
