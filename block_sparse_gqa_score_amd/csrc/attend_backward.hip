@@ -14,8 +14,14 @@
 //       pass, a scan (bwd_scan_kernel, also of the chunk counts) and a fill
 //       pass at the scanned offsets; no atomics, so the lists, and every sum
 //       taken over them, are the same on every run.
-//   bwd_dq_kernel       - query-major, on the forward's tile / union-block /
-//       LDS-ring structure with K rows and V rows as the 32-key units: per
+//   bwd_dq_kernel       - query-major: a workgroup takes 16 tokens of one
+//       query block (8 waves x 2 tokens) and streams the union of their
+//       selected blocks as 32-key units (K rows, V rows) through a 9-slot
+//       LDS ring as the forward does: no workgroup barrier, every unit has an
+//       LDS state word (claimed bit, count of the waves that still need it)
+//       and every slot a ready flag (the id of the unit whose copies last
+//       landed there, copied after the unit's 16 copies); each wave walks
+//       only the units its tokens need and claims its next one ahead.  Per
 //       unit S^T = K Q^T, dP^T = V dO^T, P^T and dS^T in registers, then
 //       dQ^T += K^T dS^T with K^T taken by transposing LDS reads.
 //   bwd_dkdv_kernel     - key-major: one workgroup per chunk of kBwdChunk
@@ -205,6 +211,23 @@ constexpr int kHalfBytes = kAttnUnit * kRowB;         // 8 KiB: 32 K rows (or V 
 constexpr int kQUnitBytes = 2 * kHalfBytes;           // K rows, then V rows
 constexpr int kQRing = 2 * kUnitsPerBlock + 1;        // 9 slots (144 KiB)
 static_assert(kQRing * kQUnitBytes <= 144 * 1024, "ring must leave LDS for the union tables");
+constexpr int kQMaxUnion = kQTok * kMaxTopk;               // distinct blocks of a tile at most (256)
+constexpr int kQMaxUnits = kUnitsPerBlock * kQMaxUnion;    // ring units of a tile at most
+// Unit state words in LDS: bits 0-7 count the waves that still have to read
+// the unit, kQClaimed marks its copies issued.  Whether they have landed is
+// read from the ring slot's flag.
+constexpr uint32_t kQClaimed = 0x100u;
+constexpr int kQSpinLimit = 1 << 14;  // polls before a wait gives up (never reached in a correct run)
+
+// Unit ids 0..kQMaxUnits-1 in device memory: the source of the ready flags'
+// copies (a slot's flag holds the id of the unit whose copies last landed).
+struct QUnitIds {
+    int v[kQMaxUnits];
+    constexpr QUnitIds() : v() {
+        for (int i = 0; i < kQMaxUnits; ++i) v[i] = i;
+    }
+};
+__device__ const QUnitIds kQUnitIds = QUnitIds();
 
 // Row r of a 32-row half, 16-byte chunk c (d 8c..8c+7), sits at chunk
 // position c ^ swz32(r).  The 16 rows one plain operand read touches,
@@ -223,61 +246,55 @@ struct DqState {
     float dsum[2];     // D of head n
 };
 
-// One union block for one wave (kA0 / kA1: which tokens compute; kDiag:
-// the query's own block, nq <= 4 units, causal mask, tokens from act_rt).
+// One ring unit (unit q of its block, K rows at Ku, V rows after them) for
+// one wave (kA0 / kA1: which tokens compute; kDiag: the query's own block,
+// causal mask, tokens from act_rt).
 template <bool kA0, bool kA1, bool kDiag>
-__device__ __forceinline__ void dq_block(DqState &st, const uint8_t *smem, int ustart, int nq,
-                                         const int (&k_row_off)[2], int nsw, int grp,
-                                         const int (&tr_row)[2], const int (&tr_x)[2], int tr_lo,
-                                         int keyb, const bool (&act_rt)[2], const int (&my_p)[2],
-                                         float scale_log2) {
+__device__ __forceinline__ void dq_unit(DqState &st, const uint8_t *Ku, int q, const int (&k_row_off)[2], int nsw,
+                                        int grp, const int (&tr_row)[2], const int (&tr_x)[2], int tr_lo, int keyb,
+                                        const bool (&act_rt)[2], const int (&my_p)[2], float scale_log2) {
     const bool act[2] = {kDiag ? act_rt[0] : kA0, kDiag ? act_rt[1] : kA1};
+    const uint8_t *Vu = Ku + kHalfBytes;
+    bf16x8 ka[4][2], va[4][2];
 #pragma unroll
-    for (int q = 0; q < kUnitsPerBlock; ++q) {
-        if (kDiag && q >= nq) break;
-        const uint8_t *Ku = smem + ((ustart + q) % kQRing) * kQUnitBytes;
-        const uint8_t *Vu = Ku + kHalfBytes;
-        bf16x8 ka[4][2], va[4][2];
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            const int off = k_row_off[mt] + (((4 * ks + grp) ^ nsw) << 4);
+            ka[ks][mt] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(Ku + off));
+            va[ks][mt] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(Vu + off));
+        }
+    // S^T and dP^T for this unit; lane (n, grp) holds keys 8grp + 4mt + i
+    bf16x8 dsb[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        if (!act[t]) continue;
+        f32x4 s[2] = {f32x4{}, f32x4{}}, dp[2] = {f32x4{}, f32x4{}};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt) {
-                const int off = k_row_off[mt] + (((4 * ks + grp) ^ nsw) << 4);
-                ka[ks][mt] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(Ku + off));
-                va[ks][mt] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(Vu + off));
+                s[mt] = mfma_16x16x32(ka[ks][mt], st.qb[t][ks], s[mt]);
+                dp[mt] = mfma_16x16x32(va[ks][mt], st.dob[t][ks], dp[mt]);
             }
-        // S^T and dP^T for this unit; lane (n, grp) holds keys 8grp + 4mt + i
-        bf16x8 dsb[2];
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            if (!act[t]) continue;
-            f32x4 s[2] = {f32x4{}, f32x4{}}, dp[2] = {f32x4{}, f32x4{}};
+        for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
+            for (int i = 0; i < 4; ++i) {
+                const bool ok = !kDiag || keyb + kAttnUnit * q + 4 * mt + i <= my_p[t];
+                const float p = ok ? __builtin_amdgcn_exp2f(s[mt][i] * scale_log2 - st.lse2[t]) : 0.f;
+                dsb[t][4 * mt + i] = (__bf16)(p * (dp[mt][i] - st.dsum[t]));
+            }
+    }
+    // dQ^T += K^T dS^T: K^T rows d = 16dt + j, keys 8grp + e from two
+    // transposing reads of K rows 8grp..8grp+3 and 8grp+4..8grp+7
 #pragma unroll
-                for (int mt = 0; mt < 2; ++mt) {
-                    s[mt] = mfma_16x16x32(ka[ks][mt], st.qb[t][ks], s[mt]);
-                    dp[mt] = mfma_16x16x32(va[ks][mt], st.dob[t][ks], dp[mt]);
-                }
+    for (int dt = 0; dt < 8; ++dt) {
+        const bf16x8 kt = join_tr(read_tr(Ku + tr_row[0] + (((2 * dt) ^ tr_x[0]) << 4) + tr_lo),
+                                  read_tr(Ku + tr_row[1] + (((2 * dt) ^ tr_x[1]) << 4) + tr_lo));
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const bool ok = !kDiag || keyb + kAttnUnit * q + 4 * mt + i <= my_p[t];
-                    const float p = ok ? __builtin_amdgcn_exp2f(s[mt][i] * scale_log2 - st.lse2[t]) : 0.f;
-                    dsb[t][4 * mt + i] = (__bf16)(p * (dp[mt][i] - st.dsum[t]));
-                }
-        }
-        // dQ^T += K^T dS^T: K^T rows d = 16dt + j, keys 8grp + e from two
-        // transposing reads of K rows 8grp..8grp+3 and 8grp+4..8grp+7
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-            const bf16x8 kt = join_tr(read_tr(Ku + tr_row[0] + (((2 * dt) ^ tr_x[0]) << 4) + tr_lo),
-                                      read_tr(Ku + tr_row[1] + (((2 * dt) ^ tr_x[1]) << 4) + tr_lo));
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-                if (act[t]) st.acc[t][dt] = mfma_16x16x32(kt, dsb[t], st.acc[t][dt]);
-        }
+        for (int t = 0; t < 2; ++t)
+            if (act[t]) st.acc[t][dt] = mfma_16x16x32(kt, dsb[t], st.acc[t][dt]);
     }
 }
 }  // namespace
@@ -297,6 +314,9 @@ __global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(
     __shared__ int s_ublk[kEntries];
     __shared__ int s_umask[kEntries];
     __shared__ int s_nu;
+    __shared__ uint32_t s_unit[kQMaxUnits];     // per ring unit: claimed bit | waves still to read it
+    __shared__ int s_wlist[kQWaves][2 * kMaxTopk];  // per wave: the union blocks it needs, ascending
+    __shared__ int s_flag[kQRing][64];          // per ring slot: id of the unit that has landed there
 
     // XCD-aware order, as in the forward: XCD x serves KV head x/2.
     const int bid = blockIdx.x;
@@ -350,11 +370,13 @@ __global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(
                               s_ublk, s_umask, &s_nu);
     const int last_units =
         (nu > 0 && s_ublk[nu - 1] == c) ? (p_last - c * kBlock) / kAttnUnit + 1 : kUnitsPerBlock;
-    const int nunits = nu > 0 ? kUnitsPerBlock * (nu - 1) + last_units : 0;
 
-    // Unit copies: copy i < 8 fills K rows 4i..4i+3, copy i >= 8 V rows
-    // 4(i-8)..+3 (lane l: row 4i' + l/16, position l%16, i.e. chunk
-    // (l%16) ^ swz32(row)).  Rows past p_last re-read row p_last.
+    // Unit copies, all 16 issued by the wave that claims the unit: copy
+    // i < 8 fills K rows 4i..4i+3, copy i >= 8 V rows 4(i-8)..+3 (lane l:
+    // row 4i' + l/16, position l%16, i.e. chunk (l%16) ^ swz32(row)).  Rows
+    // past p_last re-read row p_last.  A 17th copy puts the unit's id into
+    // the slot's flag: a wave's copies land in issue order, so the flag shows
+    // the rows landed.
     auto issue_copy = [&](int vu, int ub, int i) {
         const int qq = vu & 3;
         uint8_t *slot = smem + (vu % kQRing) * kQUnitBytes;
@@ -367,9 +389,43 @@ __global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(
     };
     auto issue_unit = [&](int vu) {
         const int ub = __builtin_amdgcn_readfirstlane(s_ublk[vu >> 2]);
-        issue_copy(vu, ub, 2 * wave);
-        issue_copy(vu, ub, 2 * wave + 1);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) issue_copy(vu, ub, i);
+        const uint32_t m0 = (uint32_t)reinterpret_cast<uintptr_t>((lds_void *)&s_flag[vu % kQRing][0]);
+        asm volatile("global_load_lds_dword %0, off" ::"v"(&kQUnitIds.v[vu]), "{m0}"(m0) : "memory");
     };
+
+    // Unit counts (the waves whose tokens selected the unit's block; units of
+    // the query's own block past the tile's last token do not exist) and each
+    // wave's list of the blocks it needs, ascending.
+    for (int u = tid; u < kUnitsPerBlock * nu; u += kQThreads) {
+        const int bi = u / kUnitsPerBlock;
+        const int m = s_umask[bi];
+        int nw = 0;
+#pragma unroll
+        for (int w = 0; w < kQWaves; ++w) nw += ((m >> (2 * w)) & 3) ? 1 : 0;
+        const bool exists = bi < nu - 1 || u % kUnitsPerBlock < last_units;
+        s_unit[u] = exists ? uint32_t(nw) : 0u;
+    }
+    int nwb = 0;
+    for (int u0 = 0; u0 < nu; u0 += 64) {
+        const int u = min(u0 + lane, nu - 1);
+        const bool mine = u0 + lane < nu && ((s_umask[u] >> (2 * wave)) & 3);
+        const uint64_t mm = __ballot(mine);
+        if (mine) s_wlist[wave][nwb + __popcll(mm & ((1ull << lane) - 1ull))] = u;
+        nwb += __popcll(mm);
+    }
+    for (int i = tid; i < kQRing * 64; i += kQThreads) (&s_flag[0][0])[i] = -1;
+    __syncthreads();
+    // The wave's list in one VGPR, entry i in lane i (read with readlane):
+    // its tokens that selected the block (bits 0-1), the block's union index
+    // (bits 2-9) and its id (bits 10-31).
+    static_assert(kQMaxUnion <= 256, "list entry fields");
+    uint32_t wl = 0u;
+    if (lane < nwb) {
+        const int bi = s_wlist[wave][lane];
+        wl = uint32_t((s_umask[bi] >> (2 * wave)) & 3) | (uint32_t(bi) << 2) | (uint32_t(s_ublk[bi]) << 10);
+    }
 
     // Lane-constant LDS offsets.  Plain reads: M-tile mt row n is key
     // 8(n/4) + 4mt + n%4, whose swz32 is nsw.  Transposing reads h = 0, 1:
@@ -387,35 +443,88 @@ __global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(
     }
     const int tr_lo = (n & 1) * 8;
 
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): operands are in (no copy issued yet)
-    int issued = min(nunits, kQRing);
-    for (int vu = 0; vu < issued; ++vu) issue_unit(vu);
-    for (int u = 0; u < nu; ++u) {
-        const int ustart = kUnitsPerBlock * u;
-        const int nq = u == nu - 1 ? nunits - ustart : kUnitsPerBlock;
-        wait_copies(2 * (issued - (ustart + nq)));
-        barrier_keep_prefetch();
+    // Unit state, read by every lane (LDS broadcast); changed by lane 0.
+    auto unit_word = [&](int u) {
+        return __builtin_amdgcn_readfirstlane(
+            __hip_atomic_load(&s_unit[u], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP));
+    };
+    // Slot u % kQRing is free for unit u once every wave needing unit u - kQRing is done with it.
+    auto fillable = [&](int u) { return u < kQRing || (unit_word(u - kQRing) & 0xFFu) == 0u; };
+    auto try_claim = [&](int u) {
+        uint32_t old = kQClaimed;
+        if (lane == 0) old = __hip_atomic_fetch_or(&s_unit[u], kQClaimed, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+        return (__builtin_amdgcn_readfirstlane(old) & kQClaimed) == 0u;
+    };
+    auto landed = [&](int u) {
+        return __builtin_amdgcn_readfirstlane(
+                   __hip_atomic_load(&s_flag[u % kQRing][lane], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP)) == u;
+    };
+    // Wait until unit u has landed; claim and copy it when nobody has and its
+    // slot is free.  Every wait is bounded (kQSpinLimit polls).
+    auto acquire = [&](int u) {
+        for (int spin = 0; spin < kQSpinLimit; ++spin) {
+            if (landed(u)) return;
+            const uint32_t wd = unit_word(u);
+            if (!(wd & kQClaimed) && fillable(u) && try_claim(u)) issue_unit(u);
+            __builtin_amdgcn_s_sleep(1);
+        }
+    };
 
-        const int b = __builtin_amdgcn_readfirstlane(s_ublk[u]);
-        const int umask = __builtin_amdgcn_readfirstlane(s_umask[u]);
-        const bool act[2] = {tok_ok[0] && ((umask >> (2 * wave)) & 1),
-                             tok_ok[1] && ((umask >> (2 * wave + 1)) & 1)};
-        for (const int ifront = min(nunits, ustart + kQRing); issued < ifront; ++issued)
-            issue_unit(issued);
+    // The wave's walk over its needed units, in union order.  Before computing
+    // a unit it claims the next one it needs, when that unit's slot is free,
+    // and issues its copies, which land during the compute; the slowest wave
+    // can always claim its next unit, since every unit kQRing places earlier
+    // was needed only by waves at or beyond it.
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): operands are in (no copy issued yet)
+    for (int kk = 0; kk < nwb; ++kk) {
+        const uint32_t e = __builtin_amdgcn_readlane(wl, kk);
+        const int bi = (e >> 2) & 255u;
+        const int b = int(e >> 10);
+        const bool act[2] = {tok_ok[0] && (e & 1u), tok_ok[1] && ((e >> 1) & 1u)};
+        const int nq = bi == nu - 1 ? last_units : kUnitsPerBlock;
+        const int nxt_bi = kk + 1 < nwb ? int((__builtin_amdgcn_readlane(wl, kk + 1) >> 2) & 255u) : -1;
         const int keyb = b * kBlock + 8 * grp;
-        if (b == c)
-            dq_block<true, true, true>(st, smem, ustart, nq, k_row_off, nsw, grp, tr_row, tr_x, tr_lo,
-                                       keyb, act, my_p, scale_log2);
-        else if (act[0] && act[1])
-            dq_block<true, true, false>(st, smem, ustart, kUnitsPerBlock, k_row_off, nsw, grp, tr_row,
-                                        tr_x, tr_lo, keyb, act, my_p, scale_log2);
-        else if (act[0])
-            dq_block<true, false, false>(st, smem, ustart, kUnitsPerBlock, k_row_off, nsw, grp, tr_row,
-                                         tr_x, tr_lo, keyb, act, my_p, scale_log2);
-        else if (act[1])
-            dq_block<false, true, false>(st, smem, ustart, kUnitsPerBlock, k_row_off, nsw, grp, tr_row,
-                                         tr_x, tr_lo, keyb, act, my_p, scale_log2);
+#pragma unroll 1
+        for (int qq = 0; qq < nq; ++qq) {
+            const int u = kUnitsPerBlock * bi + qq;
+            const int vn = qq + 1 < nq ? u + 1 : (nxt_bi >= 0 ? kUnitsPerBlock * nxt_bi : -1);
+            // One LDS round trip: u's flag, the next unit's state and the
+            // state of the unit before it in its slot.
+            const int vs = vn >= 0 ? vn : u;
+            const int vp = vn >= kQRing ? vn - kQRing : u;
+            const int fl = __hip_atomic_load(&s_flag[u % kQRing][lane], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+            const uint32_t wv = __hip_atomic_load(&s_unit[vs], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            const uint32_t wp = __hip_atomic_load(&s_unit[vp], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            if (__builtin_amdgcn_readfirstlane(fl) != u) acquire(u);
+            // claim the next unit ahead (a unit only this wave needs is marked
+            // with a non-returning atomic)
+            const uint32_t wvs = __builtin_amdgcn_readfirstlane(wv);
+            if (vn >= 0 && !(wvs & kQClaimed) && (vn < kQRing || (__builtin_amdgcn_readfirstlane(wp) & 0xFFu) == 0u)) {
+                if ((wvs & 0xFFu) == 1u) {
+                    if (lane == 0) __hip_atomic_fetch_or(&s_unit[vn], kQClaimed, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                    issue_unit(vn);
+                } else if (try_claim(vn)) {
+                    issue_unit(vn);
+                }
+            }
+            const uint8_t *Ku = smem + (u % kQRing) * kQUnitBytes;
+            if (b == c)
+                dq_unit<true, true, true>(st, Ku, qq, k_row_off, nsw, grp, tr_row, tr_x, tr_lo, keyb, act, my_p,
+                                          scale_log2);
+            else if (act[0] && act[1])
+                dq_unit<true, true, false>(st, Ku, qq, k_row_off, nsw, grp, tr_row, tr_x, tr_lo, keyb, act, my_p,
+                                           scale_log2);
+            else if (act[0])
+                dq_unit<true, false, false>(st, Ku, qq, k_row_off, nsw, grp, tr_row, tr_x, tr_lo, keyb, act, my_p,
+                                            scale_log2);
+            else if (act[1])
+                dq_unit<false, true, false>(st, Ku, qq, k_row_off, nsw, grp, tr_row, tr_x, tr_lo, keyb, act, my_p,
+                                            scale_log2);
+            // done reading unit u
+            if (lane == 0) __hip_atomic_fetch_sub(&s_unit[u], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // every copy this wave issued has landed
 
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
