@@ -25,8 +25,9 @@
 //       unit S^T = K Q^T, dP^T = V dO^T, P^T and dS^T in registers, then
 //       dQ^T += K^T dS^T with K^T taken by transposing LDS reads.
 //   bwd_dkdv_kernel     - key-major: one workgroup per chunk of kBwdChunk
-//       tokens of one block's list; 4 waves x 32 keys hold their K and V rows
-//       as MFMA operands; per step of 4 tokens (64 query rows of the KV
+//       tokens of one block's list; 8 waves x 16 keys (two waves per SIMD)
+//       hold their K and V rows as MFMA operands; per step of 4 tokens (64
+//       query rows of the KV
 //       group, with their lse and D, staged in a 4-step LDS ring) S = Q K^T,
 //       dP = dO V^T, dS, then
 //       dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T taken by
@@ -549,6 +550,8 @@ constexpr int kKvRows = kKvTok * kGroup;       // 64 query rows per step
 constexpr int kStageBytes = kKvRows * kRowB;   // 16 KiB of Q (or dO) rows
 constexpr int kStageAll = 2 * kStageBytes + 2 * kKvRows * 4;  // Q, dO, lse, D of one step
 constexpr int kStages = 4;                     // LDS ring: steps s+1..s+3 stream in during step s
+constexpr int kKvWaves = 8;                    // waves per workgroup, two per SIMD
+constexpr int kKeyTiles = kBlock / (16 * kKvWaves);  // 16-key tiles per wave (1)
 
 // HBM -> LDS copy of 4 bytes per lane (lane l writes lds_dst + 4l).
 __device__ __forceinline__ void copy_dword_to_lds(const void *src, uint8_t *lds_dst) {
@@ -577,7 +580,7 @@ __device__ __forceinline__ void wait_copies32(int n) {
 __device__ __forceinline__ int swz16(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
 }  // namespace
 
-__global__ __launch_bounds__(256) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(64 * kKvWaves) void bwd_dkdv_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const uint16_t *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ Dsum,
     const DocSpan *__restrict__ docs, const int32_t *__restrict__ blk_off, int ndocs, int nb_max,
@@ -605,10 +608,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
     const int n = lane & 15, grp = lane >> 4;
 
     // this wave's keys kb + 16kt + n as B operands (col = key, k chunk 4ks + grp)
-    const int kb = b * kBlock + 32 * wave;
-    bf16x8 kreg[2][4], vreg[2][4];
+    const int kb = b * kBlock + 16 * kKeyTiles * wave;
+    bf16x8 kreg[kKeyTiles][4], vreg[kKeyTiles][4];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int kt = 0; kt < kKeyTiles; ++kt) {
         const int kp = min(kb + 16 * kt + n, doc.len - 1);
         const size_t row = (size_t(doc.start + kp) * kKvHeads + g) * kDim;
 #pragma unroll
@@ -620,28 +623,29 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
     // use the operands once here, so that the compiler's wait for them sits
     // before the step loop (a wait inside it would also drain the prefetch)
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < kKeyTiles; ++kt)
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) asm volatile("" ::"v"(kreg[kt][ks]), "v"(vreg[kt][ks]));
-    f32x4 dkt[2][8], dvt[2][8];  // [key tile][d tile]: key 16kt + n, d 16dt + 4grp + i
+    f32x4 dkt[kKeyTiles][8], dvt[kKeyTiles][8];  // [key tile][d tile]: key 16kt + n, d 16dt + 4grp + i
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < kKeyTiles; ++kt)
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) dkt[kt][dt] = dvt[kt][dt] = f32x4{};
 
     // Stage s: tokens e0 + 4s .. +3 (past the list end: its last token,
-    // masked).  32 one-KiB copies (16 of Q, 16 of dO rows), 8 per wave;
+    // masked).  32 one-KiB copies (16 of Q, 16 of dO rows), 4 per wave;
     // copy cc fills rows 4cc..4cc+3 = heads 4(cc%4).. of token cc/4.  Wave 0
     // also copies the 4 tokens' lse rows, wave 1 their D rows (64 floats,
     // [token][head]), so that the step loop issues no vector load of its own
     // (the compiler would wait for it, and with it for the whole prefetch).
     const int nsteps = (ne + kKvTok - 1) / kKvTok;
-    const int per_stage = 8 + (wave < 2 ? 1 : 0);
+    constexpr int kCopiesPerWave = 32 / kKvWaves;
+    const int per_stage = kCopiesPerWave + (wave < 2 ? 1 : 0);
     auto issue_stage = [&](int s, int buf) {
         uint8_t *st = smem + buf * kStageAll;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int c = 8 * wave + j;
+        for (int j = 0; j < kCopiesPerWave; ++j) {
+            const int c = kCopiesPerWave * wave + j;
             const int cc = c & 15;
             const int r = 4 * cc + (lane >> 4);
             const int tok = lists[e0 + min(kKvTok * s + (cc >> 2), ne - 1)];
@@ -705,23 +709,23 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
             }
         }
         // S = Q K^T and dP = dO V^T; lane holds key 16kt + n, rows 4grp + i
-        bf16x8 pb[2][2], dsb[2][2];  // [k-step s2 = rt/2][kt]: rows 16rt + 4grp + i at 4(rt%2) + i
+        bf16x8 pb[2][kKeyTiles], dsb[2][kKeyTiles];  // [k-step s2 = rt/2][kt]: rows 16rt + 4grp + i at 4(rt%2) + i
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
-            f32x4 sacc[2] = {f32x4{}, f32x4{}}, pacc[2] = {f32x4{}, f32x4{}};
+            f32x4 sacc[kKeyTiles] = {}, pacc[kKeyTiles] = {};
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 const int off = 16 * rt * kRowB + a_off + (((4 * ks + grp) ^ a_sw) << 4);
                 const bf16x8 qa = __builtin_bit_cast(bf16x8, *(const u32x4 *)(Qs + off));
                 const bf16x8 da = __builtin_bit_cast(bf16x8, *(const u32x4 *)(Ds + off));
 #pragma unroll
-                for (int kt = 0; kt < 2; ++kt) {
+                for (int kt = 0; kt < kKeyTiles; ++kt) {
                     sacc[kt] = mfma_16x16x32(qa, kreg[kt][ks], sacc[kt]);
                     pacc[kt] = mfma_16x16x32(da, vreg[kt][ks], pacc[kt]);
                 }
             }
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
+            for (int kt = 0; kt < kKeyTiles; ++kt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const bool ok = kb + 16 * kt + n <= pos[rt];
@@ -740,7 +744,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
                 const bf16x8 doT = join_tr(read_tr(Ds + o0), read_tr(Ds + o1));
                 const bf16x8 qT = join_tr(read_tr(Qs + o0), read_tr(Qs + o1));
 #pragma unroll
-                for (int kt = 0; kt < 2; ++kt) {
+                for (int kt = 0; kt < kKeyTiles; ++kt) {
                     dvt[kt][dt] = mfma_16x16x32(doT, pb[s2][kt], dvt[kt][dt]);
                     dkt[kt][dt] = mfma_16x16x32(qT, dsb[s2][kt], dkt[kt][dt]);
                 }
@@ -751,7 +755,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
     if (chunk_off[li + 1] - chunk_off[li] == 1) {
         // the block's only chunk: its sums are final, written as bf16
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
+        for (int kt = 0; kt < kKeyTiles; ++kt) {
             const int kp = kb + 16 * kt + n;
             if (kp >= doc.len) continue;
             const size_t row = (size_t(doc.start + kp) * kKvHeads + g) * kDim + 4 * grp;
@@ -772,8 +776,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
     float *pk = part + size_t(ci) * 2 * kBlock * kDim;
     float *pv = pk + kBlock * kDim;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-        const int key = 32 * wave + 16 * kt + n;
+    for (int kt = 0; kt < kKeyTiles; ++kt) {
+        const int key = 16 * kKeyTiles * wave + 16 * kt + n;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
             *(f32x4 *)(pk + key * kDim + 16 * dt + 4 * grp) = dkt[kt][dt] * scale;
@@ -874,7 +878,7 @@ hipError_t launch_bwd_dkdv(const uint16_t *q, const uint16_t *k, const uint16_t 
                            const int32_t *blk_off, int ndocs, const BwdLayout &L, const int32_t *lists,
                            const int32_t *list_off, const int32_t *chunk_off, float scale, float *part,
                            uint16_t *dk, uint16_t *dv, hipStream_t stream) {
-    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(L.max_chunks), dim3(256), size_t(kStages) * kStageAll, stream,
+    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(L.max_chunks), dim3(64 * kKvWaves), size_t(kStages) * kStageAll, stream,
                        q, k, v, dout, lse, Dsum,
                        docs, blk_off, ndocs, L.nb_max, lists, list_off, chunk_off, L.nlists, scale,
                        scale * kLog2e, part, dk, dv);
