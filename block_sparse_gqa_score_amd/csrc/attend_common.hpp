@@ -44,6 +44,14 @@ __device__ __forceinline__ void copy_to_lds(const void *src, uint8_t *lds_dst) {
     asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0) : "memory");
 }
 
+// The same copy from a wave-uniform base (in SGPRs) plus a 32-bit unsigned
+// per-lane byte offset, the instruction's saddr form: the lane's address
+// then costs no 64-bit vector arithmetic.
+__device__ __forceinline__ void copy_to_lds_s(const void *sbase, uint32_t voff, uint8_t *lds_dst) {
+    const uint32_t m0 = (uint32_t)reinterpret_cast<uintptr_t>((lds_void *)lds_dst);
+    asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(m0) : "memory");
+}
+
 // Max over the four 16-lane rows of a wave, for each lane position: each
 // swap of a register with itself returns, at every lane, the lane's own
 // value and that of its partner row (rows r, r^2 for the 32-lane swap;

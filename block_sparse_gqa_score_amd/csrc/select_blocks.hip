@@ -211,15 +211,16 @@ __global__ __launch_bounds__(256, 2) void block_scores_kernel(
     // row before that end, in the document.
     auto issue_block = [&](const Pos &p, int buf) {
         const DocSpan doc = docs[p.d];
-        const int key_end = min(doc.len, (p.j + 1) * kScoreTile);
+        // rows past the tile's last key (only in its diagonal block) repeat that key
+        const int last = min(doc.len, (p.j + 1) * kScoreTile) - 1 - p.b * kBlock;
+        const uint8_t *base = ik + size_t(doc.start + p.b * kBlock) * L::kRowBytes;
 #pragma unroll
         for (int i = 0; i < L::kCopiesPerWave; ++i) {
             const int cp = L::kCopiesPerWave * wave + i;
             const int r = L::kRowsPerCopy * cp + lane / L::kChunks;
             const int chunk = (lane % L::kChunks) ^ sswz<kFp8>(r);
-            const int kp = min(p.b * kBlock + r, key_end - 1);
-            copy_to_lds(ik + size_t(doc.start + kp) * L::kRowBytes + 16 * chunk,
-                        smem + buf * L::kBufBytes + cp * 1024);
+            copy_to_lds_s(base, uint32_t(min(r, last) * L::kRowBytes + 16 * chunk),
+                          smem + buf * L::kBufBytes + cp * 1024);
         }
     };
 
