@@ -418,14 +418,16 @@ __global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(
     }
     for (int i = tid; i < kQRing * 64; i += kQThreads) (&s_flag[0][0])[i] = -1;
     __syncthreads();
-    // The wave's list in one VGPR, entry i in lane i (read with readlane):
-    // its tokens that selected the block (bits 0-1), the block's union index
-    // (bits 2-9) and its id (bits 10-31).
+    // The wave's list entries, packed in place (entry i by lane i): its
+    // tokens that selected the block (bits 0-1), the block's union index
+    // (bits 2-9) and its id (bits 10-31).  The walk reads them from LDS: a
+    // list held in a VGPR was spilled, and each scratch reload's vmcnt wait
+    // drained the copies the wave had issued ahead.
     static_assert(kQMaxUnion <= 256, "list entry fields");
-    uint32_t wl = 0u;
     if (lane < nwb) {
         const int bi = s_wlist[wave][lane];
-        wl = uint32_t((s_umask[bi] >> (2 * wave)) & 3) | (uint32_t(bi) << 2) | (uint32_t(s_ublk[bi]) << 10);
+        s_wlist[wave][lane] =
+            int(uint32_t((s_umask[bi] >> (2 * wave)) & 3) | (uint32_t(bi) << 2) | (uint32_t(s_ublk[bi]) << 10));
     }
 
     // Lane-constant LDS offsets.  Plain reads: M-tile mt row n is key
@@ -478,12 +480,13 @@ __global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(
     // was needed only by waves at or beyond it.
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): operands are in (no copy issued yet)
     for (int kk = 0; kk < nwb; ++kk) {
-        const uint32_t e = __builtin_amdgcn_readlane(wl, kk);
+        const uint32_t e = __builtin_amdgcn_readfirstlane(uint32_t(s_wlist[wave][kk]));
         const int bi = (e >> 2) & 255u;
         const int b = int(e >> 10);
         const bool act[2] = {tok_ok[0] && (e & 1u), tok_ok[1] && ((e >> 1) & 1u)};
         const int nq = bi == nu - 1 ? last_units : kUnitsPerBlock;
-        const int nxt_bi = kk + 1 < nwb ? int((__builtin_amdgcn_readlane(wl, kk + 1) >> 2) & 255u) : -1;
+        const int nxt_bi =
+            kk + 1 < nwb ? int((__builtin_amdgcn_readfirstlane(uint32_t(s_wlist[wave][kk + 1])) >> 2) & 255u) : -1;
         const int keyb = b * kBlock + 8 * grp;
 #pragma unroll 1
         for (int qq = 0; qq < nq; ++qq) {
