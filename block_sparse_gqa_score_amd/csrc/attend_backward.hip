@@ -9,11 +9,13 @@
 //
 // Kernels:
 //   bwd_rowdot_kernel   - D[t][h] = sum_d dO * O in fp32.
-//   bwd_list_kernel     - inverse of q2k: for every (KV head g, document
-//       block) the tokens whose row selects the block, ascending.  A count
-//       pass, a scan (bwd_scan_kernel, also of the chunk counts) and a fill
-//       pass at the scanned offsets; no atomics, so the lists, and every sum
-//       taken over them, are the same on every run.
+//   bwd_hist_kernel, bwd_colscan_kernel, bwd_scan_kernel, bwd_fill_kernel
+//       - inverse of q2k: for every (KV head g, document block) the tokens
+//       whose row selects the block, ascending, in O(T * topk): per-tile
+//       counts, a scan over the tiles and of the list lengths (and chunk
+//       counts), then a fill that ranks a tile's tokens by LDS lane masks;
+//       no atomics on global memory, so the lists, and every sum taken over
+//       them, are the same on every run.
 //   bwd_dq_kernel       - query-major: a workgroup takes 16 tokens of one
 //       query block (8 waves x 2 tokens) and streams the union of their
 //       selected blocks as 32-key units (K rows, V rows) through a 9-slot
@@ -91,77 +93,125 @@ __global__ __launch_bounds__(256) void bwd_rowdot_kernel(const uint16_t *__restr
 // ---------------------------------------------------------------------------
 // Inverse of q2k: per (KV head, document block) the selecting tokens
 // ---------------------------------------------------------------------------
-// Workgroup (Bg, g): document block Bg (blocks of all documents numbered by
-// blk_off), KV head g; list index li = g * nb_max + Bg.  Token at document
-// position p >= 128b selects block b when its row lists b (a token before
-// the block cannot: its candidates stop at its own block).
-// Whether a q2k row of topk entries lists block b (16-byte loads when every
-// row is 16-byte aligned: vec = aligned base and topk % 4 == 0).
-__device__ __forceinline__ bool row_has(const int32_t *__restrict__ r, int topk, int b, bool vec) {
-    bool hit = false;
-    if (vec) {
-        for (int s = 0; s < topk; s += 4) {
-            const u32x4 x = *(const u32x4 *)(r + s);
-            hit |= (int(x[0]) == b) | (int(x[1]) == b) | (int(x[2]) == b) | (int(x[3]) == b);
-        }
-    } else {
-        for (int s = 0; s < topk; ++s) hit |= r[s] == b;
+// List li = g * nb_max + Bg holds, ascending, the tokens whose row for KV
+// head g selects document block Bg (the blocks of all documents numbered by
+// blk_off): the entries b of the row with 0 <= b <= the token's own block,
+// each once, as the attention takes them.  Built in O(T * topk): per tile of
+// 256 tokens a count of each list's tokens (bwd_hist_kernel), a scan over
+// the tiles (bwd_colscan_kernel: each list's tokens in earlier tiles), the
+// lists' offsets (bwd_scan_kernel), and a fill (bwd_fill_kernel) in which a
+// token's rank within its tile comes from 64-bit LDS masks of the lanes
+// that select each block, one mask per wave.  No step depends on timing, so
+// the lists, and every sum taken over them, are the same on every run.
+constexpr int kListTile = 256;  // tokens per tile, one per thread
+constexpr int kListWin = 1024;  // blocks per LDS window
+
+// Token t's counted entries for KV head g as global block numbers
+// (blk_off[d] + b), -1 in the other slots.
+__device__ __forceinline__ void row_blocks(const int32_t *__restrict__ q2k, int topk, int T,
+                                           const DocSpan *__restrict__ docs,
+                                           const int32_t *__restrict__ blk_off, int ndocs, int g, int t,
+                                           int (&bg)[kMaxTopk]) {
+#pragma unroll
+    for (int j = 0; j < kMaxTopk; ++j) bg[j] = -1;
+    if (t >= T) return;
+    int lo = 0, hi = ndocs - 1;  // the document: the last whose start <= t
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (docs[mid].start <= t) lo = mid; else hi = mid - 1;
     }
-    return hit;
+    const int c = (t - docs[lo].start) / kBlock;
+    const int base = blk_off[lo];
+    const int32_t *r = q2k + (size_t(g) * T + t) * topk;
+    int b[kMaxTopk];
+#pragma unroll
+    for (int j = 0; j < kMaxTopk; ++j) b[j] = j < topk ? r[j] : -1;
+#pragma unroll
+    for (int j = 0; j < kMaxTopk; ++j) {
+        bool dup = false;
+#pragma unroll
+        for (int i = 0; i < j; ++i) dup |= b[i] == b[j];
+        if (b[j] >= 0 && b[j] <= c && !dup) bg[j] = base + b[j];
+    }
 }
 
-template <bool kFill>
-__global__ __launch_bounds__(256) void bwd_list_kernel(const int32_t *__restrict__ q2k, int topk, int T,
-                                                       const DocSpan *__restrict__ docs,
-                                                       const int32_t *__restrict__ blk_off, int ndocs,
-                                                       int nb_max, int32_t *__restrict__ cnt,
-                                                       const int32_t *__restrict__ list_off,
-                                                       int32_t *__restrict__ lists) {
-    constexpr int kSub = 4;  // rounds of 256 tokens whose rows are loaded together
-    __shared__ int s_w[kSub][4];
-    const int Bg = blockIdx.x, g = blockIdx.y;
-    const int li = g * nb_max + Bg;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    if (Bg >= blk_off[ndocs]) {
-        if (!kFill && tid == 0) cnt[li] = 0;
-        return;
-    }
-    const int d = prefix_doc(blk_off, ndocs, Bg);
-    const DocSpan doc = docs[d];
-    const int b = Bg - blk_off[d];
-    const int32_t *rows = q2k + size_t(g) * T * topk;
-    int base = kFill ? list_off[li] : 0;
-    const bool vec = (topk & 3) == 0 && (reinterpret_cast<uintptr_t>(q2k) & 15) == 0;
-    for (int p0 = b * kBlock; p0 < doc.len; p0 += 256 * kSub) {
-        bool hit[kSub];
-#pragma unroll
-        for (int j = 0; j < kSub; ++j) {
-            const int p = p0 + 256 * j + tid;
-            hit[j] = p < doc.len && row_has(rows + size_t(doc.start + p) * topk, topk, b, vec);
-        }
-        uint64_t m[kSub];
-#pragma unroll
-        for (int j = 0; j < kSub; ++j) {
-            m[j] = __ballot(hit[j]);
-            if (lane == 0) s_w[j][wave] = __popcll(m[j]);
-        }
+// Workgroup (tile, g): hist[tile][g * nb_max + Bg] = the tile's tokens in list (g, Bg).
+__global__ __launch_bounds__(kListTile) void bwd_hist_kernel(const int32_t *__restrict__ q2k, int topk, int T,
+                                                             const DocSpan *__restrict__ docs,
+                                                             const int32_t *__restrict__ blk_off, int ndocs,
+                                                             int nb_max, int nlists, int32_t *__restrict__ hist) {
+    __shared__ int s_h[kListWin];
+    const int tile = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
+    int bg[kMaxTopk];
+    row_blocks(q2k, topk, T, docs, blk_off, ndocs, g, tile * kListTile + tid, bg);
+    for (int w0 = 0; w0 < nb_max; w0 += kListWin) {
+        for (int i = tid; i < kListWin; i += kListTile) s_h[i] = 0;
         __syncthreads();
 #pragma unroll
-        for (int j = 0; j < kSub; ++j) {
-            int before = 0, all = 0;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const int x = s_w[j][w];
-                before += w < wave ? x : 0;
-                all += x;
-            }
-            if (kFill && hit[j])
-                lists[base + before + __popcll(m[j] & ((1ull << lane) - 1ull))] = doc.start + p0 + 256 * j + tid;
-            base += all;
-        }
-        __syncthreads();  // s_w is rewritten next round
+        for (int j = 0; j < kMaxTopk; ++j)
+            if (bg[j] >= w0 && bg[j] < w0 + kListWin) atomicAdd(&s_h[bg[j] - w0], 1);
+        __syncthreads();
+        for (int i = tid; i < kListWin && w0 + i < nb_max; i += kListTile)
+            hist[size_t(tile) * nlists + g * nb_max + w0 + i] = s_h[i];
+        __syncthreads();
     }
-    if (!kFill && tid == 0) cnt[li] = base;
+}
+
+// Thread li: hist[tile][li] becomes the exclusive prefix over the tiles,
+// cnt[li] the list's length.
+__global__ __launch_bounds__(256) void bwd_colscan_kernel(int32_t *__restrict__ hist, int ntiles, int nlists,
+                                                          int32_t *__restrict__ cnt) {
+    const int li = blockIdx.x * 256 + threadIdx.x;
+    if (li >= nlists) return;
+    constexpr int kBatch = 16;  // loads in flight together
+    int run = 0;
+    for (int t0 = 0; t0 < ntiles; t0 += kBatch) {
+        int x[kBatch];
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) x[i] = t0 + i < ntiles ? hist[size_t(t0 + i) * nlists + li] : 0;
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) {
+            if (t0 + i < ntiles) hist[size_t(t0 + i) * nlists + li] = run;
+            run += x[i];
+        }
+    }
+    cnt[li] = run;
+}
+
+// Workgroup (tile, g): each of the tile's entries written at its list's
+// offset + the tokens of earlier tiles + the earlier tokens of its tile.
+__global__ __launch_bounds__(kListTile) void bwd_fill_kernel(const int32_t *__restrict__ q2k, int topk, int T,
+                                                             const DocSpan *__restrict__ docs,
+                                                             const int32_t *__restrict__ blk_off, int ndocs,
+                                                             int nb_max, int nlists, const int32_t *__restrict__ hist,
+                                                             const int32_t *__restrict__ list_off,
+                                                             int32_t *__restrict__ lists) {
+    constexpr int kWaves = kListTile / 64;
+    __shared__ unsigned long long s_m[kWaves][kListWin];  // lanes of wave w selecting block w0 + x
+    const int tile = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int t = tile * kListTile + tid;
+    int bg[kMaxTopk];
+    row_blocks(q2k, topk, T, docs, blk_off, ndocs, g, t, bg);
+    const unsigned long long below = (1ull << lane) - 1ull;
+    for (int w0 = 0; w0 < nb_max; w0 += kListWin) {
+        for (int i = tid; i < kWaves * kListWin; i += kListTile) (&s_m[0][0])[i] = 0ull;
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kMaxTopk; ++j)
+            if (bg[j] >= w0 && bg[j] < w0 + kListWin) atomicOr(&s_m[wave][bg[j] - w0], 1ull << lane);
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kMaxTopk; ++j) {
+            if (bg[j] < w0 || bg[j] >= w0 + kListWin) continue;
+            const int x = bg[j] - w0;
+            int rank = __popcll(s_m[wave][x] & below);
+            for (int w = 0; w < wave; ++w) rank += __popcll(s_m[w][x]);
+            const int li = g * nb_max + bg[j];
+            lists[list_off[li] + hist[size_t(tile) * nlists + li] + rank] = t;
+        }
+        __syncthreads();
+    }
 }
 
 // Exclusive scans of n list lengths: list_off[0..n] and chunk_off[0..n]
@@ -840,6 +890,7 @@ BwdLayout bwd_layout(int T, int ndocs, int topk) {
     const size_t pairs = size_t(kKvHeads) * size_t(T) * size_t(topk);
     L.max_chunks = int((pairs + kBwdChunk - 1) / kBwdChunk) + L.nlists;
     L.list_entries = pairs;
+    L.ntiles = ceil_div(T, kListTile);
     return L;
 }
 
@@ -852,15 +903,17 @@ hipError_t launch_bwd_rowdot(const uint16_t *o, const uint16_t *dout, int T, flo
 }
 
 hipError_t launch_bwd_lists(const int32_t *q2k, int topk, int T, const DocSpan *docs,
-                            const int32_t *blk_off, int ndocs, const BwdLayout &L, int32_t *cnt,
+                            const int32_t *blk_off, int ndocs, const BwdLayout &L, int32_t *hist, int32_t *cnt,
                             int32_t *list_off, int32_t *chunk_off, int32_t *lists, hipStream_t stream) {
-    const dim3 grid(L.nb_max, kKvHeads);
-    hipLaunchKernelGGL(bwd_list_kernel<false>, grid, dim3(256), 0, stream, q2k, topk, T, docs, blk_off,
-                       ndocs, L.nb_max, cnt, (const int32_t *)nullptr, (int32_t *)nullptr);
+    const dim3 grid(L.ntiles, kKvHeads);
+    hipLaunchKernelGGL(bwd_hist_kernel, grid, dim3(kListTile), 0, stream, q2k, topk, T, docs, blk_off, ndocs,
+                       L.nb_max, L.nlists, hist);
+    hipLaunchKernelGGL(bwd_colscan_kernel, dim3(ceil_div(L.nlists, 256)), dim3(256), 0, stream, hist, L.ntiles,
+                       L.nlists, cnt);
     hipLaunchKernelGGL(bwd_scan_kernel, dim3(1), dim3(1024), 0, stream, (const int32_t *)cnt, L.nlists,
                        list_off, chunk_off);
-    hipLaunchKernelGGL(bwd_list_kernel<true>, grid, dim3(256), 0, stream, q2k, topk, T, docs, blk_off,
-                       ndocs, L.nb_max, (int32_t *)nullptr, (const int32_t *)list_off, lists);
+    hipLaunchKernelGGL(bwd_fill_kernel, grid, dim3(kListTile), 0, stream, q2k, topk, T, docs, blk_off, ndocs,
+                       L.nb_max, L.nlists, (const int32_t *)hist, (const int32_t *)list_off, lists);
     return hipGetLastError();
 }
 

@@ -94,7 +94,7 @@ PrefillWs prefill_layout(int T, int ndocs) {
 }
 
 struct BwdWs {
-    size_t docs, tile_off, blk_off, dsum, cnt, list_off, chunk_off, lists, part, total;
+    size_t docs, tile_off, blk_off, dsum, hist, cnt, list_off, chunk_off, lists, part, total;
     BwdLayout L;
 };
 
@@ -110,6 +110,8 @@ BwdWs backward_layout(int T, int ndocs, int topk) {
     o = align256(o + sizeof(int32_t) * (size_t(ndocs) + 1));
     w.dsum = o;
     o = align256(o + sizeof(float) * size_t(T) * kHeads);
+    w.hist = o;
+    o = align256(o + sizeof(int32_t) * size_t(w.L.ntiles) * size_t(w.L.nlists));
     w.cnt = o;
     o = align256(o + sizeof(int32_t) * size_t(w.L.nlists));
     w.list_off = o;
@@ -342,6 +344,7 @@ msa_status msa_sparse_attend_prefill_backward(
     int32_t *tile_off = (int32_t *)(base + ws.tile_off);
     int32_t *blk_off = (int32_t *)(base + ws.blk_off);
     float *dsum = (float *)(base + ws.dsum);
+    int32_t *hist = (int32_t *)(base + ws.hist);
     int32_t *cnt = (int32_t *)(base + ws.cnt);
     int32_t *list_off = (int32_t *)(base + ws.list_off);
     int32_t *chunk_off = (int32_t *)(base + ws.chunk_off);
@@ -356,7 +359,7 @@ msa_status msa_sparse_attend_prefill_backward(
     e = launch_bwd_rowdot(out, dout, total_tokens, dsum, s);
     if (e != hipSuccess) return hip_fail(e, "bwd_rowdot");
     tm.mark(s, "bwd_lists");
-    e = launch_bwd_lists(q2k, topk, total_tokens, docs, blk_off, num_docs, ws.L, cnt, list_off, chunk_off,
+    e = launch_bwd_lists(q2k, topk, total_tokens, docs, blk_off, num_docs, ws.L, hist, cnt, list_off, chunk_off,
                          lists, s);
     if (e != hipSuccess) return hip_fail(e, "bwd_lists");
     tm.mark(s, "bwd_dq");

@@ -72,6 +72,9 @@ CASES = [
     ("ragged_docs", [1, 127, 129, 300, 700], 3, 1, 1, "oracle"),
     ("dense_topk_ge_nb", [600, 257], 5, 0, 1, "dense"),
     ("random_rows", [130, 300, 1, 517], 6, 0, 1, "random"),
+    # 1051 document blocks: the list build's block windows (1024 blocks) come twice
+    ("many_docs_two_windows", [300, 1, 2, 129] + [1 + i % 3 for i in range(1040)] + [260, 45], 5, 0, 1,
+     "random"),
 ]
 
 
