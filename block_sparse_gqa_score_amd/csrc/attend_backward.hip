@@ -280,14 +280,13 @@ struct QUnitIds {
 };
 __device__ const QUnitIds kQUnitIds = QUnitIds();
 
-// Row r of a 32-row half, 16-byte chunk c (d 8c..8c+7), sits at chunk
-// position c ^ swz32(r).  The 16 rows one plain operand read touches,
-// 8a + 4mt + e (a, e < 4), map to 16 distinct positions, and the 4 rows
-// 8a + 4h + e (e < 4) of one transposing read to 4 distinct position pairs.
-// (A swizzle without conflicts between a transposing read's two 16-lane
-// groups exists, but its extra arithmetic spilled registers in this kernel
-// and measured no faster.)
-__device__ __forceinline__ int swz32(int r) { return ((r & 3) << 2) | ((r >> 3) & 3); }
+// Row r = 8a + 4m + e (a, e < 4) of a 32-row half, 16-byte chunk c
+// (d 8c..8c+7), sits at chunk position c ^ swz32(r), swz32 = 4e + 2(a%2) +
+// a/2.  The 16 rows one plain operand read touches (a, e < 4, m fixed) map
+// to 16 distinct positions, and the 8 rows of a transposing read's 32-lane
+// half (a in {0, 1} or {2, 3}, e < 4, m = h) to 8 distinct position pairs
+// (swz32 / 2 = 2e + a%2 differs).
+__device__ __forceinline__ int swz32(int r) { return ((r & 3) << 2) | ((r >> 2) & 2) | ((r >> 4) & 1); }
 
 struct DqState {
     bf16x8 qb[2][4];   // Q^T operand of each token (column n = head n)
