@@ -19,14 +19,16 @@
 //       tiles); 8 waves, two per SIMD, each owning 3 token slots x 16 heads
 //       (tile token i is slot i/8 of wave i%8): their Q^T operands stay in
 //       VGPRs and their O^T accumulators in AGPRs.  The workgroup streams the
-//       union of its tokens' selected blocks, ascending, as 32-key units (K
-//       rows 8 KiB + V^T rows 8 KiB) HBM -> LDS by global_load_lds_dwordx4
-//       through a 9-slot ring, with no workgroup barrier: every unit has an
+//       union of its tokens' selected blocks as 32-key units (K rows 8 KiB +
+//       V^T rows 8 KiB) HBM -> LDS by global_load_lds_dwordx4 through a
+//       9-slot ring, unit-major (unit 0 of every union block, ascending, then
+//       unit 1, ...: any 9 consecutive units span 9 blocks, which most of the
+//       waves need), with no workgroup barrier: every unit has an
 //       LDS state word (claimed bit, count of the waves that still need it)
 //       and every slot a flag, the id of the unit whose copies last landed
 //       there (a 17th copy, of the id, issued after the unit's 16: a wave's
 //       copies land in issue order).  Each wave walks only the units its
-//       tokens need.  A wave that needs a unit nobody has copied yet claims
+//       tokens need, in ring order, from a visit list built per tile.  A wave that needs a unit nobody has copied yet claims
 //       it and issues its copies once every wave needing the unit 9 places
 //       earlier is done with that slot; before computing a unit it claims its
 //       next one the same way, so the copies land during the compute.  A unit
@@ -427,14 +429,27 @@ __global__ __launch_bounds__(kThreads) void attend_prefill_kernel(
     const int ns = nu;
     const int last_units = (ns > 0 && ublk[ns - 1] == c) ? q_hi + 1 : kUnitsPerBlock;
     // unit counts: the waves whose tokens selected the unit's block
-    for (int u = tid; u < kUnitsPerBlock * ns; u += kThreads) {
-        const int bi = u / kUnitsPerBlock;
+    // Ring order: unit-major, unit q of every union block, then unit q + 1.
+    // A window of kRing consecutive units then spans kRing blocks, needed by
+    // most of the waves, instead of the two or three blocks of block-major
+    // order, which only some of them need (in block-major order, waiting for
+    // a slot took 40% of the waves' time).  Only existing units are numbered (the diagonal block,
+    // last, stops at unit last_units - 1: passes q < last_units hold ns units,
+    // later ones ns - 1), so a slot's previous occupant is always the unit
+    // kRing places earlier.
+    const int nunits = kUnitsPerBlock * (ns - 1) + last_units;
+    auto unit_id = [&](int q, int bi) { return q * ns - max(0, q - last_units) + bi; };
+    auto unit_block = [&](int u) {  // the unit's union block index
+        const int u1 = u - last_units * ns;
+        return u1 < 0 ? u % ns : u1 % max(ns - 1, 1);
+    };
+    for (int u = tid; u < nunits; u += kThreads) {
+        const int bi = unit_block(u);
         const uint32_t m = umask[bi];
         int nw = 0;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) nw += ((m >> (kBitsPerWave * w)) & ((1u << kBitsPerWave) - 1u)) ? 1 : 0;
-        const bool exists = bi < ns - 1 || u % kUnitsPerBlock < last_units;
-        s_unit[u] = exists ? uint32_t(nw) : 0u;
+        s_unit[u] = uint32_t(nw);
     }
     // each wave lists the ring blocks its tokens selected, ascending
     int nwb = 0;
@@ -477,9 +492,10 @@ __global__ __launch_bounds__(kThreads) void attend_prefill_kernel(
     // V^T rows 16(i-8)..+15 (lane l: row 16(i-8) + l/4, chunk
     // (l%4) ^ vswz(row)).  Both come from the per-unit copies (8 KiB per
     // unit and head in either), whose rows past the document end are zero.
-    auto issue_unit = [&](int u) {
-        const int ub = __builtin_amdgcn_readfirstlane(s_sblk[u / kUnitsPerBlock]);
-        const size_t unit = size_t(uoff + ub * kUnitsPerBlock + u % kUnitsPerBlock) * kKvHeads + g;
+    // (ub: the unit's block id, q: its 32-key unit within the block, both
+    // known to the caller)
+    auto issue_unit = [&](int u, int ub, int q) {
+        const size_t unit = size_t(uoff + ub * kUnitsPerBlock + q) * kKvHeads + g;
         const uint16_t *ksrc = ku + unit * (kAttnUnit * kDim);
         const uint16_t *vsrc = vt + unit * (kAttnUnit * kDim);
         uint8_t *slot = smem + (u % kRing) * kUnitBytes;
@@ -515,11 +531,11 @@ __global__ __launch_bounds__(kThreads) void attend_prefill_kernel(
     };
     // Wait until unit u has landed; claim and copy it when nobody has and its
     // slot is free.  Every wait is bounded (kSpinLimit polls).
-    auto acquire = [&](int u) {
+    auto acquire = [&](int u, int ub, int q) {
         for (int spin = 0; spin < kSpinLimit; ++spin) {
             if (landed(u)) return;
             const uint32_t wd = unit_word(u);
-            if (!(wd & kClaimed) && fillable(u) && try_claim(u)) issue_unit(u);
+            if (!(wd & kClaimed) && fillable(u) && try_claim(u)) issue_unit(u, ub, q);
             __builtin_amdgcn_s_sleep(1);
         }
     };
@@ -527,54 +543,88 @@ __global__ __launch_bounds__(kThreads) void attend_prefill_kernel(
     // ---- the wave's walk over its needed units, in ring order.  Before
     // computing a unit it claims the next one it needs, when that unit's slot
     // is free, and issues its copies, which land during the compute.
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): query operands are in (no copy issued yet)
-    for (int k = 0; k < nwb; ++k) {
-        // keep every O^T accumulator in AGPRs across the loop (the register
+    // One visit: unit u (unit qq of list entry e's block) computed, with the
+    // next unit v (vq of block vub) claimed ahead; v = -1: none.
+    auto visit = [&](int u, uint32_t e, int qq, int v, int vub, int vq) {
+        // keep every O^T accumulator in AGPRs across the walk (the register
         // allocator would otherwise carry some of them in VGPRs, which the
         // query operands and the working set need)
 #pragma unroll
         for (int t = 0; t < kTpw; ++t)
 #pragma unroll
             for (int dt = 0; dt < 8; ++dt) asm volatile("" : "+a"(st.acc_o[t][dt]));
-        const uint32_t e = __builtin_amdgcn_readlane(wl, k);
-        const int bi = (e >> 3) & 511u;
         const uint32_t act = e & 7u;
-        const int nq = bi == ns - 1 ? last_units : kUnitsPerBlock;
         const bool own = int(e >> 12) == c;
-        const int nxt_bi = k + 1 < nwb ? int((__builtin_amdgcn_readlane(wl, k + 1) >> 3) & 511u) : -1;
-#pragma unroll 1
-        for (int qq = 0; qq < nq; ++qq) {
-            const int u = kUnitsPerBlock * bi + qq;
-            const int v = qq + 1 < nq ? u + 1 : (nxt_bi >= 0 ? kUnitsPerBlock * nxt_bi : -1);
-            // One LDS round trip: u's flag, v's state and the state of the unit
-            // before v in its slot (v = -1: none; below kRing: the slot is new).
-            const int vs = v >= 0 ? v : u;
-            const int vp = v >= kRing ? v - kRing : u;
-            const int fl = __hip_atomic_load(&s_flag[u % kRing][lane], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
-            const uint32_t wv = __hip_atomic_load(&s_unit[vs], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-            const uint32_t wp = __hip_atomic_load(&s_unit[vp], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-            if (__builtin_amdgcn_readfirstlane(fl) != u) acquire(u);
-            // claim v ahead when its slot is free: a unit that only this wave
-            // needs (count 1, nobody has read it) is marked without a returning
-            // atomic; a shared one goes to whichever wave claims it first
-            const uint32_t wvs = __builtin_amdgcn_readfirstlane(wv);
-            if (v >= 0 && !(wvs & kClaimed) && (v < kRing || (__builtin_amdgcn_readfirstlane(wp) & 0xFFu) == 0u)) {
-                if ((wvs & 0xFFu) == 1u) {
-                    if (lane == 0) __hip_atomic_fetch_or(&s_unit[v], kClaimed, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-                    issue_unit(v);
-                } else if (try_claim(v)) {
-                    issue_unit(v);
-                }
+        // One LDS round trip: u's flag, v's state and the state of the unit
+        // before v in its slot (v = -1: none; below kRing: the slot is new).
+        const int vs = v >= 0 ? v : u;
+        const int vp = v >= kRing ? v - kRing : u;
+        const int fl = __hip_atomic_load(&s_flag[u % kRing][lane], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        const uint32_t wv = __hip_atomic_load(&s_unit[vs], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        const uint32_t wp = __hip_atomic_load(&s_unit[vp], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (__builtin_amdgcn_readfirstlane(fl) != u) acquire(u, int(e >> 12), qq);
+        // claim v ahead when its slot is free: a unit that only this wave
+        // needs (count 1, nobody has read it) is marked without a returning
+        // atomic; a shared one goes to whichever wave claims it first
+        const uint32_t wvs = __builtin_amdgcn_readfirstlane(wv);
+        if (v >= 0 && !(wvs & kClaimed) && (v < kRing || (__builtin_amdgcn_readfirstlane(wp) & 0xFFu) == 0u)) {
+            if ((wvs & 0xFFu) == 1u) {
+                if (lane == 0) __hip_atomic_fetch_or(&s_unit[v], kClaimed, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                issue_unit(v, vub, vq);
+            } else if (try_claim(v)) {
+                issue_unit(v, vub, vq);
             }
-            const uint8_t *Ku = smem + (u % kRing) * kUnitBytes;
-            // the tile's own units of the query block: keys past each token drop
-            if (act)
-                ring_unit(st, Ku, act, k_row_off, v_off, n, grp, own && qq >= q_lo, kAttnUnit * qq + 8 * grp,
-                          pos0 - c * kBlock, scale_log2);
-            // done reading unit u: its slot may be refilled once every wave needing it is done
-            if (lane == 0)
-                __hip_atomic_fetch_sub(&s_unit[u], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
         }
+        const uint8_t *Ku = smem + (u % kRing) * kUnitBytes;
+        // the tile's own units of the query block: keys past each token drop
+        if (act)
+            ring_unit(st, Ku, act, k_row_off, v_off, n, grp, own && qq >= q_lo, kAttnUnit * qq + 8 * grp,
+                      pos0 - c * kBlock, scale_log2);
+        // done reading unit u: its slot may be refilled once every wave needing it is done
+        if (lane == 0) __hip_atomic_fetch_sub(&s_unit[u], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    };
+    // The wave's visits in ring order (ascending unit number), packed
+    // u | k << 11 | q << 17 (unit q of list entry k's block), visit i in lane
+    // i % 64 of vis0, vis1, vis2 (i / 64).  Pass q holds every entry except a
+    // diagonal last one past its last unit, so (k, q) is visit
+    // q nwb - max(0, q - lw) + k.  Written through LDS scratch at the start of
+    // the ring (free until the walk), one KiB per wave.
+    static_assert(kTpw * kMaxTopk * kUnitsPerBlock <= 192 && kUnitsPerBlock * kMaxUnion <= 2048, "visit fields");
+    auto entry = [&](int k) { return __builtin_amdgcn_readlane(wl, k); };
+    const int lw = nwb > 0 && int((entry(nwb - 1) >> 3) & 511u) == ns - 1 ? last_units : kUnitsPerBlock;
+    const int nvis = nwb > 0 ? kUnitsPerBlock * (nwb - 1) + lw : 0;
+    uint32_t vis0, vis1, vis2;  // three named registers (an array indexed at run time would go to scratch)
+    {
+        uint32_t *svis = (uint32_t *)(smem + wave * 1024);
+        if (lane < nwb) {
+            const int bi = (wl >> 3) & 511u;
+            const int nq = lane == nwb - 1 ? lw : kUnitsPerBlock;
+            for (int q = 0; q < nq; ++q) {
+                const int i = q * nwb - max(0, q - lw) + lane;
+                svis[i] = uint32_t(unit_id(q, bi)) | (uint32_t(lane) << 11) | (uint32_t(q) << 17);
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+        vis0 = svis[lane];
+        vis1 = svis[64 + lane];
+        vis2 = svis[128 + lane];
+    }
+    __syncthreads();  // every wave has its visits before any copy lands in the ring
+    auto vis_at = [&](int i) {
+        const uint32_t r = i < 64 ? vis0 : i < 128 ? vis1 : vis2;
+        return __builtin_amdgcn_readlane(r, i & 63);
+    };
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): query operands are in (no copy issued yet)
+    for (int i = 0; i < nvis; ++i) {
+        const uint32_t x = vis_at(i);
+        int v = -1, vub = 0, vq = 0;
+        if (i + 1 < nvis) {
+            const uint32_t y = vis_at(i + 1);
+            v = int(y & 2047u);
+            vub = int(entry((y >> 11) & 63u) >> 12);
+            vq = int(y >> 17);
+        }
+        visit(int(x & 2047u), entry((x >> 11) & 63u), int(x >> 17), v, vub, vq);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // every copy this wave issued has landed
 
