@@ -358,11 +358,14 @@ __global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
     constexpr int kEntries = kQTok * kMaxTopk;
     static_assert(kQThreads >= kEntries, "one thread per (token, slot) pair");
-    __shared__ int s_id[kEntries];
-    __shared__ int s_first[kEntries];
-    __shared__ int s_mask[kEntries];
-    __shared__ int s_ublk[kEntries];
-    __shared__ int s_umask[kEntries];
+    // The union tables (s_id, s_first, s_mask, s_ublk, s_umask) are dead once
+    // the walk starts; their space then holds the waves' visit lists.
+    constexpr int kVisits = kUnitsPerBlock * 2 * kMaxTopk;  // visits of a wave at most
+    static_assert(kQWaves * kVisits <= 5 * kEntries, "visit lists fit the union tables");
+    __shared__ int s_tab[5 * kEntries];
+    int *const s_id = s_tab, *const s_first = s_tab + kEntries, *const s_mask = s_tab + 2 * kEntries;
+    int *const s_ublk = s_tab + 3 * kEntries, *const s_umask = s_tab + 4 * kEntries;
+    uint32_t *const s_vis = reinterpret_cast<uint32_t *>(s_tab);  // [kQWaves][kVisits]
     __shared__ int s_nu;
     __shared__ uint32_t s_unit[kQMaxUnits];     // per ring unit: claimed bit | waves still to read it
     __shared__ int s_wlist[kQWaves][2 * kMaxTopk];  // per wave: the union blocks it needs, ascending
@@ -420,27 +423,34 @@ __global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(
                               s_ublk, s_umask, &s_nu);
     const int last_units =
         (nu > 0 && s_ublk[nu - 1] == c) ? (p_last - c * kBlock) / kAttnUnit + 1 : kUnitsPerBlock;
+    // Ring order, unit-major: unit 0 of every union block (ascending), then
+    // unit 1, and so on.  Only existing units are numbered: the query's own
+    // block, last in the union, stops at the unit of the tile's last token.
+    // Any kQRing consecutive units then span kQRing blocks, most of which
+    // several waves need; in block-major order a window spans two or three
+    // blocks that only some waves need, and the others wait for ring slots.
+    const int nunits = kUnitsPerBlock * (nu - 1) + last_units;
+    auto unit_id = [&](int qq, int bi) { return qq * nu - max(0, qq - last_units) + bi; };
 
     // Unit copies, all 16 issued by the wave that claims the unit: copy
-    // i < 8 fills K rows 4i..4i+3, copy i >= 8 V rows 4(i-8)..+3 (lane l:
-    // row 4i' + l/16, position l%16, i.e. chunk (l%16) ^ swz32(row)).  Rows
-    // past p_last re-read row p_last.  A 17th copy puts the unit's id into
+    // pair i fills K rows and V rows 4i..4i+3 (lane l: row 4i + l/16,
+    // position l%16, i.e. chunk (l%16) ^ swz32(row)), from the unit's first
+    // row in scalar registers and a 32-bit lane offset.  Rows past p_last
+    // re-read row p_last.  A 17th copy puts the unit's id into
     // the slot's flag: a wave's copies land in issue order, so the flag shows
     // the rows landed.
-    auto issue_copy = [&](int vu, int ub, int i) {
-        const int qq = vu & 3;
+    auto issue_unit = [&](int vu, int ub, int qq) {
         uint8_t *slot = smem + (vu % kQRing) * kQUnitBytes;
-        const int ii = i & 7;
-        const int r = 4 * ii + (lane >> 4);
-        const int ch = (lane & 15) ^ swz32(r);
-        const int kp = min(ub * kBlock + qq * kAttnUnit + r, p_last);
-        const uint16_t *src = (i < 8 ? k : v) + (size_t(doc.start + kp) * kKvHeads + g) * kDim + 8 * ch;
-        copy_to_lds(src, slot + (i < 8 ? 0 : kHalfBytes) + ii * 1024);
-    };
-    auto issue_unit = [&](int vu) {
-        const int ub = __builtin_amdgcn_readfirstlane(s_ublk[vu >> 2]);
+        const int key0 = ub * kBlock + qq * kAttnUnit;
+        const size_t row0 = (size_t(doc.start + key0) * kKvHeads + g) * kDim;
+        const int lim = p_last - key0;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) issue_copy(vu, ub, i);
+        for (int ii = 0; ii < 8; ++ii) {
+            const int r = 4 * ii + (lane >> 4);
+            const uint32_t voff = uint32_t(min(r, lim) * (kKvHeads * kRowB) + (((lane & 15) ^ swz32(r)) << 4));
+            copy_to_lds_s(k + row0, voff, slot + ii * 1024);
+            copy_to_lds_s(v + row0, voff, slot + kHalfBytes + ii * 1024);
+        }
         const uint32_t m0 = (uint32_t)reinterpret_cast<uintptr_t>((lds_void *)&s_flag[vu % kQRing][0]);
         asm volatile("global_load_lds_dword %0, off" ::"v"(&kQUnitIds.v[vu]), "{m0}"(m0) : "memory");
     };
@@ -448,14 +458,14 @@ __global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(
     // Unit counts (the waves whose tokens selected the unit's block; units of
     // the query's own block past the tile's last token do not exist) and each
     // wave's list of the blocks it needs, ascending.
-    for (int u = tid; u < kUnitsPerBlock * nu; u += kQThreads) {
-        const int bi = u / kUnitsPerBlock;
+    for (int u = tid; u < nunits; u += kQThreads) {
+        const int u1 = u - last_units * nu;
+        const int bi = u1 < 0 ? u % nu : u1 % max(nu - 1, 1);
         const int m = s_umask[bi];
         int nw = 0;
 #pragma unroll
         for (int w = 0; w < kQWaves; ++w) nw += ((m >> (2 * w)) & 3) ? 1 : 0;
-        const bool exists = bi < nu - 1 || u % kUnitsPerBlock < last_units;
-        s_unit[u] = exists ? uint32_t(nw) : 0u;
+        s_unit[u] = uint32_t(nw);
     }
     int nwb = 0;
     for (int u0 = 0; u0 < nu; u0 += 64) {
@@ -467,16 +477,26 @@ __global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(
     }
     for (int i = tid; i < kQRing * 64; i += kQThreads) (&s_flag[0][0])[i] = -1;
     __syncthreads();
-    // The wave's list entries, packed in place (entry i by lane i): its
-    // tokens that selected the block (bits 0-1), the block's union index
-    // (bits 2-9) and its id (bits 10-31).  The walk reads them from LDS: a
-    // list held in a VGPR was spilled, and each scratch reload's vmcnt wait
-    // drained the copies the wave had issued ahead.
-    static_assert(kQMaxUnion <= 256, "list entry fields");
+    // The wave's visits in ring order (lane k holds its k-th list block, for
+    // each of the block's units): the unit's id (bits 0-9), its index in the
+    // block (bits 10-11), the wave's tokens that selected the block (bits
+    // 12-13) and the block's id (bits 14-31).  The walk reads them from LDS
+    // one visit ahead: a list held in VGPRs was spilled, and each scratch
+    // reload's vmcnt wait drained the copies the wave had issued ahead.
+    static_assert(kQMaxUnits <= 1024 && kBwdMaxTokens / kBlock <= (1 << 18), "visit entry fields");
+    const int lw = (nwb > 0 && s_wlist[wave][nwb - 1] == nu - 1) ? last_units : kUnitsPerBlock;
+    const int nvis = nwb > 0 ? kUnitsPerBlock * (nwb - 1) + lw : 0;
+    int bi = 0;
+    uint32_t e = 0u;
     if (lane < nwb) {
-        const int bi = s_wlist[wave][lane];
-        s_wlist[wave][lane] =
-            int(uint32_t((s_umask[bi] >> (2 * wave)) & 3) | (uint32_t(bi) << 2) | (uint32_t(s_ublk[bi]) << 10));
+        bi = s_wlist[wave][lane];
+        e = uint32_t((s_umask[bi] >> (2 * wave)) & 3) << 12 | uint32_t(s_ublk[bi]) << 14;
+    }
+    __syncthreads();  // every wave has read the union tables
+    if (lane < nwb) {
+        const int nq = lane == nwb - 1 ? lw : kUnitsPerBlock;
+        for (int qq = 0; qq < nq; ++qq)
+            s_vis[wave * kVisits + qq * nwb - max(0, qq - lw) + lane] = uint32_t(unit_id(qq, bi)) | uint32_t(qq) << 10 | e;
     }
 
     // Lane-constant LDS offsets.  Plain reads: M-tile mt row n is key
@@ -513,69 +533,65 @@ __global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(
     };
     // Wait until unit u has landed; claim and copy it when nobody has and its
     // slot is free.  Every wait is bounded (kQSpinLimit polls).
-    auto acquire = [&](int u) {
+    auto acquire = [&](int u, int ub, int qq) {
         for (int spin = 0; spin < kQSpinLimit; ++spin) {
             if (landed(u)) return;
             const uint32_t wd = unit_word(u);
-            if (!(wd & kQClaimed) && fillable(u) && try_claim(u)) issue_unit(u);
+            if (!(wd & kQClaimed) && fillable(u) && try_claim(u)) issue_unit(u, ub, qq);
             __builtin_amdgcn_s_sleep(1);
         }
     };
 
-    // The wave's walk over its needed units, in union order.  Before computing
-    // a unit it claims the next one it needs, when that unit's slot is free,
+    // The wave's walk over its visits, in ring order.  Before computing a
+    // unit it claims the next one it needs, when that unit's slot is free,
     // and issues its copies, which land during the compute; the slowest wave
     // can always claim its next unit, since every unit kQRing places earlier
     // was needed only by waves at or beyond it.
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): operands are in (no copy issued yet)
-    for (int kk = 0; kk < nwb; ++kk) {
-        const uint32_t e = __builtin_amdgcn_readfirstlane(uint32_t(s_wlist[wave][kk]));
-        const int bi = (e >> 2) & 255u;
-        const int b = int(e >> 10);
-        const bool act[2] = {tok_ok[0] && (e & 1u), tok_ok[1] && ((e >> 1) & 1u)};
-        const int nq = bi == nu - 1 ? last_units : kUnitsPerBlock;
-        const int nxt_bi =
-            kk + 1 < nwb ? int((__builtin_amdgcn_readfirstlane(uint32_t(s_wlist[wave][kk + 1])) >> 2) & 255u) : -1;
-        const int keyb = b * kBlock + 8 * grp;
+    uint32_t nx = nvis > 0 ? __builtin_amdgcn_readfirstlane(s_vis[wave * kVisits]) : 0u;
 #pragma unroll 1
-        for (int qq = 0; qq < nq; ++qq) {
-            const int u = kUnitsPerBlock * bi + qq;
-            const int vn = qq + 1 < nq ? u + 1 : (nxt_bi >= 0 ? kUnitsPerBlock * nxt_bi : -1);
-            // One LDS round trip: u's flag, the next unit's state and the
-            // state of the unit before it in its slot.
-            const int vs = vn >= 0 ? vn : u;
-            const int vp = vn >= kQRing ? vn - kQRing : u;
-            const int fl = __hip_atomic_load(&s_flag[u % kQRing][lane], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
-            const uint32_t wv = __hip_atomic_load(&s_unit[vs], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-            const uint32_t wp = __hip_atomic_load(&s_unit[vp], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-            if (__builtin_amdgcn_readfirstlane(fl) != u) acquire(u);
-            // claim the next unit ahead (a unit only this wave needs is marked
-            // with a non-returning atomic)
-            const uint32_t wvs = __builtin_amdgcn_readfirstlane(wv);
-            if (vn >= 0 && !(wvs & kQClaimed) && (vn < kQRing || (__builtin_amdgcn_readfirstlane(wp) & 0xFFu) == 0u)) {
-                if ((wvs & 0xFFu) == 1u) {
-                    if (lane == 0) __hip_atomic_fetch_or(&s_unit[vn], kQClaimed, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-                    issue_unit(vn);
-                } else if (try_claim(vn)) {
-                    issue_unit(vn);
-                }
+    for (int i = 0; i < nvis; ++i) {
+        const uint32_t x = nx;
+        const int u = x & 1023u, qq = (x >> 10) & 3u, b = int(x >> 14);
+        const bool act[2] = {tok_ok[0] && ((x >> 12) & 1u), tok_ok[1] && ((x >> 13) & 1u)};
+        // One LDS round trip: u's flag, the next visit, the next unit's
+        // state and the state of the unit before it in its slot.
+        nx = i + 1 < nvis ? __builtin_amdgcn_readfirstlane(s_vis[wave * kVisits + i + 1]) : 0u;
+        const int vn = i + 1 < nvis ? int(nx & 1023u) : -1;
+        const int vs = vn >= 0 ? vn : u;
+        const int vp = vn >= kQRing ? vn - kQRing : u;
+        const int fl = __hip_atomic_load(&s_flag[u % kQRing][lane], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        const uint32_t wv = __hip_atomic_load(&s_unit[vs], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        const uint32_t wp = __hip_atomic_load(&s_unit[vp], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (__builtin_amdgcn_readfirstlane(fl) != u) acquire(u, b, qq);
+        // claim the next unit ahead (a unit only this wave needs is marked
+        // with a non-returning atomic)
+        const uint32_t wvs = __builtin_amdgcn_readfirstlane(wv);
+        if (vn >= 0 && !(wvs & kQClaimed) && (vn < kQRing || (__builtin_amdgcn_readfirstlane(wp) & 0xFFu) == 0u)) {
+            const int nb = int(nx >> 14), nqq = (nx >> 10) & 3u;
+            if ((wvs & 0xFFu) == 1u) {
+                if (lane == 0) __hip_atomic_fetch_or(&s_unit[vn], kQClaimed, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                issue_unit(vn, nb, nqq);
+            } else if (try_claim(vn)) {
+                issue_unit(vn, nb, nqq);
             }
-            const uint8_t *Ku = smem + (u % kQRing) * kQUnitBytes;
-            if (b == c)
-                dq_unit<true, true, true>(st, Ku, qq, k_row_off, nsw, grp, tr_row, tr_x, tr_lo, keyb, act, my_p,
-                                          scale_log2);
-            else if (act[0] && act[1])
-                dq_unit<true, true, false>(st, Ku, qq, k_row_off, nsw, grp, tr_row, tr_x, tr_lo, keyb, act, my_p,
-                                           scale_log2);
-            else if (act[0])
-                dq_unit<true, false, false>(st, Ku, qq, k_row_off, nsw, grp, tr_row, tr_x, tr_lo, keyb, act, my_p,
-                                            scale_log2);
-            else if (act[1])
-                dq_unit<false, true, false>(st, Ku, qq, k_row_off, nsw, grp, tr_row, tr_x, tr_lo, keyb, act, my_p,
-                                            scale_log2);
-            // done reading unit u
-            if (lane == 0) __hip_atomic_fetch_sub(&s_unit[u], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
         }
+        const int keyb = b * kBlock + 8 * grp;
+        const uint8_t *Ku = smem + (u % kQRing) * kQUnitBytes;
+        if (b == c)
+            dq_unit<true, true, true>(st, Ku, qq, k_row_off, nsw, grp, tr_row, tr_x, tr_lo, keyb, act, my_p,
+                                      scale_log2);
+        else if (act[0] && act[1])
+            dq_unit<true, true, false>(st, Ku, qq, k_row_off, nsw, grp, tr_row, tr_x, tr_lo, keyb, act, my_p,
+                                       scale_log2);
+        else if (act[0])
+            dq_unit<true, false, false>(st, Ku, qq, k_row_off, nsw, grp, tr_row, tr_x, tr_lo, keyb, act, my_p,
+                                        scale_log2);
+        else if (act[1])
+            dq_unit<false, true, false>(st, Ku, qq, k_row_off, nsw, grp, tr_row, tr_x, tr_lo, keyb, act, my_p,
+                                        scale_log2);
+        // done reading unit u
+        if (lane == 0) __hip_atomic_fetch_sub(&s_unit[u], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // every copy this wave issued has landed
 
@@ -923,6 +939,8 @@ hipError_t launch_bwd_dq(const uint16_t *q, const uint16_t *k, const uint16_t *v
     const int max_tiles = ceil_div(T, kQTok) + ndocs;
     const int grid = 8 * 8 * ceil_div(max_tiles, 16);
     const size_t lds = size_t(kQRing) * kQUnitBytes;
+    static const bool fits = lds_fits(reinterpret_cast<const void *>(bwd_dq_kernel), lds);
+    if (!fits) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(bwd_dq_kernel, dim3(grid), dim3(kQThreads), lds, stream, q, k, v, dout, lse, Dsum,
                        q2k, topk, docs, tile_off, ndocs, T, scale, scale * kLog2e, dq);
     return hipGetLastError();

@@ -677,6 +677,8 @@ hipError_t launch_attend_prefill(const uint16_t *q, const uint16_t *vt,
     // 8 XCDs x slots; an XCD pair serves 2 groups of 5 tiles per 5 slots
     const int grid = 8 * kTilesPerBlock * ceil_div(max_tiles, 2 * kTilesPerBlock);
     const size_t lds = size_t(kRing) * kUnitBytes;
+    static const bool fits = lds_fits(reinterpret_cast<const void *>(attend_prefill_kernel), lds);
+    if (!fits) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(attend_prefill_kernel, dim3(grid), dim3(kThreads), lds, stream, q,
                        vt + unit_elems(T, ndocs), vt, q2k, topk, docs, tile_off, unit_off, ndocs, T,
                        scale * kLog2e, out, lse);

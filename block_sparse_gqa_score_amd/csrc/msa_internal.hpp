@@ -19,6 +19,15 @@ constexpr int kAttnUnit = 32;    // keys per prefill-attention pipeline unit
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// LDS of one workgroup on gfx950.  A kernel's static LDS plus the dynamic
+// size it is launched with must fit: the queue rejects a larger dispatch
+// (and aborts) instead of failing the launch call.
+constexpr size_t kCuLdsBytes = 160 * 1024;
+inline bool lds_fits(const void *kernel, size_t dynamic_bytes) {
+    hipFuncAttributes a{};
+    return hipFuncGetAttributes(&a, kernel) == hipSuccess && a.sharedSizeBytes + dynamic_bytes <= kCuLdsBytes;
+}
+
 // Geometry: sanitised document spans plus, for two tile sizes, the prefix
 // count of document-aligned tiles (off[d] = tiles in documents < d).
 hipError_t launch_doc_setup(const int32_t *cu, int ndocs, int T, int max_seqlen, int tile_a,
