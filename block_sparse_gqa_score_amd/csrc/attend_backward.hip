@@ -792,12 +792,22 @@ __global__ __launch_bounds__(64 * kKvWaves) void bwd_dkdv_kernel(
                     pacc[kt] = mfma_16x16x32(da, vreg[kt][ks], pacc[kt]);
                 }
             }
+            // Only a row whose token lies in the wave's keys (or a padding
+            // row, pos -1) masks keys: a wave-uniform branch, so that the
+            // other rows skip the compare and select per score.  A masked
+            // score becomes -inf, whose exponential is 0.
+            if (pos[rt] < kb + 16 * kKeyTiles - 1) {
+#pragma unroll
+                for (int kt = 0; kt < kKeyTiles; ++kt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (kb + 16 * kt + n > pos[rt]) sacc[kt][i] = -INFINITY;
+            }
 #pragma unroll
             for (int kt = 0; kt < kKeyTiles; ++kt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const bool ok = kb + 16 * kt + n <= pos[rt];
-                    const float p = ok ? __builtin_amdgcn_exp2f(sacc[kt][i] * scale_log2 - lse2[rt][i]) : 0.f;
+                    const float p = __builtin_amdgcn_exp2f(sacc[kt][i] * scale_log2 - lse2[rt][i]);
                     pb[rt >> 1][kt][4 * (rt & 1) + i] = (__bf16)p;
                     dsb[rt >> 1][kt][4 * (rt & 1) + i] = (__bf16)(p * (pacc[kt][i] - dsum[rt][i]));
                 }

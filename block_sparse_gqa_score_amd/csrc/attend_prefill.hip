@@ -502,12 +502,12 @@ __global__ __launch_bounds__(kThreads) void attend_prefill_kernel(
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int r = 4 * i + (lane >> 4);
-            copy_to_lds(ksrc + r * kDim + 8 * ((lane & 15) ^ kswz(r)), slot + i * 1024);
+            copy_to_lds_s(ksrc, uint32_t(2 * (r * kDim + 8 * ((lane & 15) ^ kswz(r)))), slot + i * 1024);
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int dd = 16 * i + (lane >> 2);
-            copy_to_lds(vsrc + dd * kAttnUnit + 8 * ((lane & 3) ^ vswz(dd)), slot + kKUnitBytes + i * 1024);
+            copy_to_lds_s(vsrc, uint32_t(2 * (dd * kAttnUnit + 8 * ((lane & 3) ^ vswz(dd)))), slot + kKUnitBytes + i * 1024);
         }
         // Copies land in issue order: once the flag holds u, the data has landed.
         const uint32_t m0 = (uint32_t)reinterpret_cast<uintptr_t>((lds_void *)&s_flag[u % kRing][0]);
