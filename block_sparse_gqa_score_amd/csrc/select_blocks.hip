@@ -301,7 +301,7 @@ __global__ __launch_bounds__(256, 2) void block_scores_kernel(
         float mxv[2] = {-INFINITY, -INFINITY};
         auto item = [&](auto diag_tag) {
             constexpr bool kDiag = decltype(diag_tag)::value;
-            constexpr int kD = kFp8 ? 2 : 3;           // fragment read distance (steps)
+            constexpr int kD = 3;                      // fragment read distance (steps)
             constexpr int kSt = 4 * kSteps;            // steps per item
             constexpr int kChunk = kSteps >= 4 ? 4 : kSteps;  // steps carrying a part of the max
             constexpr int kRows = 16 / kChunk;         // accumulator rows per part
