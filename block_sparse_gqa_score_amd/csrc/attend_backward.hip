@@ -8,7 +8,6 @@
 //   dq = scale dS K,   dk = scale dS^T Q,   dv = P^T dO.
 //
 // Kernels:
-//   bwd_rowdot_kernel   - D[t][h] = sum_d dO * O in fp32.
 //   bwd_hist_kernel, bwd_colscan_kernel, bwd_scan_kernel, bwd_fill_kernel
 //       - inverse of q2k: for every (KV head g, document block) the tokens
 //       whose row selects the block, ascending, in O(T * topk): per-tile
@@ -25,7 +24,9 @@
 //       landed there, copied after the unit's 16 copies); each wave walks
 //       only the units its tokens need and claims its next one ahead.  Per
 //       unit S^T = K Q^T, dP^T = V dO^T, P^T and dS^T in registers, then
-//       dQ^T += K^T dS^T with K^T taken by transposing LDS reads.
+//       dQ^T += K^T dS^T with K^T taken by transposing LDS reads.  Its
+//       prologue also computes D = rowsum(dO * O) in fp32 for its rows and
+//       stores it for dK/dV, which runs after it.
 //   bwd_dkdv_kernel     - key-major: one workgroup per chunk of kBwdChunk
 //       tokens of one block's list; 8 waves x 16 keys (two waves per SIMD)
 //       hold their K and V rows as MFMA operands; per step of 4 tokens (64
@@ -67,28 +68,6 @@ __device__ __forceinline__ bf16x8 join_tr(const i16x4 &a, const i16x4 &b) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 }  // namespace
-
-// ---------------------------------------------------------------------------
-// D = rowsum(dO * O)
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void bwd_rowdot_kernel(const uint16_t *__restrict__ o,
-                                                         const uint16_t *__restrict__ dout,
-                                                         int64_t rows, float *__restrict__ Dsum) {
-    const int64_t row = int64_t(blockIdx.x) * 16 + (threadIdx.x >> 4);
-    const int c = threadIdx.x & 15;
-    float acc = 0.f;
-    if (row < rows) {
-        const u32x4 a = *(const u32x4 *)(o + row * kDim + 8 * c);
-        const u32x4 b = *(const u32x4 *)(dout + row * kDim + 8 * c);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc += bf16_lo(a[i]) * bf16_lo(b[i]) + bf16_hi(a[i]) * bf16_hi(b[i]);
-    }
-    acc += __shfl_xor(acc, 1);
-    acc += __shfl_xor(acc, 2);
-    acc += __shfl_xor(acc, 4);
-    acc += __shfl_xor(acc, 8);
-    if (c == 0 && row < rows) Dsum[row] = acc;
-}
 
 // ---------------------------------------------------------------------------
 // Inverse of q2k: per (KV head, document block) the selecting tokens
@@ -351,8 +330,8 @@ __device__ __forceinline__ void dq_unit(DqState &st, const uint8_t *Ku, int q, c
 
 __global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
-    const uint16_t *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ Dsum,
-    const int32_t *__restrict__ q2k, int topk, const DocSpan *__restrict__ docs,
+    const uint16_t *__restrict__ dout, const uint16_t *__restrict__ o, const float *__restrict__ lse,
+    float *__restrict__ Dsum, const int32_t *__restrict__ q2k, int topk, const DocSpan *__restrict__ docs,
     const int32_t *__restrict__ tile_off, int ndocs, int T, float scale, float scale_log2,
     uint16_t *__restrict__ dq) {
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
@@ -408,7 +387,21 @@ __global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) st.acc[t][dt] = f32x4{};
         st.lse2[t] = lse[row] * kLog2e;
-        st.dsum[t] = Dsum[row];
+        // D = rowsum(dO * O) of row (token, head n): this lane's 32 of its
+        // 128 products (d = 32ks + 8grp .. +7), then the 4 lanes of the row.
+        // dK/dV (launched after this kernel) reads it from Dsum.
+        const uint16_t *os = o + row * kDim;
+        float dsp = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const bf16x8 ob = __builtin_bit_cast(bf16x8, *(const u32x4 *)(os + 32 * ks + 8 * grp));
+#pragma unroll
+            for (int j = 0; j < 8; ++j) dsp += float(st.dob[t][ks][j]) * float(ob[j]);
+        }
+        dsp += __shfl_xor(dsp, 16);
+        dsp += __shfl_xor(dsp, 32);
+        st.dsum[t] = dsp;
+        if (grp == 0 && tok_ok[t]) Dsum[row] = dsp;
     }
     // use the loaded operands once here, so that the compiler's wait for them
     // sits before the block loop (a wait inside it would drain the prefetch)
@@ -919,14 +912,6 @@ BwdLayout bwd_layout(int T, int ndocs, int topk) {
     return L;
 }
 
-hipError_t launch_bwd_rowdot(const uint16_t *o, const uint16_t *dout, int T, float *Dsum,
-                             hipStream_t stream) {
-    const int64_t rows = int64_t(T) * kHeads;
-    hipLaunchKernelGGL(bwd_rowdot_kernel, dim3(unsigned((rows + 15) / 16)), dim3(256), 0, stream, o, dout,
-                       rows, Dsum);
-    return hipGetLastError();
-}
-
 hipError_t launch_bwd_lists(const int32_t *q2k, int topk, int T, const DocSpan *docs,
                             const int32_t *blk_off, int ndocs, const BwdLayout &L, int32_t *hist, int32_t *cnt,
                             int32_t *list_off, int32_t *chunk_off, int32_t *lists, hipStream_t stream) {
@@ -943,7 +928,7 @@ hipError_t launch_bwd_lists(const int32_t *q2k, int topk, int T, const DocSpan *
 }
 
 hipError_t launch_bwd_dq(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *dout,
-                         const float *lse, const float *Dsum, const int32_t *q2k, int topk,
+                         const uint16_t *o, const float *lse, float *Dsum, const int32_t *q2k, int topk,
                          const DocSpan *docs, const int32_t *tile_off, int ndocs, int T, float scale,
                          uint16_t *dq, hipStream_t stream) {
     const int max_tiles = ceil_div(T, kQTok) + ndocs;
@@ -951,7 +936,7 @@ hipError_t launch_bwd_dq(const uint16_t *q, const uint16_t *k, const uint16_t *v
     const size_t lds = size_t(kQRing) * kQUnitBytes;
     static const bool fits = lds_fits(reinterpret_cast<const void *>(bwd_dq_kernel), lds);
     if (!fits) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(bwd_dq_kernel, dim3(grid), dim3(kQThreads), lds, stream, q, k, v, dout, lse, Dsum,
+    hipLaunchKernelGGL(bwd_dq_kernel, dim3(grid), dim3(kQThreads), lds, stream, q, k, v, dout, o, lse, Dsum,
                        q2k, topk, docs, tile_off, ndocs, T, scale, scale * kLog2e, dq);
     return hipGetLastError();
 }

@@ -355,15 +355,12 @@ msa_status msa_sparse_attend_prefill_backward(
     hipError_t e = launch_doc_setup(cu_seqlens, num_docs, total_tokens, max_seqlen, kAttnTile, kBlock, docs,
                                     tile_off, blk_off, s);
     if (e != hipSuccess) return hip_fail(e, "doc_setup");
-    tm.mark(s, "bwd_rowdot");
-    e = launch_bwd_rowdot(out, dout, total_tokens, dsum, s);
-    if (e != hipSuccess) return hip_fail(e, "bwd_rowdot");
     tm.mark(s, "bwd_lists");
     e = launch_bwd_lists(q2k, topk, total_tokens, docs, blk_off, num_docs, ws.L, hist, cnt, list_off, chunk_off,
                          lists, s);
     if (e != hipSuccess) return hip_fail(e, "bwd_lists");
     tm.mark(s, "bwd_dq");
-    e = launch_bwd_dq(q, k, v, dout, lse, dsum, q2k, topk, docs, tile_off, num_docs, total_tokens,
+    e = launch_bwd_dq(q, k, v, dout, out, lse, dsum, q2k, topk, docs, tile_off, num_docs, total_tokens,
                       softmax_scale, dq, s);
     if (e != hipSuccess) return hip_fail(e, "bwd_dq");
     tm.mark(s, "bwd_dkdv");

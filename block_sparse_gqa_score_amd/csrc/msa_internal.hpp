@@ -68,13 +68,11 @@ struct BwdLayout {
     int ntiles;           // 256-token tiles of the list build
 };
 BwdLayout bwd_layout(int T, int ndocs, int topk);
-hipError_t launch_bwd_rowdot(const uint16_t *o, const uint16_t *dout, int T, float *Dsum,
-                             hipStream_t stream);
 hipError_t launch_bwd_lists(const int32_t *q2k, int topk, int T, const DocSpan *docs,
                             const int32_t *blk_off, int ndocs, const BwdLayout &L, int32_t *hist, int32_t *cnt,
                             int32_t *list_off, int32_t *chunk_off, int32_t *lists, hipStream_t stream);
 hipError_t launch_bwd_dq(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *dout,
-                         const float *lse, const float *Dsum, const int32_t *q2k, int topk,
+                         const uint16_t *o, const float *lse, float *Dsum, const int32_t *q2k, int topk,
                          const DocSpan *docs, const int32_t *tile_off, int ndocs, int T, float scale,
                          uint16_t *dq, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *dout,
