@@ -707,7 +707,7 @@ def main():
         calibrate_copy()
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has no "
               f"multi-GPU path: run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
